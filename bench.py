@@ -1,0 +1,223 @@
+"""Benchmark of FusedKV reconstruction-layer attention on one MI355X.
+
+One step is one decode pass over every reconstruction layer of the 650M-shape
+model (16 layers; layers 9..16 rebuild K/V from layers 1 and 8): 8 calls of
+fkv_decode, batch 32, 8192 cached tokens, 16 query / 8 KV heads, head dim 96,
+bf16, head-major caches, each layer with its own queries and fusion vectors.
+`value` is the step's algorithmic cache traffic divided by its time (GB/s).
+Beside it the line reports the causal prefill of the 1.5B shape (batch 4,
+S = 8192, 16/8 heads, D = 128, 12 fused layers) in TFLOP/s, the Lite and
+plain-control variants, the roofline of the decode kernel, and the fp64
+oracle timed on the host cores on a bounded sample of the decode workload.
+
+Algorithmic work (what the method must move or compute, per layer call):
+  decode  bytes = 4*B*S*Hkv*D*2 (four bf16 source caches; 2 for Lite/vanilla)
+                  + 2*B*Hq*D*2 (Q, O) + 16*Hkv*D (fp32 weights)
+  prefill flops = 2*D*S*(S+1)*B*Hq (QK^T and PV over the causal triangle)
+Inputs are synthetic and seeded (see cross_layer_kv_amd/inputs.py) and
+resident in HBM before timing starts.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+
+DECODE = dict(name="650M-shape FusedKV decode, layers 9-16 fused from layers 1 and 8",
+              B=32, S=8192, Hq=16, Hkv=8, D=96, layers=8, seed=0xF0002)
+PREFILL = dict(name="1.5B-shape FusedKV causal prefill, layers 13-24 fused from layers 1 and 12",
+               B=4, S=8192, Hq=16, Hkv=8, D=128, layers=12, seed=0xF0003)
+
+
+def decode_bytes(B, S, Hq, Hkv, D, sources, elt=2):
+    return sources * B * S * Hkv * D * elt + 2 * B * Hq * D * elt + (16 * Hkv * D if sources == 4 else 0)
+
+
+def prefill_flops(B, S, Hq, D):
+    return 2 * D * S * (S + 1) * B * Hq
+
+
+def _time_region(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        fn()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps  # ms per call of fn
+
+
+def run_decode(cfg, steps, warmup, stream):
+    import torch
+    from cross_layer_kv_amd import binding, inputs
+    dev = "cuda:0"
+    B, S, Hq, Hkv, D, nl = cfg["B"], cfg["S"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["layers"]
+    base = inputs.make_layer(B, 1, S, Hq, Hkv, D, torch.bfloat16, cfg["seed"], dev)
+    qs = [inputs.make_queries(B, 1, Hq, D, torch.bfloat16, cfg["seed"] * 97 + i, dev,
+                              positions=torch.full((1,), S - 1)) for i in range(nl)]
+    ws_list = [inputs.make_weights(Hkv, D, cfg["seed"] * 89 + i, device=dev) for i in range(nl)]
+    outs = [torch.empty_like(q) for q in qs]
+    ws = binding.decode_workspace(qs[0], base.k1)
+
+    def fused_step():
+        for i in range(nl):
+            binding.fkv_decode(qs[i], base.k1, base.kn, base.v1, base.vn, ws_list[i], out=outs[i],
+                               workspace=ws, stream=stream)
+
+    def lite_step():
+        for i in range(nl):
+            binding.fkv_lite_decode(qs[i], base.kn, base.v1, out=outs[i], workspace=ws, stream=stream)
+
+    def vanilla_step():  # storage-layer control: attention over a layer's own caches
+        for i in range(nl):
+            k, v = (base.k1, base.v1) if i % 2 == 0 else (base.kn, base.vn)
+            binding.fkv_lite_decode(qs[i], k, v, out=outs[i], workspace=ws, stream=stream)
+
+    res = {}
+    for name, fn, src in (("fused", fused_step, 4), ("lite", lite_step, 2), ("vanilla", vanilla_step, 2)):
+        ms = _time_region(fn, steps, warmup, stream)
+        byts = decode_bytes(B, S, Hq, Hkv, D, src) * nl
+        res[name] = dict(ms_per_step=ms, ms_per_layer=ms / nl, gbs=byts / (ms * 1e-3) / 1e9,
+                         bytes_per_layer=byts // nl)
+    return res, base
+
+
+def run_prefill(cfg, steps, warmup, stream):
+    import torch
+    from cross_layer_kv_amd import binding, inputs
+    dev = "cuda:0"
+    B, S, Hq, Hkv, D, nl = cfg["B"], cfg["S"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["layers"]
+    base = inputs.make_layer(B, S, S, Hq, Hkv, D, torch.bfloat16, cfg["seed"], dev, decode=False)
+    qs = [base.q] + [inputs.make_queries(B, S, Hq, D, torch.bfloat16, cfg["seed"] * 97 + i, dev)
+                     for i in range(1, nl)]
+    ws_list = [base.weights] + [inputs.make_weights(Hkv, D, cfg["seed"] * 89 + i, device=dev)
+                                for i in range(1, nl)]
+    out = torch.empty_like(base.q)
+
+    def fused_step():
+        for i in range(nl):
+            binding.fkv_prefill(qs[i], base.k1, base.kn, base.v1, base.vn, ws_list[i], out=out, causal=True,
+                                stream=stream)
+
+    def lite_step():
+        for i in range(nl):
+            binding.fkv_lite_prefill(qs[i], base.kn, base.v1, out=out, causal=True, stream=stream)
+
+    res = {}
+    fl = prefill_flops(B, S, Hq, D)
+    for name, fn in (("fused", fused_step), ("lite", lite_step)):
+        ms = _time_region(fn, max(1, steps // 2), max(1, warmup // 2), stream)
+        res[name] = dict(ms_per_step=ms, ms_per_layer=ms / nl,
+                         tflops=fl * nl / (ms * 1e-3) / 1e12)
+    del qs, out, base
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(cfg, base, budget_s=12.0):
+    """The fp64 oracle (unchanged) on the host cores, on whole layers of the
+    decode workload: one layer at a time until ~budget_s seconds have passed."""
+    import oracle
+    from cross_layer_kv_amd import inputs
+    h = inputs.host_array
+    q, k1, kn, v1, vn = (h(t) for t in (base.q, base.k1, base.kn, base.v1, base.vn))
+    w = [x.cpu().numpy() for x in base.weights]
+    B, S, Hq, Hkv, D = cfg["B"], cfg["S"], cfg["Hq"], cfg["Hkv"], cfg["D"]
+    # bounded sample: a prefix of the batch sized so one repetition is short
+    nb = B
+    t0 = time.perf_counter()
+    oracle.attend(q[:1], k1[:1], v1[:1], kn[:1], vn[:1], k_w1=w[0], k_wn=w[1], v_w1=w[2], v_wn=w[3])
+    one = time.perf_counter() - t0
+    nb = int(max(1, min(B, budget_s / max(one, 1e-3) / 2)))
+    reps, elapsed = 0, 0.0
+    t0 = time.perf_counter()
+    while elapsed < budget_s / 2 or reps == 0:
+        oracle.attend(q[:nb], k1[:nb], v1[:nb], kn[:nb], vn[:nb], k_w1=w[0], k_wn=w[1], v_w1=w[2], v_wn=w[3])
+        reps += 1
+        elapsed = time.perf_counter() - t0
+    byts = decode_bytes(nb, S, Hq, Hkv, D, 4) * reps
+    return dict(value=round(byts / elapsed / 1e9, 4), unit="GB/s", cores=oracle.num_threads(), kind="oracle",
+                sample="%d x one fused decode layer on batch rows 0..%d of the 650M-shape workload "
+                       "(S=%d, %d/%d heads, D=%d), %.1f s" % (reps, nb - 1, S, Hq, Hkv, D, elapsed))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--part", choices=["all", "decode", "prefill"], default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run its own "
+              "share of batch rows or KV heads with no exchange); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from cross_layer_kv_amd import binding
+    binding.load_library()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    line = {"metric": "fused-KV decode attn HBM GB/s (% peak); prefill TFLOP/s (% MFMA) at S=8k",
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) post-RoPE caches, N(0.5,0.25) tied fusion weights)"}
+    dec = None
+    if args.part in ("all", "decode"):
+        print("bench: decode %s" % DECODE["name"], file=sys.stderr, flush=True)
+        dec, base = run_decode(DECODE, args.steps, args.warmup, stream)
+        f = dec["fused"]
+        line.update(value=round(f["gbs"], 2), ms_per_step=round(f["ms_per_step"], 4))
+        line["config"] = {"workload": DECODE["name"], "batch": DECODE["B"], "seq_len": DECODE["S"],
+                          "q_heads": DECODE["Hq"], "kv_heads": DECODE["Hkv"], "head_dim": DECODE["D"],
+                          "layers_per_step": DECODE["layers"], "cache_layout": "head-major [B,Hkv,S,D]",
+                          "parallelism": "single GPU"}
+        line["roofline"] = {"bound": "hbm", "kernel": "decode_kernel<bf16,96,fused,G=2>",
+                            "achieved": round(f["bytes_per_layer"] / (f["ms_per_layer"] * 1e-3) / 1e9, 2),
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(f["bytes_per_layer"] / (f["ms_per_layer"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "traffic": None,
+                            "bytes_per_launch": f["bytes_per_layer"],
+                            "avg_launch_us": round(f["ms_per_layer"] * 1e3, 2)}
+        line["decode_variants"] = {k: {"GB/s": round(v["gbs"], 2), "us_per_layer": round(v["ms_per_layer"] * 1e3, 2),
+                                       "frac": round(v["gbs"] / HBM_PEAK_GBS, 4)} for k, v in dec.items()}
+        line["decode_variants"]["fused_over_vanilla_time"] = round(dec["fused"]["ms_per_layer"] /
+                                                                   dec["vanilla"]["ms_per_layer"], 3)
+        if not args.no_cpu_baseline:
+            print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+            line["cpu_baseline"] = cpu_baseline(DECODE, base)
+        del base
+        torch.cuda.empty_cache()
+    if args.part in ("all", "prefill"):
+        print("bench: prefill %s" % PREFILL["name"], file=sys.stderr, flush=True)
+        pre = run_prefill(PREFILL, args.steps, args.warmup, stream)
+        line["prefill"] = {"workload": PREFILL["name"], "batch": PREFILL["B"], "seq_len": PREFILL["S"],
+                           "q_heads": PREFILL["Hq"], "kv_heads": PREFILL["Hkv"], "head_dim": PREFILL["D"],
+                           "flops_per_layer": prefill_flops(PREFILL["B"], PREFILL["S"], PREFILL["Hq"], PREFILL["D"]),
+                           "peak_tflops": MFMA_BF16_PEAK_TFLOPS}
+        for k, v in pre.items():
+            line["prefill"][k] = {"TFLOP/s": round(v["tflops"], 2), "ms_per_layer": round(v["ms_per_layer"], 4),
+                                  "frac": round(v["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)}
+        if dec is None:
+            line.update(value=round(pre["fused"]["tflops"], 2), unit="TFLOP/s",
+                        ms_per_step=round(pre["fused"]["ms_per_step"], 4),
+                        config={"workload": PREFILL["name"]})
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,207 @@
+"""Thin ctypes binding of libfusedkv (declared in include/fusedkv.h).
+
+The Python functions carry the C entry points' names and only marshal
+arguments: torch tensors become device pointers, shapes become an
+``fkv_params`` block, cache tensors become ``fkv_cache`` views (their strides
+are passed through, so head-major and token-major storage both work).  Every
+step of the computation runs in the HIP kernels of the library; there is no
+fallback.  Tensors must live on a GPU; the library must have been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfusedkv.so")
+
+FKV_SUCCESS, FKV_ERROR_INVALID_VALUE, FKV_ERROR_UNSUPPORTED, FKV_ERROR_WORKSPACE, FKV_ERROR_LAUNCH = range(5)
+FKV_F32, FKV_BF16 = 0, 1
+
+
+class FkvError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("%s (status %d)" % (message, status))
+        self.status = status
+
+
+class fkv_cache(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
+                ("stride_s", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
+
+
+class fkv_params(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen_q", ctypes.c_int32),
+                ("seqlen_k", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("causal", ctypes.c_int32)]
+
+
+class fkv_fusion(ctypes.Structure):
+    _fields_ = [("k_w1", ctypes.c_void_p), ("k_wn", ctypes.c_void_p),
+                ("v_w1", ctypes.c_void_p), ("v_wn", ctypes.c_void_p)]
+
+
+EXPORTS = ["fkv_abi_version", "fkv_status_string", "fkv_last_error", "fkv_decode_workspace_size",
+           "fkv_decode", "fkv_lite_decode", "fkv_prefill", "fkv_lite_prefill", "fkv_check_tied"]
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libfusedkv.so and declare its signatures.  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libfusedkv.so is not built (expected at %s); run __graft_entry__.build()" % path)
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    vp = ctypes.c_void_p
+    lib.fkv_abi_version.restype = ctypes.c_int
+    lib.fkv_abi_version.argtypes = []
+    lib.fkv_status_string.restype = ctypes.c_char_p
+    lib.fkv_status_string.argtypes = [ctypes.c_int]
+    lib.fkv_last_error.restype = ctypes.c_char_p
+    lib.fkv_last_error.argtypes = []
+    lib.fkv_decode_workspace_size.restype = ctypes.c_size_t
+    lib.fkv_decode_workspace_size.argtypes = [P(fkv_params)]
+    lib.fkv_decode.restype = ctypes.c_int
+    lib.fkv_decode.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, fkv_cache, fkv_cache,
+                               P(fkv_fusion), vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fkv_lite_decode.restype = ctypes.c_int
+    lib.fkv_lite_decode.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, vp, vp, vp, vp,
+                                    ctypes.c_size_t, vp]
+    lib.fkv_prefill.restype = ctypes.c_int
+    lib.fkv_prefill.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, fkv_cache, fkv_cache,
+                                P(fkv_fusion), vp, vp, vp]
+    lib.fkv_lite_prefill.restype = ctypes.c_int
+    lib.fkv_lite_prefill.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, vp, vp, vp]
+    lib.fkv_check_tied.restype = ctypes.c_int
+    lib.fkv_check_tied.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float]
+    if lib.fkv_abi_version() != 1:
+        raise RuntimeError("libfusedkv ABI version mismatch")
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != FKV_SUCCESS:
+        lib = load_library()
+        raise FkvError(status, lib.fkv_last_error().decode() or lib.fkv_status_string(status).decode())
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return FKV_F32
+    if t.dtype == torch.bfloat16:
+        return FKV_BF16
+    raise TypeError("data must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _dev(t, name):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a GPU tensor" % name)
+    return t.data_ptr()
+
+
+def cache_view(t: torch.Tensor) -> fkv_cache:
+    """fkv_cache of a logical [B, S, H, D] tensor (any strides, channel axis
+    contiguous)."""
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("a cache is a [B, S, H, D] view with a contiguous channel axis")
+    _dev(t, "cache")
+    return fkv_cache(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def make_params(q: torch.Tensor, k: torch.Tensor, *, softmax_scale: float = 0.0, causal: bool = False) -> fkv_params:
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    return fkv_params(B, Sq, Sk, Hq, Hkv, D, _dtype(q), float(softmax_scale), 1 if causal else 0)
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _fusion(weights) -> fkv_fusion:
+    if weights is None or len(weights) != 4:
+        raise ValueError("weights are the four [Hkv, D] float32 vectors (a, a', b, b')")
+    for w in weights:
+        if w.dtype != torch.float32 or not w.is_contiguous():
+            raise TypeError("fusion weights must be contiguous float32")
+    return fkv_fusion(*[_dev(w, "weight") for w in weights])
+
+
+def fkv_decode_workspace_size(params: fkv_params) -> int:
+    return int(load_library().fkv_decode_workspace_size(ctypes.byref(params)))
+
+
+def decode_workspace(q: torch.Tensor, k: torch.Tensor) -> torch.Tensor:
+    """A zero-filled workspace for decode calls with these shapes."""
+    n = fkv_decode_workspace_size(make_params(q, k))
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=q.device)
+
+
+def fkv_decode(q, k1, kn, v1, vn, weights, *, out, workspace, lse=None, seqlens_k=None,
+               softmax_scale=0.0, stream=None):
+    """FusedKV decode step of one reconstruction layer (see fkv_decode in
+    include/fusedkv.h).  q, out: [B, 1, Hq, D]; caches [B, Sk, Hkv, D]."""
+    lib = load_library()
+    p = make_params(q, k1, softmax_scale=softmax_scale)
+    f = _fusion(weights)
+    _check(lib.fkv_decode(ctypes.byref(p), _dev(q, "q"), cache_view(k1), cache_view(kn), cache_view(v1),
+                          cache_view(vn), ctypes.byref(f), _dev(seqlens_k, "seqlens_k"), _dev(out, "out"),
+                          _dev(lse, "lse"), _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
+
+
+def fkv_lite_decode(q, k_src, v_src, *, out, workspace, lse=None, seqlens_k=None, softmax_scale=0.0,
+                    stream=None):
+    """Single-source decode step: FusedKV-Lite with (K^n, V^1), or plain
+    attention of a storage layer over its own caches."""
+    lib = load_library()
+    p = make_params(q, k_src, softmax_scale=softmax_scale)
+    _check(lib.fkv_lite_decode(ctypes.byref(p), _dev(q, "q"), cache_view(k_src), cache_view(v_src),
+                               _dev(seqlens_k, "seqlens_k"), _dev(out, "out"), _dev(lse, "lse"),
+                               _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
+
+
+def fkv_prefill(q, k1, kn, v1, vn, weights, *, out, lse=None, causal=True, softmax_scale=0.0, stream=None):
+    """FusedKV prefill of one reconstruction layer (bf16).  q, out:
+    [B, S, Hq, D]; caches [B, S, Hkv, D]."""
+    lib = load_library()
+    p = make_params(q, k1, softmax_scale=softmax_scale, causal=causal)
+    f = _fusion(weights)
+    _check(lib.fkv_prefill(ctypes.byref(p), _dev(q, "q"), cache_view(k1), cache_view(kn), cache_view(v1),
+                           cache_view(vn), ctypes.byref(f), _dev(out, "out"), _dev(lse, "lse"), _stream(stream)))
+
+
+def fkv_lite_prefill(q, k_src, v_src, *, out, lse=None, causal=True, softmax_scale=0.0, stream=None):
+    """Single-source prefill (FusedKV-Lite or the plain control)."""
+    lib = load_library()
+    p = make_params(q, k_src, softmax_scale=softmax_scale, causal=causal)
+    _check(lib.fkv_lite_prefill(ctypes.byref(p), _dev(q, "q"), cache_view(k_src), cache_view(v_src),
+                                _dev(out, "out"), _dev(lse, "lse"), _stream(stream)))
+
+
+def fkv_check_tied(k_w: torch.Tensor, pairing: str = "interleaved", tol: float = 0.0) -> bool:
+    """Host check that key weights [Hkv, D] are tied on RoPE pairs."""
+    lib = load_library()
+    w = k_w.detach().to("cpu", torch.float32).contiguous()
+    code = {"interleaved": 0, "half": 1}[pairing]
+    st = lib.fkv_check_tied(ctypes.c_void_p(w.data_ptr()), w.shape[0], w.shape[1], code, float(tol))
+    if st == FKV_SUCCESS:
+        return True
+    if st == FKV_ERROR_INVALID_VALUE:
+        return False
+    _check(st)
+    return False

@@ -1,0 +1,349 @@
+// fkv_api.cpp -- host side of libfusedkv: argument validation, work planning
+// and the exported C entry points.  No HIP headers: every check here reads
+// only the host-side parameter structs and pointer values, so an invalid call
+// returns before anything is enqueued.  The device work is in
+// fkv_decode.hip / fkv_prefill.hip.
+#include "../../include/fusedkv.h"
+#include "fkv_internal.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+fkv_status fail(fkv_status s, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    if (std::getenv("FKV_LOG")) std::fprintf(stderr, "libfusedkv: %s\n", g_last_error);
+    return s;
+}
+
+fkv_status ok()
+{
+    g_last_error[0] = '\0';
+    return FKV_SUCCESS;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elt_size(int32_t dtype) { return dtype == FKV_F32 ? 4 : 2; }
+
+bool supported_head_dim(int32_t d) { return d == 64 || d == 80 || d == 96 || d == 128; }
+
+bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+// Shape checks common to decode and prefill.
+fkv_status check_shape(const fkv_params* p)
+{
+    if (!p) return fail(FKV_ERROR_INVALID_VALUE, "params is NULL");
+    if (p->batch < 0 || p->seqlen_q < 0 || p->seqlen_k < 0)
+        return fail(FKV_ERROR_INVALID_VALUE, "negative batch or sequence length");
+    if (p->num_kv_heads < 1 || p->num_q_heads < 1)
+        return fail(FKV_ERROR_INVALID_VALUE, "head counts must be >= 1");
+    if (p->num_q_heads % p->num_kv_heads != 0)
+        return fail(FKV_ERROR_INVALID_VALUE, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                    p->num_q_heads, p->num_kv_heads);
+    if (p->dtype != FKV_F32 && p->dtype != FKV_BF16)
+        return fail(FKV_ERROR_INVALID_VALUE, "unknown dtype %d", p->dtype);
+    if (!std::isfinite(p->softmax_scale) || p->softmax_scale < 0.0f)
+        return fail(FKV_ERROR_INVALID_VALUE, "softmax_scale must be finite and >= 0 (0 = 1/sqrt(D))");
+    if (!supported_head_dim(p->head_dim))
+        return fail(FKV_ERROR_UNSUPPORTED, "head_dim %d not in {64, 80, 96, 128}", p->head_dim);
+    if (!supported_group(p->num_q_heads / p->num_kv_heads))
+        return fail(FKV_ERROR_UNSUPPORTED, "GQA ratio %d not in {1, 2, 4, 8}",
+                    p->num_q_heads / p->num_kv_heads);
+    return FKV_SUCCESS;
+}
+
+// A cache view is usable when its base and every row start are 16-byte
+// aligned and its strides are non-negative.
+fkv_status check_cache(const fkv_params* p, const fkv_cache& c, const char* name)
+{
+    if (!c.data && p->seqlen_k == 0) return FKV_SUCCESS;  // an empty cache is never read
+    if (!c.data) return fail(FKV_ERROR_INVALID_VALUE, "%s.data is NULL", name);
+    if (!aligned16(c.data)) return fail(FKV_ERROR_INVALID_VALUE, "%s.data is not 16-byte aligned", name);
+    if (c.stride_b < 0 || c.stride_s < 0 || c.stride_h < 0)
+        return fail(FKV_ERROR_INVALID_VALUE, "%s has a negative stride", name);
+    const int64_t e = (int64_t)elt_size(p->dtype);
+    if ((c.stride_b * e) % 16 || (c.stride_s * e) % 16 || (c.stride_h * e) % 16)
+        return fail(FKV_ERROR_INVALID_VALUE, "%s strides do not keep rows 16-byte aligned", name);
+    if (p->seqlen_k > 1 && c.stride_s < p->head_dim)
+        return fail(FKV_ERROR_INVALID_VALUE, "%s token stride overlaps a row", name);
+    return FKV_SUCCESS;
+}
+
+fkv::View view_of(const fkv_cache& c)
+{
+    return fkv::View{c.data, c.stride_b, c.stride_s, c.stride_h};
+}
+
+float scale_log2_of(const fkv_params* p)
+{
+    const double s = p->softmax_scale != 0.0f ? (double)p->softmax_scale
+                                              : 1.0 / std::sqrt((double)p->head_dim);
+    return (float)(s * 1.4426950408889634); // log2(e)
+}
+
+// Split plan for decode.  Every split covers a multiple of 64 tokens (one
+// workgroup iteration).  The workgroup count aims at one resident wave of
+// workgroups on a 256-CU part: the four-source kernel keeps 3 workgroups per
+// CU resident, the two-source kernel 5, so all splits run at once and no
+// tail round is left.  The count is capped at 256 splits so the merge stays
+// cheap.  The plan depends on the parameters only (no device query), so the
+// workspace size is a pure function of them.  FKV_DECODE_SPLITS overrides the
+// split count, FKV_DECODE_WGS the workgroup target.
+fkv::DecodePlan plan_decode(const fkv_params* p, bool fused)
+{
+    fkv::DecodePlan pl{};
+    const int64_t units = (int64_t)p->batch * p->num_kv_heads;
+    const int64_t S = p->seqlen_k;
+    const int64_t max_splits = S > 0 ? (S + 63) / 64 : 1;
+    int64_t target = fused ? 768 : 1280;
+    if (const char* env = std::getenv("FKV_DECODE_WGS")) {
+        const long v = std::strtol(env, nullptr, 10);
+        if (v > 0) target = v;
+    }
+    int64_t ns = units > 0 ? (target + units - 1) / units : 1;
+    if (const char* env = std::getenv("FKV_DECODE_SPLITS")) {
+        const long v = std::strtol(env, nullptr, 10);
+        if (v > 0) ns = v;
+    }
+    if (ns > max_splits) ns = max_splits;
+    if (ns > 256) ns = 256;
+    if (ns < 1) ns = 1;
+    int64_t chunk = S > 0 ? (S + ns - 1) / ns : 64;
+    chunk = (chunk + 63) / 64 * 64;
+    ns = S > 0 ? (S + chunk - 1) / chunk : 1;
+    pl.n_splits = (int32_t)ns;
+    pl.chunk = (int32_t)chunk;
+    const int64_t G = p->num_q_heads / p->num_kv_heads;
+    pl.counters_bytes = (size_t)((units * 4 + 255) / 256 * 256);
+    pl.ml_bytes = (size_t)((units * ns * G * 2 * 4 + 255) / 256 * 256);
+    pl.part_bytes = (size_t)(units * ns * G * p->head_dim * 4);
+    pl.total_bytes = pl.counters_bytes + pl.ml_bytes + pl.part_bytes;
+    return pl;
+}
+
+fkv_status decode_common(const fkv_params* p, const void* q, const fkv_cache* caches,
+                         const char* const* names, int ncaches, const fkv_fusion* fusion,
+                         const int32_t* seqlens_k, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream)
+{
+    fkv_status s = check_shape(p);
+    if (s) return s;
+    if (p->seqlen_q != 1) return fail(FKV_ERROR_INVALID_VALUE, "decode needs seqlen_q == 1 (got %d)", p->seqlen_q);
+    if (p->batch == 0) return ok();
+    if (!q || !out) return fail(FKV_ERROR_INVALID_VALUE, "q or out is NULL");
+    if (!aligned16(q) || !aligned16(out)) return fail(FKV_ERROR_INVALID_VALUE, "q or out is not 16-byte aligned");
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return fail(FKV_ERROR_INVALID_VALUE, "lse is not 4-byte aligned");
+    if (seqlens_k && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u))
+        return fail(FKV_ERROR_INVALID_VALUE, "seqlens_k is not 4-byte aligned");
+    for (int i = 0; i < ncaches; ++i)
+        if ((s = check_cache(p, caches[i], names[i]))) return s;
+    const bool fused = ncaches == 4;
+    if (fused) {
+        if (!fusion || !fusion->k_w1 || !fusion->k_wn || !fusion->v_w1 || !fusion->v_wn)
+            return fail(FKV_ERROR_INVALID_VALUE, "fusion weights missing");
+        if (!aligned16(fusion->k_w1) || !aligned16(fusion->k_wn) || !aligned16(fusion->v_w1) ||
+            !aligned16(fusion->v_wn))
+            return fail(FKV_ERROR_INVALID_VALUE, "fusion weights are not 16-byte aligned");
+    }
+    const bool fused_plan = ncaches == 4;
+    const fkv::DecodePlan pl = plan_decode(p, fused_plan);
+    if (!workspace || workspace_bytes < pl.total_bytes)
+        return fail(FKV_ERROR_WORKSPACE, "workspace needs %zu bytes (got %zu)", pl.total_bytes,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(FKV_ERROR_WORKSPACE, "workspace is not 256-byte aligned");
+
+    fkv::DecodeArgs a{};
+    a.q = q;
+    a.k1 = view_of(caches[0]);
+    a.v1 = view_of(caches[fused ? 2 : 1]);
+    if (fused) {
+        a.kn = view_of(caches[1]);
+        a.vn = view_of(caches[3]);
+        a.kw1 = fusion->k_w1;
+        a.kwn = fusion->k_wn;
+        a.vw1 = fusion->v_w1;
+        a.vwn = fusion->v_wn;
+    }
+    a.seqlens = seqlens_k;
+    a.out = out;
+    a.lse = lse;
+    char* ws = static_cast<char*>(workspace);
+    a.counters = reinterpret_cast<unsigned*>(ws);
+    a.ml = reinterpret_cast<float*>(ws + pl.counters_bytes);
+    a.part = reinterpret_cast<float*>(ws + pl.counters_bytes + pl.ml_bytes);
+    a.B = p->batch;
+    a.Sk = p->seqlen_k;
+    a.Hq = p->num_q_heads;
+    a.Hkv = p->num_kv_heads;
+    a.D = p->head_dim;
+    a.G = p->num_q_heads / p->num_kv_heads;
+    a.n_splits = pl.n_splits;
+    a.chunk = pl.chunk;
+    a.scale_log2 = scale_log2_of(p);
+    if (std::getenv("FKV_TRACE"))
+        std::fprintf(stderr, "libfusedkv: decode %s B=%d Sk=%d Hq=%d Hkv=%d D=%d splits=%d chunk=%d\n",
+                     fused ? "fused" : "single", a.B, a.Sk, a.Hq, a.Hkv, a.D, a.n_splits, a.chunk);
+    const int rc = fkv::launch_decode(a, fused, p->dtype, stream);
+    if (rc) return fail(FKV_ERROR_LAUNCH, "decode launch failed (HIP error %d)", rc);
+    return ok();
+}
+
+fkv_status prefill_common(const fkv_params* p, const void* q, const fkv_cache* caches,
+                          const char* const* names, int ncaches, const fkv_fusion* fusion,
+                          void* out, float* lse, void* stream)
+{
+    fkv_status s = check_shape(p);
+    if (s) return s;
+    if (p->dtype != FKV_BF16) return fail(FKV_ERROR_UNSUPPORTED, "prefill supports bfloat16 data only");
+    if (p->seqlen_q != p->seqlen_k)
+        return fail(FKV_ERROR_UNSUPPORTED, "prefill needs seqlen_q == seqlen_k (got %d, %d)", p->seqlen_q,
+                    p->seqlen_k);
+    if (p->causal != 0 && p->causal != 1) return fail(FKV_ERROR_INVALID_VALUE, "causal must be 0 or 1");
+    if (p->batch == 0 || p->seqlen_q == 0) return ok();
+    if (!q || !out) return fail(FKV_ERROR_INVALID_VALUE, "q or out is NULL");
+    if (!aligned16(q) || !aligned16(out)) return fail(FKV_ERROR_INVALID_VALUE, "q or out is not 16-byte aligned");
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return fail(FKV_ERROR_INVALID_VALUE, "lse is not 4-byte aligned");
+    for (int i = 0; i < ncaches; ++i)
+        if ((s = check_cache(p, caches[i], names[i]))) return s;
+    const bool fused = ncaches == 4;
+    if (fused) {
+        if (!fusion || !fusion->k_w1 || !fusion->k_wn || !fusion->v_w1 || !fusion->v_wn)
+            return fail(FKV_ERROR_INVALID_VALUE, "fusion weights missing");
+        if (!aligned16(fusion->k_w1) || !aligned16(fusion->k_wn) || !aligned16(fusion->v_w1) ||
+            !aligned16(fusion->v_wn))
+            return fail(FKV_ERROR_INVALID_VALUE, "fusion weights are not 16-byte aligned");
+    }
+    const int G = p->num_q_heads / p->num_kv_heads;
+    const int bm = fkv::prefill_rows_per_tile(G);
+    if (bm <= 0) return fail(FKV_ERROR_UNSUPPORTED, "GQA ratio %d not supported by prefill", G);
+
+    fkv::PrefillArgs a{};
+    a.q = q;
+    a.k1 = view_of(caches[0]);
+    a.v1 = view_of(caches[fused ? 2 : 1]);
+    if (fused) {
+        a.kn = view_of(caches[1]);
+        a.vn = view_of(caches[3]);
+        a.kw1 = fusion->k_w1;
+        a.kwn = fusion->k_wn;
+        a.vw1 = fusion->v_w1;
+        a.vwn = fusion->v_wn;
+    }
+    a.out = out;
+    a.lse = lse;
+    a.B = p->batch;
+    a.S = p->seqlen_q;
+    a.Hq = p->num_q_heads;
+    a.Hkv = p->num_kv_heads;
+    a.D = p->head_dim;
+    a.G = G;
+    a.causal = p->causal;
+    a.n_qtiles = (p->seqlen_q + bm - 1) / bm;
+    a.scale_log2 = scale_log2_of(p);
+    if (std::getenv("FKV_TRACE"))
+        std::fprintf(stderr, "libfusedkv: prefill %s B=%d S=%d Hq=%d Hkv=%d D=%d qtiles=%d causal=%d\n",
+                     fused ? "fused" : "single", a.B, a.S, a.Hq, a.Hkv, a.D, a.n_qtiles, a.causal);
+    const int rc = fkv::launch_prefill(a, fused, stream);
+    if (rc) return fail(FKV_ERROR_LAUNCH, "prefill launch failed (HIP error %d)", rc);
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int fkv_abi_version(void) { return FKV_ABI_VERSION; }
+
+const char* fkv_status_string(fkv_status status)
+{
+    switch (status) {
+    case FKV_SUCCESS: return "success";
+    case FKV_ERROR_INVALID_VALUE: return "invalid value";
+    case FKV_ERROR_UNSUPPORTED: return "unsupported";
+    case FKV_ERROR_WORKSPACE: return "workspace missing or too small";
+    case FKV_ERROR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+const char* fkv_last_error(void) { return g_last_error; }
+
+size_t fkv_decode_workspace_size(const fkv_params* params)
+{
+    if (check_shape(params) != FKV_SUCCESS || params->seqlen_q != 1) return 0;
+    const size_t f = plan_decode(params, true).total_bytes;
+    const size_t s = plan_decode(params, false).total_bytes;
+    return f > s ? f : s;
+}
+
+fkv_status fkv_decode(const fkv_params* params, const void* q, fkv_cache k1, fkv_cache kn,
+                      fkv_cache v1, fkv_cache vn, const fkv_fusion* fusion,
+                      const int32_t* seqlens_k, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream)
+{
+    const fkv_cache c[4] = {k1, kn, v1, vn};
+    static const char* const n[4] = {"k1", "kn", "v1", "vn"};
+    return decode_common(params, q, c, n, 4, fusion, seqlens_k, out, lse, workspace,
+                         workspace_bytes, stream);
+}
+
+fkv_status fkv_lite_decode(const fkv_params* params, const void* q, fkv_cache k_src,
+                           fkv_cache v_src, const int32_t* seqlens_k, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream)
+{
+    const fkv_cache c[2] = {k_src, v_src};
+    static const char* const n[2] = {"k_src", "v_src"};
+    return decode_common(params, q, c, n, 2, nullptr, seqlens_k, out, lse, workspace,
+                         workspace_bytes, stream);
+}
+
+fkv_status fkv_prefill(const fkv_params* params, const void* q, fkv_cache k1, fkv_cache kn,
+                       fkv_cache v1, fkv_cache vn, const fkv_fusion* fusion, void* out,
+                       float* lse, void* stream)
+{
+    const fkv_cache c[4] = {k1, kn, v1, vn};
+    static const char* const n[4] = {"k1", "kn", "v1", "vn"};
+    return prefill_common(params, q, c, n, 4, fusion, out, lse, stream);
+}
+
+fkv_status fkv_lite_prefill(const fkv_params* params, const void* q, fkv_cache k_src,
+                            fkv_cache v_src, void* out, float* lse, void* stream)
+{
+    const fkv_cache c[2] = {k_src, v_src};
+    static const char* const n[2] = {"k_src", "v_src"};
+    return prefill_common(params, q, c, n, 2, nullptr, out, lse, stream);
+}
+
+fkv_status fkv_check_tied(const float* host_k_w, int32_t h_kv, int32_t d, int32_t pairing, float tol)
+{
+    if (!host_k_w || h_kv < 1 || d < 2 || (d & 1) || !(tol >= 0.0f))
+        return fail(FKV_ERROR_INVALID_VALUE, "bad arguments to fkv_check_tied");
+    if (pairing != 0 && pairing != 1) return fail(FKV_ERROR_INVALID_VALUE, "pairing must be 0 or 1");
+    for (int32_t h = 0; h < h_kv; ++h) {
+        const float* w = host_k_w + (int64_t)h * d;
+        for (int32_t j = 0; j < d / 2; ++j) {
+            const int32_t i1 = pairing == 0 ? 2 * j : j;
+            const int32_t i2 = pairing == 0 ? 2 * j + 1 : j + d / 2;
+            const float diff = std::fabs(w[i1] - w[i2]);
+            if (!(diff <= tol))
+                return fail(FKV_ERROR_INVALID_VALUE, "head %d channels %d and %d differ by %g", h, i1, i2,
+                            (double)diff);
+        }
+    }
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,427 @@
+// fkv_decode.hip -- split-K flash-decode for FusedKV reconstruction layers on
+// gfx950 (CDNA4, wave64).
+//
+// Pages cited (by title):
+//   [Deck]  "FusedKV: Reconstructing KV Caches with Cross-Layer Fusion"
+//   [Notes] "FusedKV:通过跨层融合重构 KV 缓存"
+//
+// What a call computes: for every batch row b and query head h (KV head
+// g = h / G), attention of q[b, h] over keys a(.)K1 + a'(.)Kn and values
+// b(.)V1 + b'(.)Vn of KV head g ([Deck] frame "FusedKV learns two-source,
+// channel-wise fusion", Eqs. (4)-(5)), or over one key and one value source
+// for FusedKV-Lite / the plain control ([Deck] frame "Lite separates the key
+// source from the value source", Eq. (6)).  The reconstruction is formed in
+// float32 registers, tile by tile, and never stored ([Notes] section 2.3).
+//
+// Decode is bound by HBM: every cached element is read once and used for a
+// handful of flops ([Deck] frame "Decode cost depends on the inference
+// regime": memory-bound TPOT of FusedKV is about 1.5x vanilla over a model).
+// The design therefore aims only at streaming the four source caches at full
+// bandwidth with little VALU work per byte:
+//   * work unit = (batch, KV head, split of the key axis); all G query heads
+//     of the KV head live in the same lanes, so each fused element is built
+//     once and used G times;
+//   * a lane owns 8 channels (one 16-byte bf16 load, two for f32) of one
+//     token; the D/8 lanes of a token form a 8- or 16-lane group, and the
+//     score of that token is a DPP butterfly sum inside the group;
+//   * each lane runs its own online softmax over the tokens its group sees;
+//     groups, waves and finally splits are merged with the usual
+//     (max, sum) rescaling, all in the log2 domain (scale * log2 e is folded
+//     into the query);
+//   * the last workgroup of a (batch, KV head) to finish -- found with a
+//     completion counter in the workspace -- merges the splits and writes O
+//     and LSE, so one call is one kernel launch.  It resets the counter.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fkv_internal.h"
+
+namespace fkv {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kIterTokens = 64;  // tokens per workgroup iteration
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Raw bits of 8 channels of one row: one 16-byte load for bf16, two for f32.
+template <typename T>
+struct Raw8 {
+    static constexpr int NV = sizeof(T) == 2 ? 1 : 2;
+    uint4 v[NV];
+};
+
+template <typename T>
+__device__ __forceinline__ void load8(Raw8<T>& r, const T* p, bool pred)
+{
+#pragma unroll
+    for (int i = 0; i < Raw8<T>::NV; ++i)
+        r.v[i] = pred ? reinterpret_cast<const uint4*>(p)[i] : make_uint4(0u, 0u, 0u, 0u);
+}
+
+template <typename T>
+__device__ __forceinline__ void widen8(const Raw8<T>& r, float* f)
+{
+    if constexpr (sizeof(T) == 2) {
+        const uint32_t w[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = bf16_lo(w[i]);
+            f[2 * i + 1] = bf16_hi(w[i]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            f[4 * i + 0] = __uint_as_float(r.v[i].x);
+            f[4 * i + 1] = __uint_as_float(r.v[i].y);
+            f[4 * i + 2] = __uint_as_float(r.v[i].z);
+            f[4 * i + 3] = __uint_as_float(r.v[i].w);
+        }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ uint16_t from_f32<uint16_t>(float x)
+{
+    // round to nearest even; NaN stays a quiet NaN
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Sum over the LPT lanes of a token group with DPP lane permutations:
+// xor 1, xor 2 (quad permutes), then mirror within 8 and within 16 lanes.
+// After the quad steps every lane of a quad holds the quad sum, so the
+// mirrors add exactly the partner quad / partner half-row.
+template <int LPT>
+__device__ __forceinline__ float group_sum(float v)
+{
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    if constexpr (LPT == 16)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    return v;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Weight of a partial (max m) relative to a common max M; 0 for an empty one.
+__device__ __forceinline__ float rel(float m, float M) { return m == -INFINITY ? 0.0f : exp2_fast(m - M); }
+
+template <typename T, int D, bool FUSED, int G>
+__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
+{
+    constexpr int NP = D / 8;              // 8-channel pieces per row
+    constexpr int LPT = NP <= 8 ? 8 : 16;  // lanes per token group
+    constexpr int TPW = 64 / LPT;          // tokens per wave step
+    constexpr int U = kIterTokens / (kWaves * TPW);  // steps per iteration
+
+    __shared__ float s_acc[kWaves][G][D];
+    __shared__ float s_ml[kWaves][G][2];
+    __shared__ float s_w[256 * G];
+    __shared__ float4 s_red[kThreads];
+    __shared__ float s_M[G], s_L[G];
+    __shared__ int s_last;
+
+    const int split = blockIdx.x;
+    const int bg = blockIdx.y;  // b * Hkv + g
+    const int b = bg / a.Hkv, g = bg - (bg / a.Hkv) * a.Hkv;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int grp = lane / LPT, pc = lane % LPT;
+    const bool active = pc < NP;
+    const int c0 = active ? pc * 8 : 0;
+
+    int len = a.seqlens ? a.seqlens[b] : a.Sk;
+    len = len < 0 ? 0 : (len > a.Sk ? a.Sk : len);
+    const int t_begin = split * a.chunk;
+    const int t_end = min(len, t_begin + a.chunk);
+
+    // Query of the G heads, pre-scaled into the log2 domain, and the lane's
+    // fusion weights.
+    float qs[G][8];
+    {
+        const T* qp = static_cast<const T*>(a.q) + ((int64_t)b * a.Hq + (int64_t)g * G) * D + c0;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            Raw8<T> r;
+            load8(r, qp + (int64_t)hh * D, active);
+            widen8(r, qs[hh]);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) qs[hh][c] *= a.scale_log2;
+        }
+    }
+    float wk1[8], wkn[8], wv1[8], wvn[8];
+    if constexpr (FUSED) {
+        const int64_t wo = (int64_t)g * D + c0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            wk1[c] = active ? a.kw1[wo + c] : 0.0f;
+            wkn[c] = active ? a.kwn[wo + c] : 0.0f;
+            wv1[c] = active ? a.vw1[wo + c] : 0.0f;
+            wvn[c] = active ? a.vwn[wo + c] : 0.0f;
+        }
+    }
+
+    const T* k1p = static_cast<const T*>(a.k1.data) + (int64_t)b * a.k1.sb + (int64_t)g * a.k1.sh + c0;
+    const T* v1p = static_cast<const T*>(a.v1.data) + (int64_t)b * a.v1.sb + (int64_t)g * a.v1.sh + c0;
+    const T* knp = k1p;
+    const T* vnp = v1p;
+    if constexpr (FUSED) {
+        knp = static_cast<const T*>(a.kn.data) + (int64_t)b * a.kn.sb + (int64_t)g * a.kn.sh + c0;
+        vnp = static_cast<const T*>(a.vn.data) + (int64_t)b * a.vn.sb + (int64_t)g * a.vn.sh + c0;
+    }
+
+    float m[G], l[G], acc[G][8];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+        m[hh] = -INFINITY;
+        l[hh] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[hh][c] = 0.0f;
+    }
+
+    for (int t0 = t_begin; t0 < t_end; t0 += kIterTokens) {
+        Raw8<T> rk1[U], rkn[U], rv1[U], rvn[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = t0 + (wave * U + u) * TPW + grp;
+            ok[u] = t < t_end;
+            const bool pr = active && ok[u];
+            load8(rk1[u], k1p + (int64_t)t * a.k1.ss, pr);
+            if constexpr (FUSED) load8(rkn[u], knp + (int64_t)t * a.kn.ss, pr);
+            load8(rv1[u], v1p + (int64_t)t * a.v1.ss, pr);
+            if constexpr (FUSED) load8(rvn[u], vnp + (int64_t)t * a.vn.ss, pr);
+        }
+
+        // scores of the U tokens of this lane's group, log2 domain
+        float s[U][G];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float kf[8];
+            widen8(rk1[u], kf);
+            if constexpr (FUSED) {
+                float kn[8];
+                widen8(rkn[u], kn);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) kf[c] = wk1[c] * kf[c] + wkn[c] * kn[c];
+            }
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) {
+                float d = 0.0f;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) d += qs[hh][c] * kf[c];
+                d = group_sum<LPT>(d);
+                s[u][hh] = ok[u] ? d : -INFINITY;
+            }
+        }
+
+        // online softmax: raise the running max if needed, then accumulate
+        float msub[G];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            float mx = s[0][hh];
+#pragma unroll
+            for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u][hh]);
+            if (mx > m[hh]) {
+                const float corr = rel(m[hh], mx);
+                l[hh] *= corr;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[hh][c] *= corr;
+                m[hh] = mx;
+            }
+            msub[hh] = m[hh] == -INFINITY ? 0.0f : m[hh];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float vf[8];
+            widen8(rv1[u], vf);
+            if constexpr (FUSED) {
+                float vn[8];
+                widen8(rvn[u], vn);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) vf[c] = wv1[c] * vf[c] + wvn[c] * vn[c];
+            }
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) {
+                const float p = exp2_fast(s[u][hh] - msub[hh]);
+                l[hh] += p;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[hh][c] += p * vf[c];
+            }
+        }
+    }
+
+    // merge the token groups of the wave (lanes with equal pc)
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            const float mo = __shfl_xor(m[hh], off);
+            const float lo = __shfl_xor(l[hh], off);
+            const float M = fmaxf(m[hh], mo);
+            const float fa = rel(m[hh], M), fb = rel(mo, M);
+            l[hh] = l[hh] * fa + lo * fb;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[hh][c] = acc[hh][c] * fa + __shfl_xor(acc[hh][c], off) * fb;
+            m[hh] = M;
+        }
+    }
+    if (grp == 0 && active) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) s_acc[wave][hh][c0 + c] = acc[hh][c];
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            s_ml[wave][hh][0] = m[hh];
+            s_ml[wave][hh][1] = l[hh];
+        }
+    }
+    __syncthreads();
+
+    // merge the waves; write this split's partial (unnormalised) result
+    const int64_t slot = (int64_t)bg * a.n_splits + split;
+    for (int e = tid; e < G * D; e += kThreads) {
+        const int hh = e / D, d = e - (e / D) * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][hh][0]);
+        float o = 0.0f, ls = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = rel(s_ml[w][hh][0], M);
+            o += s_acc[w][hh][d] * f;
+            ls += s_ml[w][hh][1] * f;
+        }
+        a.part[slot * G * D + e] = o;
+        if (d == 0) {
+            a.ml[(slot * G + hh) * 2 + 0] = M;
+            a.ml[(slot * G + hh) * 2 + 1] = ls;
+        }
+    }
+
+    // completion counter: the last split of this (b, g) merges all splits
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&a.counters[bg], 1u) == (unsigned)(a.n_splits - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+
+    const int ns = a.n_splits;
+    const float* mlp = a.ml + (int64_t)bg * ns * G * 2;
+    const float* pp = a.part + (int64_t)bg * ns * G * D;
+    for (int i = tid; i < ns * G; i += kThreads) s_w[i] = mlp[2 * i];
+    __syncthreads();
+    if (tid < G) {
+        float M = -INFINITY;
+        for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, s_w[sp * G + tid]);
+        s_M[tid] = M;
+    }
+    __syncthreads();
+    for (int i = tid; i < ns * G; i += kThreads) s_w[i] = rel(s_w[i], s_M[i % G]);
+    __syncthreads();
+    if (tid < G) {
+        float L = 0.0f;
+        for (int sp = 0; sp < ns; ++sp) L += s_w[sp * G + tid] * mlp[2 * (sp * G + tid) + 1];
+        s_L[tid] = L;
+    }
+    __syncthreads();
+
+    // O = sum_s w_s * part_s / L over float4 columns; the splits are spread
+    // over NSUB threads per column so that many loads are in flight.
+    constexpr int NE4 = G * D / 4;
+    constexpr int NSUB = kThreads / NE4;
+    static_assert(NE4 <= kThreads && NSUB >= 1, "merge layout");
+    if (tid < NSUB * NE4) {
+        const int sub = tid / NE4, e4 = tid - (tid / NE4) * NE4;
+        const int hh = (e4 * 4) / D;
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4* p4 = reinterpret_cast<const float4*>(pp) + e4;
+#pragma unroll 8
+        for (int sp = sub; sp < ns; sp += NSUB) {
+            const float w = s_w[sp * G + hh];
+            const float4 x = p4[(int64_t)sp * NE4];
+            o.x += w * x.x;
+            o.y += w * x.y;
+            o.z += w * x.z;
+            o.w += w * x.w;
+        }
+        s_red[tid] = o;
+    }
+    __syncthreads();
+    if (tid < NE4) {
+        float4 o = s_red[tid];
+        for (int sub = 1; sub < NSUB; ++sub) {
+            const float4 x = s_red[sub * NE4 + tid];
+            o.x += x.x;
+            o.y += x.y;
+            o.z += x.z;
+            o.w += x.w;
+        }
+        const int hh = (tid * 4) / D, d = tid * 4 - hh * D;
+        const float L = s_L[hh];
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        T* op = static_cast<T*>(a.out) + ((int64_t)b * a.Hq + (int64_t)g * G + hh) * D + d;
+        op[0] = from_f32<T>(o.x * inv);
+        op[1] = from_f32<T>(o.y * inv);
+        op[2] = from_f32<T>(o.z * inv);
+        op[3] = from_f32<T>(o.w * inv);
+        if (d == 0 && a.lse)
+            a.lse[(int64_t)b * a.Hq + (int64_t)g * G + hh] =
+                L > 0.0f ? (s_M[hh] + log2f(L)) * kLn2 : -INFINITY;
+    }
+    if (tid == 0) atomicExch(&a.counters[bg], 0u);
+}
+
+template <typename T, int D, bool FUSED>
+int launch_g(const DecodeArgs& a, hipStream_t st)
+{
+    const dim3 grid(a.n_splits, a.B * a.Hkv);
+    switch (a.G) {
+    case 1: hipLaunchKernelGGL((decode_kernel<T, D, FUSED, 1>), grid, dim3(kThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<T, D, FUSED, 2>), grid, dim3(kThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<T, D, FUSED, 4>), grid, dim3(kThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<T, D, FUSED, 8>), grid, dim3(kThreads), 0, st, a); break;
+    default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}
+
+template <typename T, bool FUSED>
+int launch_d(const DecodeArgs& a, hipStream_t st)
+{
+    switch (a.D) {
+    case 64: return launch_g<T, 64, FUSED>(a, st);
+    case 80: return launch_g<T, 80, FUSED>(a, st);
+    case 96: return launch_g<T, 96, FUSED>(a, st);
+    case 128: return launch_g<T, 128, FUSED>(a, st);
+    default: return (int)hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int launch_decode(const DecodeArgs& a, bool fused, int dtype, void* stream)
+{
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (a.B == 0) return 0;
+    if (a.n_splits > 256 || (int64_t)a.B * a.Hkv > 65535) return (int)hipErrorInvalidValue;
+    if (dtype == 0) return fused ? launch_d<float, true>(a, st) : launch_d<float, false>(a, st);
+    return fused ? launch_d<uint16_t, true>(a, st) : launch_d<uint16_t, false>(a, st);
+}
+
+}  // namespace fkv

@@ -1,0 +1,414 @@
+// fkv_prefill.hip -- causal flash-attention prefill for FusedKV reconstruction
+// layers on gfx950 matrix cores (fp16 operands, fp32 accumulate).
+//
+// Pages cited (by title):
+//   [Deck]  "FusedKV: Reconstructing KV Caches with Cross-Layer Fusion"
+//   [Notes] "FusedKV:通过跨层融合重构 KV 缓存"
+//
+// What a call computes: O = softmax(Q K^T * scale) V for every query row of
+// the layer with keys a(.)K1 + a'(.)Kn and values b(.)V1 + b'(.)Vn ([Deck]
+// frame "FusedKV learns two-source, channel-wise fusion", Eqs. (4)-(5)), or
+// one key and one value source (FusedKV-Lite, [Deck] frame "Lite separates
+// the key source from the value source", Eq. (6); or the plain control).
+// The fusion runs on each 64-token tile as it is staged into LDS, never in
+// HBM ([Notes] section 2.3).  The pages measure such a fused kernel at about
+// 28% below an MHA kernel ([Deck] frame "Prefill improves while kernel
+// throughput falls", Fig. 4): the extra source loads and fusion arithmetic
+// are what this file keeps off the matrix-core critical path.
+//
+// Layout of the work
+//   * A workgroup of 8 waves owns one (batch, KV head, tile of BM query
+//     rows) and all G query heads of that KV head: 8 * 32 = 256 query
+//     columns, BM = 256 / G rows.  Each fused K/V tile is built once in LDS
+//     and consumed by all 256 columns.
+//   * Scores are computed transposed, S^T = K~ Q^T, with
+//     v_mfma_f32_32x32x16_f16: a lane then holds 16 scores of ONE query, so
+//     the row max and row sum are lane-local except for one exchange with
+//     the lane 32 apart.  The probabilities feed the P*V product straight
+//     from registers: the V tile is stored transposed in LDS with its keys
+//     permuted to match the accumulator layout of the score product.
+//   * Tiles are double-buffered in LDS; the global loads of tile j+1 are in
+//     flight while tile j is multiplied, and fused into the other buffer
+//     afterwards (one barrier per tile).
+//   * Softmax is in the log2 domain with scale * log2 e folded into one FMA;
+//     the accumulator is rescaled only when a running max rises.
+//   * Matrix-core operands are IEEE binary16: bf16 inputs (Q, unfused K/V)
+//     convert to it exactly inside its range, and the float32 fused tiles and
+//     probabilities keep 11 significant bits instead of bf16's 8.  The
+//     v_mfma_f32_32x32x16_f16 rate equals the bf16 one, so this costs nothing
+//     and cuts the rounding error of the fused tiles by 8x; magnitudes must
+//     stay below 65504 (the fp16 range).
+//   * Workgroups are mapped so that all query tiles of one (batch, KV head)
+//     run on the same XCD (shared L2 for the K/V tiles), heaviest causal
+//     tiles first.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fkv_internal.h"
+
+namespace fkv {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int BN = 64;  // keys per tile
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> packed fp16 pair, round to nearest even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack2(float lo, float hi)
+{
+    f16x2 v;
+    v[0] = (_Float16)lo;
+    v[1] = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi)
+{
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    bf16x2 v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// A packed pair of bf16 values re-encoded as fp16 (exact inside fp16 range).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) { return pack2(bf16_lo(w), bf16_hi(w)); }
+
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 u)
+{
+    return make_uint4(bf16x2_to_f16x2(u.x), bf16x2_to_f16x2(u.y), bf16x2_to_f16x2(u.z), bf16x2_to_f16x2(u.w));
+}
+
+__device__ __forceinline__ f16x8 as_f16x8(uint4 u) { return __builtin_bit_cast(f16x8, u); }
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+int rows_per_tile(int G) { return (G == 1 || G == 2 || G == 4 || G == 8) ? 256 / G : 0; }
+
+template <int D, bool FUSED, int G>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
+{
+    constexpr int BM = 256 / G;          // query rows per workgroup
+    constexpr int WPH = kWaves / G;      // waves per query head
+    constexpr int DP = (D + 31) / 32 * 32;
+    constexpr int KS = D / 16;           // k-steps of the score product
+    constexpr int KROW = D + 8;          // LDS row pitch of K~ (elements)
+    constexpr int VROW = BN + 8;         // LDS row pitch of V~^T
+    constexpr int CPR = D / 8;           // 16-byte chunks per key row
+    constexpr int RPP = kThreads / CPR;  // key rows per load pass
+    constexpr int KPASS = (BN + RPP - 1) / RPP;
+    constexpr int NVITEM = (D / 2) * (BN / 8);  // (channel pair, key octet) items
+    static_assert(NVITEM <= kThreads, "one V item per thread");
+
+    __shared__ __attribute__((aligned(16))) uint16_t Kt[2][BN * KROW];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][DP * VROW];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    // ---- work item: XCD-aware, heaviest causal tile first ----
+    const int nq = a.n_qtiles;
+    const int items = a.B * a.Hkv * nq;
+    int item = blockIdx.x;
+    if ((items & 7) == 0) item = (blockIdx.x & 7) * (items >> 3) + (blockIdx.x >> 3);
+    const int unit = item / nq;
+    const int qt = a.causal ? nq - 1 - (item - unit * nq) : item - unit * nq;
+    const int b = unit / a.Hkv, g = unit - (unit / a.Hkv) * a.Hkv;
+    const int S = a.S;
+    const int q0 = qt * BM;
+
+    // this wave's 32 query rows of local head hh
+    const int hh = wave / WPH;
+    const int h = g * G + hh;
+    const int r0 = q0 + (wave - hh * WPH) * 32;
+
+    // zero the padded channel rows of V~^T (D < DP); they are never written
+    if constexpr (DP > D) {
+        for (int i = tid; i < (DP - D) * VROW; i += kThreads) {
+            Vt[0][D * VROW + i] = 0;
+            Vt[1][D * VROW + i] = 0;
+        }
+    }
+
+    // ---- queries: B operand of S^T = K~ Q^T, 8 channels per lane per k-step
+    f16x8 qreg[KS];
+    {
+        const int row = r0 + l32;
+        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (((int64_t)b * S + row) * a.Hq + h) * D + hi * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 u = make_uint4(0u, 0u, 0u, 0u);
+            if (row < S) u = *reinterpret_cast<const uint4*>(qp + ks * 16);
+            qreg[ks] = as_f16x8(bf16x8_to_f16x8(u));
+        }
+    }
+
+    // ---- tile loaders ----
+    const int kc = tid % CPR, kr = tid / CPR;  // key chunk column / first row
+    const bool k_active = kr < RPP;
+    const int vj = tid % (D / 2), vo = tid / (D / 2);  // channel pair, key octet
+    const bool v_active = tid < NVITEM;
+    const int vkey0 = (vo >> 1) * 16 + (vo & 1) * 4;   // octet's first key
+
+    float wa[8], wa2[8], wb[2], wb2[2];
+    if constexpr (FUSED) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            wa[c] = k_active ? a.kw1[g * D + kc * 8 + c] : 0.0f;
+            wa2[c] = k_active ? a.kwn[g * D + kc * 8 + c] : 0.0f;
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            wb[c] = v_active ? a.vw1[g * D + 2 * vj + c] : 0.0f;
+            wb2[c] = v_active ? a.vwn[g * D + 2 * vj + c] : 0.0f;
+        }
+    }
+    const uint16_t* k1p = static_cast<const uint16_t*>(a.k1.data) + (int64_t)b * a.k1.sb + (int64_t)g * a.k1.sh;
+    const uint16_t* v1p = static_cast<const uint16_t*>(a.v1.data) + (int64_t)b * a.v1.sb + (int64_t)g * a.v1.sh;
+    const uint16_t* knp = k1p;
+    const uint16_t* vnp = v1p;
+    if constexpr (FUSED) {
+        knp = static_cast<const uint16_t*>(a.kn.data) + (int64_t)b * a.kn.sb + (int64_t)g * a.kn.sh;
+        vnp = static_cast<const uint16_t*>(a.vn.data) + (int64_t)b * a.vn.sb + (int64_t)g * a.vn.sh;
+    }
+
+    uint4 rk1[KPASS], rkn[KPASS];
+    uint32_t rv1[8], rvn[8];
+
+    auto issue_loads = [&](int j) {
+#pragma unroll
+        for (int p = 0; p < KPASS; ++p) {
+            const int row = kr + p * RPP;
+            const int key = j * BN + row;
+            const bool ok = k_active && row < BN && key < S;
+            rk1[p] = make_uint4(0u, 0u, 0u, 0u);
+            rkn[p] = make_uint4(0u, 0u, 0u, 0u);
+            if (ok) {
+                rk1[p] = *reinterpret_cast<const uint4*>(k1p + (int64_t)key * a.k1.ss + kc * 8);
+                if constexpr (FUSED) rkn[p] = *reinterpret_cast<const uint4*>(knp + (int64_t)key * a.kn.ss + kc * 8);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int key = j * BN + vkey0 + (s & 3) + (s >> 2) * 8;
+            const bool ok = v_active && key < S;
+            rv1[s] = 0u;
+            rvn[s] = 0u;
+            if (ok) {
+                rv1[s] = *reinterpret_cast<const uint32_t*>(v1p + (int64_t)key * a.v1.ss + 2 * vj);
+                if constexpr (FUSED) rvn[s] = *reinterpret_cast<const uint32_t*>(vnp + (int64_t)key * a.vn.ss + 2 * vj);
+            }
+        }
+    };
+
+    // fuse the loaded registers (float32) and store fp16 tiles into buffer nb
+    auto store_tile = [&](int nb) {
+#pragma unroll
+        for (int p = 0; p < KPASS; ++p) {
+            const int row = kr + p * RPP;
+            if (k_active && row < BN) {
+                uint4 o;
+                if constexpr (FUSED) {
+                    const uint32_t x1[4] = {rk1[p].x, rk1[p].y, rk1[p].z, rk1[p].w};
+                    const uint32_t xn[4] = {rkn[p].x, rkn[p].y, rkn[p].z, rkn[p].w};
+                    uint32_t r[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float lo = wa[2 * i] * bf16_lo(x1[i]) + wa2[2 * i] * bf16_lo(xn[i]);
+                        const float hi2 = wa[2 * i + 1] * bf16_hi(x1[i]) + wa2[2 * i + 1] * bf16_hi(xn[i]);
+                        r[i] = pack2(lo, hi2);
+                    }
+                    o = make_uint4(r[0], r[1], r[2], r[3]);
+                } else {
+                    o = bf16x8_to_f16x8(rk1[p]);
+                }
+                *reinterpret_cast<uint4*>(&Kt[nb][row * KROW + kc * 8]) = o;
+            }
+        }
+        if (v_active) {
+            uint32_t lo[4], hv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (FUSED) {
+                    const float a0 = wb[0] * bf16_lo(rv1[2 * i]) + wb2[0] * bf16_lo(rvn[2 * i]);
+                    const float a1 = wb[0] * bf16_lo(rv1[2 * i + 1]) + wb2[0] * bf16_lo(rvn[2 * i + 1]);
+                    const float c0 = wb[1] * bf16_hi(rv1[2 * i]) + wb2[1] * bf16_hi(rvn[2 * i]);
+                    const float c1 = wb[1] * bf16_hi(rv1[2 * i + 1]) + wb2[1] * bf16_hi(rvn[2 * i + 1]);
+                    lo[i] = pack2(a0, a1);
+                    hv[i] = pack2(c0, c1);
+                } else {
+                    lo[i] = pack2(bf16_lo(rv1[2 * i]), bf16_lo(rv1[2 * i + 1]));
+                    hv[i] = pack2(bf16_hi(rv1[2 * i]), bf16_hi(rv1[2 * i + 1]));
+                }
+            }
+            *reinterpret_cast<uint4*>(&Vt[nb][(2 * vj) * VROW + vo * 8]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            *reinterpret_cast<uint4*>(&Vt[nb][(2 * vj + 1) * VROW + vo * 8]) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+        }
+    };
+
+    // ---- main loop over key tiles ----
+    const int kend = a.causal ? min(S, q0 + BM) : S;
+    const int nt = (kend + BN - 1) / BN;
+
+    f32x16 oacc[DP / 32];
+#pragma unroll
+    for (int i = 0; i < DP / 32; ++i) oacc[i] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.0f;
+    const int qrow = r0 + l32;
+    const float sl2 = a.scale_log2;
+
+    issue_loads(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int j = 0; j < nt; ++j) {
+        const int buf = j & 1;
+        if (j + 1 < nt) issue_loads(j + 1);
+
+        const int kbase = j * BN;
+        const bool wave_live = !a.causal || kbase <= r0 + 31;
+        if (wave_live) {
+            // S^T = K~ Q^T : two 32-key blocks
+            f32x16 sacc[2] = {f32x16{}, f32x16{}};
+            const uint16_t* kt = &Kt[buf][0];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const uint4 av = *reinterpret_cast<const uint4*>(kt + (kb * 32 + l32) * KROW + ks * 16 + hi * 8);
+                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(av), qreg[ks], sacc[kb], 0, 0, 0);
+                }
+            }
+            // mask: causal diagonal and keys past the end
+            const bool need_mask = (a.causal && kbase + BN - 1 > r0) || kbase + BN > S;
+            if (need_mask) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = kbase + kb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
+                        const bool dead = key >= S || (a.causal && key > qrow);
+                        if (dead) sacc[kb][i] = -INFINITY;
+                    }
+            }
+            // running max (log2 domain)
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx * sl2);
+            if (__any(m_new > m_run)) {
+                const float corr = m_run == -INFINITY ? 0.0f : exp2_fast(m_run - m_new);
+                l_run *= corr;
+#pragma unroll
+                for (int d = 0; d < DP / 32; ++d)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[d][i] *= corr;
+                m_run = m_new;
+            }
+            const float msub = m_run == -INFINITY ? 0.0f : m_run;
+            // probabilities -> fp16 B operands of O^T += V~^T P^T
+            f16x8 pb[4];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float p0 = exp2_fast(sacc[kb][half * 8 + 2 * i] * sl2 - msub);
+                        const float p1 = exp2_fast(sacc[kb][half * 8 + 2 * i + 1] * sl2 - msub);
+                        l_run += p0 + p1;
+                        w[i] = pack2(p0, p1);
+                    }
+                    pb[kb * 2 + half] = as_f16x8(make_uint4(w[0], w[1], w[2], w[3]));
+                }
+            }
+            const uint16_t* vt = &Vt[buf][0];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+#pragma unroll
+                for (int d = 0; d < DP / 32; ++d) {
+                    const uint4 av = *reinterpret_cast<const uint4*>(vt + (d * 32 + l32) * VROW + c * 16 + hi * 8);
+                    oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(av), pb[c], oacc[d], 0, 0, 0);
+                }
+            }
+        }
+        if (j + 1 < nt) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l) ----
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    if (qrow < S) {
+        uint16_t* op = static_cast<uint16_t*>(a.out) + (((int64_t)b * S + qrow) * a.Hq + h) * D;
+#pragma unroll
+        for (int d = 0; d < DP / 32; ++d) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ch = d * 32 + r * 8 + hi * 4;
+                if (ch < D) {
+                    const uint32_t w0 = pack2_bf16(oacc[d][r * 4 + 0] * inv, oacc[d][r * 4 + 1] * inv);
+                    const uint32_t w1 = pack2_bf16(oacc[d][r * 4 + 2] * inv, oacc[d][r * 4 + 3] * inv);
+                    *reinterpret_cast<uint2*>(op + ch) = make_uint2(w0, w1);
+                }
+            }
+        }
+        if (hi == 0 && a.lse)
+            a.lse[((int64_t)b * a.Hq + h) * S + qrow] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+}
+
+template <int D, bool FUSED>
+int launch_g(const PrefillArgs& a, hipStream_t st)
+{
+    const dim3 grid((unsigned)a.B * a.Hkv * a.n_qtiles);
+    switch (a.G) {
+    case 1: hipLaunchKernelGGL((prefill_kernel<D, FUSED, 1>), grid, dim3(kThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<D, FUSED, 2>), grid, dim3(kThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<D, FUSED, 4>), grid, dim3(kThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<D, FUSED, 8>), grid, dim3(kThreads), 0, st, a); break;
+    default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}
+
+template <bool FUSED>
+int launch_d(const PrefillArgs& a, hipStream_t st)
+{
+    switch (a.D) {
+    case 64: return launch_g<64, FUSED>(a, st);
+    case 80: return launch_g<80, FUSED>(a, st);
+    case 96: return launch_g<96, FUSED>(a, st);
+    case 128: return launch_g<128, FUSED>(a, st);
+    default: return (int)hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int prefill_rows_per_tile(int G) { return rows_per_tile(G); }
+
+int launch_prefill(const PrefillArgs& a, bool fused, void* stream)
+{
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (a.B == 0 || a.S == 0) return 0;
+    if ((int64_t)a.B * a.Hkv * a.n_qtiles > 0x7fffffff) return (int)hipErrorInvalidValue;
+    return fused ? launch_d<true>(a, st) : launch_d<false>(a, st);
+}
+
+}  // namespace fkv

@@ -1,0 +1,211 @@
+/*
+ * fusedkv.h -- C ABI of libfusedkv: FusedKV reconstruction-layer attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (by title):
+ *   [Deck]  "FusedKV: Reconstructing KV Caches with Cross-Layer Fusion"
+ *           (reading slides of arXiv:2512.03870v3, Lin et al.)
+ *   [Notes] "FusedKV:通过跨层融合重构 KV 缓存" (reading notes of the same paper)
+ *
+ * The method.  A model of L = 2n layers keeps KV caches only for its lower
+ * half (storage layers 1..n).  Each upper layer i > n rebuilds its keys and
+ * values from the stored post-RoPE caches of layer 1 and layer n with its own
+ * per-channel vectors, broadcast over tokens ([Deck] frame "FusedKV learns
+ * two-source, channel-wise fusion", Eqs. (4)-(5); [Notes] section 2.3):
+ *     K^i = a  (.) K^1 + a' (.) K^n,        V^i = b (.) V^1 + b' (.) V^n
+ * and runs its own layer-specific queries through grouped-query softmax
+ * attention over them.  The reconstruction happens tile by tile inside the
+ * attention kernels and is never written to memory ([Deck] frame "Half the
+ * storage can require 50% more cache I/O"; [Notes] section 2.3).
+ * FusedKV-Lite takes K^i = K^n and V^i = V^1 unchanged ([Deck] frame "Lite
+ * separates the key source from the value source", Eq. (6)); the same
+ * single-source entry points run plain attention of a storage layer over its
+ * own caches, the control.
+ *
+ * Conventions shared by every entry point
+ *   - One call handles one layer.  All work is enqueued on `stream` (a
+ *     hipStream_t; NULL means the default stream) and the call returns after
+ *     the enqueue; nothing is synchronised.
+ *   - Every pointer except the host-side parameter structs is DEVICE memory
+ *     owned by the caller.  The library never allocates or frees memory and
+ *     keeps no pointer after returning.
+ *   - Q and O are contiguous [B, S_q, H_q, D] in the data dtype.  The optional
+ *     LSE output is contiguous float32 [B, H_q, S_q], natural log.
+ *   - A cache is a [B, S_k, H_kv, D] view given by a base pointer and element
+ *     strides for the batch, token and head axes; the channel axis is
+ *     contiguous.  Head-major storage [B, H_kv, S_k, D] (stride_s = D) streams
+ *     best.  Base pointers and every row start must be 16-byte aligned.
+ *   - Query head h reads KV head h / G, G = H_q / H_kv (contiguous groups).
+ *   - softmax scale: 0 selects 1/sqrt(D); negative scales are rejected.
+ *   - Fusion weights are float32 device arrays [H_kv, D] for one layer.  Key
+ *     weights must be equal on the two coordinates of each RoPE pair so that
+ *     fused post-RoPE scores stay relative-position only ([Deck] frame
+ *     "Post-RoPE fusion needs paired key weights", Eqs. (7)-(8); [Notes]
+ *     section 2.4); the kernels do not re-check this (see fkv_check_tied).
+ *
+ * Errors.  Arguments are validated on the host from the parameter structs and
+ * pointer values only (null, alignment, sizes); an invalid call returns a
+ * non-zero status before anything is enqueued, and fkv_last_error() gives the
+ * reason on that thread.  A failed launch returns FKV_ERROR_LAUNCH.  Faults
+ * inside kernels surface at the caller's next synchronisation.  No C++
+ * exception crosses this interface.  Calls are re-entrant.
+ */
+#ifndef FUSEDKV_H_
+#define FUSEDKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FKV_ABI_VERSION 1
+
+typedef enum {
+    FKV_SUCCESS = 0,
+    FKV_ERROR_INVALID_VALUE = 1, /* null/misaligned pointer, bad shape or stride */
+    FKV_ERROR_UNSUPPORTED = 2,   /* valid request outside what the kernels cover */
+    FKV_ERROR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+    FKV_ERROR_LAUNCH = 4         /* the HIP runtime rejected a launch */
+} fkv_status;
+
+typedef enum {
+    FKV_F32 = 0, /* float32 data, float32 arithmetic */
+    FKV_BF16 = 1 /* bfloat16 data, float32 accumulation */
+} fkv_dtype;
+
+/* A [B, S_k, H_kv, D] cache view: element strides for b, s, h. */
+typedef struct {
+    const void* data;
+    int64_t stride_b, stride_s, stride_h;
+} fkv_cache;
+
+typedef struct {
+    int32_t batch;        /* B >= 0 */
+    int32_t seqlen_q;     /* S_q: 1 for decode; S_k for prefill */
+    int32_t seqlen_k;     /* S_k >= 0: cached tokens (the cache's token extent) */
+    int32_t num_q_heads;  /* H_q, a multiple of num_kv_heads */
+    int32_t num_kv_heads; /* H_kv >= 1 */
+    int32_t head_dim;     /* D in {64, 80, 96, 128} */
+    int32_t dtype;        /* fkv_dtype */
+    float softmax_scale;  /* 0 -> 1/sqrt(D); otherwise finite and > 0 */
+    int32_t causal;       /* prefill: 1 = causal mask (query p sees keys t <= p) */
+} fkv_params;
+
+/* Per-layer fusion vectors, device float32 [H_kv, D] each:
+ * k_w1 = a, k_wn = a' (keys), v_w1 = b, v_wn = b' (values). */
+typedef struct {
+    const float* k_w1;
+    const float* k_wn;
+    const float* v_w1;
+    const float* v_wn;
+} fkv_fusion;
+
+/* ABI version of the loaded library (FKV_ABI_VERSION). */
+int fkv_abi_version(void);
+
+/* Static text for a status code. */
+const char* fkv_status_string(fkv_status status);
+
+/* Reason for the last non-success status returned on the calling thread. */
+const char* fkv_last_error(void);
+
+/*
+ * Bytes of device workspace fkv_decode / fkv_lite_decode need for `params`
+ * (split-K partial results and per-(batch, KV head) completion counters);
+ * the size covers both entry points.
+ * Returns 0 when params is invalid.  The caller allocates it and fills it
+ * with zeros ONCE; every call leaves the counters at zero again, so the same
+ * workspace may be reused by later calls on the same stream.  Calls that run
+ * concurrently need separate workspaces.
+ */
+size_t fkv_decode_workspace_size(const fkv_params* params);
+
+/*
+ * fkv_decode -- one decode step (S_q = 1) of a FusedKV reconstruction layer.
+ * [Deck] frame "FusedKV learns two-source, channel-wise fusion", Eqs. (4)-(5);
+ * [Notes] section 2.3 (fuse inside the attention kernel, block by block).
+ *
+ * The query of every batch row attends to keys t in [0, len_b), len_b =
+ * seqlens_k[b] clamped to [0, seqlen_k] (or seqlen_k when seqlens_k is NULL):
+ * the new token's keys are already in the caches of layers 1 and n when the
+ * upper layers run ([Notes] section 2.3).  Keys are a (.) K1 + a' (.) Kn and
+ * values b (.) V1 + b' (.) Vn, formed in float32 in registers and never
+ * stored.  An empty row yields O = 0 and LSE = -inf.
+ *
+ *   q          device [B, 1, H_q, D]
+ *   k1, kn     caches of layers 1 and n (post-RoPE keys)
+ *   v1, vn     value caches of layers 1 and n
+ *   fusion     device weights of this layer (all four non-NULL)
+ *   seqlens_k  device int32 [B] or NULL
+ *   out        device [B, 1, H_q, D], data dtype
+ *   lse        device float32 [B, H_q] or NULL
+ *   workspace  device, >= fkv_decode_workspace_size(params) bytes, 256-byte
+ *              aligned, zero-filled before its first use
+ */
+fkv_status fkv_decode(const fkv_params* params, const void* q,
+                      fkv_cache k1, fkv_cache kn, fkv_cache v1, fkv_cache vn,
+                      const fkv_fusion* fusion, const int32_t* seqlens_k,
+                      void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * fkv_lite_decode -- one decode step over a single key cache and a single
+ * value cache.  FusedKV-Lite passes (K^n, V^1) ([Deck] frame "Lite separates
+ * the key source from the value source", Eq. (6)); plain attention of a
+ * storage layer (the control) passes that layer's own (K^i, V^i).  Arguments
+ * otherwise as fkv_decode.
+ */
+fkv_status fkv_lite_decode(const fkv_params* params, const void* q,
+                           fkv_cache k_src, fkv_cache v_src,
+                           const int32_t* seqlens_k, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * fkv_prefill -- attention of a FusedKV reconstruction layer over a whole
+ * prompt (S_q == S_k), bfloat16 data.  With causal = 1, query row p sees keys
+ * t <= p.  Key and value tiles are fused in float32 and rounded once to IEEE
+ * binary16 for the matrix-core products (bf16 queries convert exactly), and
+ * the softmax probabilities are rounded to binary16 as well; softmax and
+ * accumulation are float32.  Queries, fused keys and fused values must
+ * therefore stay below 65504 in magnitude.  [Deck] frames "FusedKV learns two-source, channel-wise fusion"
+ * (Eqs. (4)-(5)) and "Prefill improves while kernel throughput falls"
+ * (the fused kernel's throughput, paper Fig. 4).
+ *
+ *   q     device [B, S, H_q, D] bfloat16
+ *   out   device [B, S, H_q, D] bfloat16
+ *   lse   device float32 [B, H_q, S] or NULL
+ */
+fkv_status fkv_prefill(const fkv_params* params, const void* q,
+                       fkv_cache k1, fkv_cache kn, fkv_cache v1, fkv_cache vn,
+                       const fkv_fusion* fusion, void* out, float* lse,
+                       void* stream);
+
+/*
+ * fkv_lite_prefill -- prefill over one key cache and one value cache
+ * (FusedKV-Lite with (K^n, V^1), or the plain control with a layer's own
+ * caches).  Arguments otherwise as fkv_prefill.
+ */
+fkv_status fkv_lite_prefill(const fkv_params* params, const void* q,
+                            fkv_cache k_src, fkv_cache v_src, void* out,
+                            float* lse, void* stream);
+
+/*
+ * fkv_check_tied -- host-side check that key fusion weights are tied on RoPE
+ * pairs: |w[h, i] - w[h, j]| <= tol for every pair (i, j) of every head.
+ * pairing 0: interleaved pairs (2j, 2j+1); 1: half-split pairs (j, j + D/2).
+ * host_k_w is HOST float32 [h_kv, d].  Returns FKV_SUCCESS when tied,
+ * FKV_ERROR_INVALID_VALUE when not (or on bad arguments).  [Deck] frame
+ * "Post-RoPE fusion needs paired key weights"; [Notes] section 2.4 (the pair
+ * to tie is the one the RoPE layout actually rotates together).
+ */
+fkv_status fkv_check_tied(const float* host_k_w, int32_t h_kv, int32_t d,
+                          int32_t pairing, float tol);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FUSEDKV_H_ */

@@ -1,0 +1,179 @@
+"""CPU tests of the C ABI: the library loads, exports every declared entry
+point, and rejects invalid calls on the host before anything is enqueued.
+No call here reaches a kernel launch (each one fails validation, or has an
+empty batch)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fusedkv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from cross_layer_kv_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from cross_layer_kv_amd import build
+        build.build()
+    return binding.load_library()
+
+
+@pytest.fixture(scope="module")
+def B():
+    from cross_layer_kv_amd import binding
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fkv_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib, B):
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.fkv_abi_version() == 1
+    for s in range(5):
+        assert lib.fkv_status_string(s)
+    assert lib.fkv_status_string(99) == b"unknown status"
+
+
+FAKE = 0x10000  # 16-byte aligned host value; never dereferenced
+
+
+def _params(B, batch=2, sq=1, sk=64, hq=4, hkv=2, d=64, dtype=1, scale=0.0, causal=0):
+    return B.fkv_params(batch, sq, sk, hq, hkv, d, dtype, scale, causal)
+
+
+def _cache(B, d=64, hkv=2, sk=64, ptr=FAKE):
+    return B.fkv_cache(ptr, hkv * sk * d, d, sk * d)
+
+
+def _fusion(B, ptr=FAKE):
+    return B.fkv_fusion(ptr, ptr + 256, ptr + 512, ptr + 768)
+
+
+def _decode(lib, B, p, q=FAKE, caches=None, fusion="default", ws_bytes=None, ws=FAKE, seqlens=None, lse=None,
+            out=FAKE):
+    c = caches or [_cache(B, p.head_dim, p.num_kv_heads, p.seqlen_k)] * 4
+    f = _fusion(B) if fusion == "default" else fusion
+    if ws_bytes is None:
+        ws_bytes = lib.fkv_decode_workspace_size(ctypes.byref(p)) if p else 0
+    return lib.fkv_decode(ctypes.byref(p) if p else None, q, c[0], c[1], c[2], c[3],
+                          ctypes.byref(f) if f is not None else None, seqlens, out, lse, ws, ws_bytes, None)
+
+
+def _prefill(lib, B, p, q=FAKE, caches=None, fusion="default"):
+    c = caches or [_cache(B, p.head_dim, p.num_kv_heads, p.seqlen_k)] * 4
+    f = _fusion(B) if fusion == "default" else fusion
+    return lib.fkv_prefill(ctypes.byref(p), q, c[0], c[1], c[2], c[3],
+                           ctypes.byref(f) if f is not None else None, FAKE, None, None)
+
+
+def test_decode_validation_codes(lib, B):
+    INV, UNS, WS = B.FKV_ERROR_INVALID_VALUE, B.FKV_ERROR_UNSUPPORTED, B.FKV_ERROR_WORKSPACE
+    assert lib.fkv_decode(None, FAKE, _cache(B), _cache(B), _cache(B), _cache(B), None, None, FAKE, None,
+                          FAKE, 1 << 20, None) == INV
+    assert lib.fkv_last_error()
+    assert _decode(lib, B, _params(B, hq=5, hkv=2)) == INV
+    assert _decode(lib, B, _params(B, d=72)) == UNS
+    assert _decode(lib, B, _params(B, hq=6, hkv=2)) == UNS        # G = 3
+    assert _decode(lib, B, _params(B, sq=2)) == INV
+    assert _decode(lib, B, _params(B, dtype=7)) == INV
+    assert _decode(lib, B, _params(B, scale=-1.0)) == INV
+    assert _decode(lib, B, _params(B, scale=float("nan"))) == INV
+    assert _decode(lib, B, _params(B, batch=-1)) == INV
+    assert _decode(lib, B, _params(B), q=FAKE + 8) == INV           # misaligned q
+    assert _decode(lib, B, _params(B), out=0) == INV
+    assert _decode(lib, B, _params(B), fusion=None) == INV
+    assert _decode(lib, B, _params(B), fusion=B.fkv_fusion(FAKE, 0, FAKE, FAKE)) == INV
+    assert _decode(lib, B, _params(B), lse=FAKE + 2) == INV
+    bad = B.fkv_cache(FAKE, 2 * 64 * 64, 60, 64 * 64)             # row stride breaks alignment
+    assert _decode(lib, B, _params(B), caches=[bad] * 4) == INV
+    overlap = B.fkv_cache(FAKE, 2 * 64 * 64, 32, 64 * 64)         # token stride < D
+    assert _decode(lib, B, _params(B), caches=[overlap] * 4) == INV
+    assert _decode(lib, B, _params(B), caches=[B.fkv_cache(0, 0, 64, 0)] * 4) == INV
+    # a NULL cache is accepted only when it holds no tokens (it is never read)
+    assert _decode(lib, B, _params(B, batch=0, sk=0), caches=[B.fkv_cache(0, 0, 64, 0)] * 4) == B.FKV_SUCCESS
+    p = _params(B)
+    need = lib.fkv_decode_workspace_size(ctypes.byref(p))
+    assert _decode(lib, B, p, ws_bytes=need - 1) == WS
+    assert _decode(lib, B, p, ws=0) == WS
+    assert _decode(lib, B, p, ws=FAKE + 16) == WS                  # not 256-byte aligned
+    # an empty batch is a valid no-op: nothing is launched
+    assert _decode(lib, B, _params(B, batch=0)) == B.FKV_SUCCESS
+    assert lib.fkv_last_error() == b""
+
+
+def test_lite_decode_validation_codes(lib, B):
+    p = _params(B, sq=3)
+    c = _cache(B)
+    assert lib.fkv_lite_decode(ctypes.byref(p), FAKE, c, c, None, FAKE, None, FAKE, 1 << 20, None) == \
+        B.FKV_ERROR_INVALID_VALUE
+    p = _params(B, batch=0)
+    assert lib.fkv_lite_decode(ctypes.byref(p), FAKE, c, c, None, FAKE, None, FAKE, 0, None) == B.FKV_SUCCESS
+
+
+def test_prefill_validation_codes(lib, B):
+    INV, UNS = B.FKV_ERROR_INVALID_VALUE, B.FKV_ERROR_UNSUPPORTED
+    assert _prefill(lib, B, _params(B, sq=64, sk=64, dtype=0)) == UNS   # f32 prefill
+    assert _prefill(lib, B, _params(B, sq=32, sk=64)) == UNS            # S_q != S_k
+    assert _prefill(lib, B, _params(B, sq=64, sk=64, causal=2)) == INV
+    assert _prefill(lib, B, _params(B, sq=64, sk=64, d=100)) == UNS
+    assert _prefill(lib, B, _params(B, sq=64, sk=64), fusion=None) == INV
+    assert _prefill(lib, B, _params(B, sq=64, sk=64), q=FAKE + 4) == INV
+    assert _prefill(lib, B, _params(B, batch=0, sq=64, sk=64)) == B.FKV_SUCCESS
+    assert _prefill(lib, B, _params(B, sq=0, sk=0)) == B.FKV_SUCCESS
+    p = _params(B, sq=64, sk=64)
+    c = _cache(B)
+    assert lib.fkv_lite_prefill(ctypes.byref(p), FAKE, c, B.fkv_cache(0, 0, 64, 0), FAKE, None, None) == INV
+
+
+def test_workspace_size(lib, B):
+    assert lib.fkv_decode_workspace_size(None) == 0
+    p = _params(B, sq=2)
+    assert lib.fkv_decode_workspace_size(ctypes.byref(p)) == 0
+    # 650M-shape decode: B=32, Hkv=8, S=8192, D=96, G=2
+    p = _params(B, batch=32, sk=8192, hq=16, hkv=8, d=96)
+    n = lib.fkv_decode_workspace_size(ctypes.byref(p))
+    units, G, D = 32 * 8, 2, 96
+    # splits of the two-source plan: 1280 workgroups / 256 units -> 5 splits of 1664 tokens
+    ns = 5
+    expect = 1024 + math.ceil(units * ns * G * 2 * 4 / 256) * 256 + units * ns * G * D * 4
+    assert n == expect
+    # empty cache still gets room for one (empty) split per unit
+    p = _params(B, sk=0)
+    assert lib.fkv_decode_workspace_size(ctypes.byref(p)) > 0
+
+
+def test_check_tied(lib, B):
+    from cross_layer_kv_amd import inputs
+    for pairing in ("interleaved", "half"):
+        kw1, kwn, vw1, _ = inputs.make_weights(3, 16, 1, pairing=pairing)
+        assert B.fkv_check_tied(kw1, pairing)
+        assert B.fkv_check_tied(kwn, pairing)
+        assert not B.fkv_check_tied(vw1, pairing)
+    kw1, _, _, _ = inputs.make_weights(2, 8, 2, pairing="half")
+    assert not B.fkv_check_tied(kw1, "interleaved")
+    w = torch.ones(2, 8)
+    w[1, 3] += 1e-3
+    assert not B.fkv_check_tied(w, "interleaved", 1e-4)
+    assert B.fkv_check_tied(w, "interleaved", 1e-2)
+    assert lib.fkv_check_tied(None, 2, 8, 0, 0.0) == B.FKV_ERROR_INVALID_VALUE
+    assert lib.fkv_check_tied(ctypes.c_void_p(w.data_ptr()), 2, 7, 0, 0.0) == B.FKV_ERROR_INVALID_VALUE
+
+
+def test_binding_refuses_host_tensors(B):
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    w = [torch.zeros(2, 64)] * 4
+    with pytest.raises(TypeError):
+        B.fkv_decode(q, k, k, k, k, w, out=q, workspace=torch.zeros(4096, dtype=torch.uint8))

@@ -1,0 +1,160 @@
+"""GPU parity of fkv_decode / fkv_lite_decode against the fp64 oracle, through
+the C ABI.  Every test prints its case before touching the GPU."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from cross_layer_kv_amd import binding, inputs
+from parity import TOL, gpu_rows, lse_err, oracle_layer, rel_err, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def run_decode(L, fused=True, single=("kn", "v1"), ws=None):
+    B, _, Hq, D = L.q.shape
+    out = torch.full_like(L.q, float("nan"))
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=DEV)
+    if ws is None:
+        ws = binding.decode_workspace(L.q, L.k1)
+    if fused:
+        binding.fkv_decode(L.q, L.k1, L.kn, L.v1, L.vn, L.weights, out=out, lse=lse, workspace=ws,
+                           seqlens_k=L.seqlens_k)
+    else:
+        binding.fkv_lite_decode(L.q, getattr(L, single[0]), getattr(L, single[1]), out=out, lse=lse,
+                                workspace=ws, seqlens_k=L.seqlens_k)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def check(L, fused=True, single=("kn", "v1"), tol=None):
+    B, _, Hq, D = L.q.shape
+    out, lse = run_decode(L, fused, single)
+    ro, rl = oracle_layer(L, fused=fused, single=single)
+    tol = tol or TOL[L.q.dtype]
+    e = rel_err(gpu_rows(out, B, Hq, 1, D), ro)
+    el = lse_err(lse.cpu().numpy().reshape(-1), rl)
+    say("  err=%.3e lse_err=%.3e tol=%.0e" % (e, el, tol))
+    assert e <= tol and el <= tol, (e, el)
+    return out, lse
+
+
+def test_tiny_fp32_config_fused_and_lite():
+    """Tiny decode: B=1, S=1024, Hq=4, Hkv=2, D=64, fp32, FusedKV and Lite."""
+    say("decode tiny fp32 B=1 S=1024 Hq=4 Hkv=2 D=64 seed=0xF0001")
+    L = inputs.make_layer(1, 1, 1024, 4, 2, 64, torch.float32, 0xF0001, DEV)
+    check(L, fused=True)
+    check(L, fused=False)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("D", [64, 80, 96, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_head_dims_and_gqa_ratios(dtype, D, G):
+    Hkv = 2
+    say("decode sweep dtype=%s D=%d G=%d B=2 S=333" % (dtype, D, G))
+    L = inputs.make_layer(2, 1, 333, Hkv * G, Hkv, D, dtype, 100 + D + G, DEV)
+    check(L, fused=True)
+    check(L, fused=False)
+
+
+@pytest.mark.parametrize("layout", ["bhsd", "bshd"])
+def test_layouts_and_ragged_lengths(layout):
+    say("decode layout=%s ragged seqlens" % layout)
+    L = inputs.make_layer(5, 1, 517, 16, 8, 96, torch.bfloat16, 7, DEV, layout=layout,
+                          seqlens_k=[517, 1, 0, 64, 300])
+    out, lse = check(L, fused=True)
+    # the empty row: O = 0 and LSE = -inf exactly
+    assert torch.all(out[2] == 0) and torch.all(torch.isneginf(lse[2]))
+    check(L, fused=False)
+
+
+def test_empty_cache():
+    say("decode seqlen_k=0")
+    L = inputs.make_layer(2, 1, 0, 4, 2, 64, torch.bfloat16, 9, DEV)
+    out, lse = run_decode(L)
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 64])
+def test_forced_split_counts(splits, monkeypatch):
+    monkeypatch.setenv("FKV_DECODE_SPLITS", str(splits))
+    say("decode forced splits=%d" % splits)
+    L = inputs.make_layer(2, 1, 4100, 8, 4, 128, torch.bfloat16, 11, DEV)
+    check(L, fused=True)
+    check(L, fused=False)
+
+
+def test_selector_weights_equal_lite_bitwise(monkeypatch):
+    """(a, a', b, b') = (0, 1, 1, 0) makes the fused kernel read exactly K^n
+    and V^1; with the same split plan it must agree with the Lite kernel bit
+    for bit ([Deck] frame "Lite separates the key source from the value
+    source", Eq. (6))."""
+    monkeypatch.setenv("FKV_DECODE_SPLITS", "5")
+    say("decode selector weights vs lite")
+    L = inputs.make_layer(3, 1, 1000, 8, 4, 80, torch.bfloat16, 12, DEV)
+    z = torch.zeros_like(L.weights[0])
+    o = torch.ones_like(L.weights[0])
+    L.weights = (z, o, o, z)
+    of, lf = run_decode(L, fused=True)
+    ol, ll = run_decode(L, fused=False, single=("kn", "v1"))
+    assert torch.equal(of, ol) and torch.equal(lf, ll)
+
+
+def test_workspace_reuse_is_deterministic():
+    say("decode repeated calls on one workspace")
+    L = inputs.make_layer(4, 1, 2000, 16, 8, 128, torch.bfloat16, 13, DEV)
+    ws = binding.decode_workspace(L.q, L.k1)
+    a = run_decode(L, ws=ws)
+    b = run_decode(L, ws=ws)
+    c = run_decode(L, fused=False, ws=ws)
+    d = run_decode(L, ws=ws)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[0], d[0])
+    assert not torch.equal(a[0], c[0])
+    # counters are back at zero after every call
+    assert int(ws[:4 * 4 * 8].view(torch.int32).abs().sum()) == 0
+
+
+def test_vanilla_control_on_own_caches():
+    """Plain storage-layer attention: the single-source kernel over (K^1, V^1)."""
+    say("decode vanilla control (K1, V1)")
+    L = inputs.make_layer(2, 1, 700, 16, 8, 128, torch.bfloat16, 14, DEV)
+    check(L, fused=False, single=("k1", "v1"))
+
+
+def _sampled(B, S, Hq, Hkv, D, seed, n_batches=2, n_heads=None, layers=1):
+    say("decode full size B=%d S=%d Hq=%d Hkv=%d D=%d seed=%#x (sampled rows)" % (B, S, Hq, Hkv, D, seed))
+    L = inputs.make_layer(B, 1, S, Hq, Hkv, D, torch.bfloat16, seed, DEV)
+    rng = np.random.default_rng(seed)
+    bs = sorted(set([0, B - 1] + list(rng.integers(0, B, size=max(0, n_batches - 2)))))
+    for fused in (True, False):
+        out, lse = run_decode(L, fused=fused)
+        ro, rl = oracle_layer(L, fused=fused, batch=bs)
+        got = gpu_rows(out[bs], len(bs), Hq, 1, D)
+        e = rel_err(got, ro)
+        el = lse_err(lse[bs].cpu().numpy().reshape(-1), rl)
+        say("  fused=%s batches=%s err=%.3e lse_err=%.3e" % (fused, bs, e, el))
+        assert e <= 1e-2 and el <= 1e-2
+        # every row finite
+        assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    del L
+    torch.cuda.empty_cache()
+
+
+def test_full_size_650m_decode():
+    """650M shape: B=32, S=8192, 16/8 heads, D=96, bf16 (the benchmarked
+    launch configuration); oracle on every head of sampled batch rows."""
+    _sampled(32, 8192, 16, 8, 96, 0xF0002, n_batches=3)
+
+
+def test_full_size_4b_decode():
+    """4B shape: B=16, S=32768, 32/16 heads, D=80."""
+    _sampled(16, 32768, 32, 16, 80, 0xF0004, n_batches=2)
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_full_size_long_context_decode(B):
+    """Long context: S=131072, 16/8 heads, D=128, batch 1 and 8."""
+    _sampled(B, 131072, 16, 8, 128, 0xF0005, n_batches=2)

@@ -1,0 +1,131 @@
+"""GPU parity of fkv_prefill / fkv_lite_prefill (bf16 MFMA) against the fp64
+oracle, through the C ABI.  Every test prints its case before touching the
+GPU."""
+import numpy as np
+import pytest
+import torch
+
+from cross_layer_kv_amd import binding, inputs
+from parity import gpu_rows, lse_err, oracle_layer, rel_err, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = 1e-2
+
+
+def run_prefill(L, fused=True, causal=True, single=("kn", "v1")):
+    B, S, Hq, D = L.q.shape
+    out = torch.full_like(L.q, float("nan"))
+    lse = torch.full((B, Hq, S), float("nan"), dtype=torch.float32, device=DEV)
+    if fused:
+        binding.fkv_prefill(L.q, L.k1, L.kn, L.v1, L.vn, L.weights, out=out, lse=lse, causal=causal)
+    else:
+        binding.fkv_lite_prefill(L.q, getattr(L, single[0]), getattr(L, single[1]), out=out, lse=lse,
+                                 causal=causal)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def check(L, fused=True, causal=True, single=("kn", "v1")):
+    B, S, Hq, D = L.q.shape
+    out, lse = run_prefill(L, fused, causal, single)
+    ro, rl = oracle_layer(L, fused=fused, causal=causal, single=single)
+    e = rel_err(gpu_rows(out, B, Hq, S, D), ro)
+    el = lse_err(lse.cpu().numpy().reshape(-1), rl)
+    say("  err=%.3e lse_err=%.3e" % (e, el))
+    assert e <= TOL and el <= TOL, (e, el)
+    return out, lse
+
+
+@pytest.mark.parametrize("D", [64, 80, 96, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_head_dims_and_gqa_ratios(D, G):
+    say("prefill sweep D=%d G=%d B=1 S=200 causal" % (D, G))
+    L = inputs.make_layer(1, 200, 200, 2 * G, 2, D, torch.bfloat16, 200 + D + G, DEV, decode=False)
+    check(L, fused=True)
+    check(L, fused=False)
+
+
+@pytest.mark.parametrize("S", [1, 63, 64, 65, 130, 257, 600])
+def test_ragged_lengths(S):
+    say("prefill ragged S=%d D=128 G=2" % S)
+    L = inputs.make_layer(2, S, S, 4, 2, 128, torch.bfloat16, 300 + S, DEV, decode=False)
+    check(L, fused=True)
+    check(L, fused=False)
+
+
+@pytest.mark.parametrize("D", [80, 128])
+def test_non_causal(D):
+    say("prefill non-causal D=%d S=190" % D)
+    L = inputs.make_layer(1, 190, 190, 4, 2, D, torch.bfloat16, 400 + D, DEV, decode=False)
+    check(L, fused=True, causal=False)
+    check(L, fused=False, causal=False)
+
+
+@pytest.mark.parametrize("layout", ["bhsd", "bshd"])
+def test_layouts(layout):
+    say("prefill layout=%s" % layout)
+    L = inputs.make_layer(2, 300, 300, 16, 8, 96, torch.bfloat16, 500, DEV, layout=layout, decode=False)
+    check(L, fused=True)
+
+
+def test_selector_weights_equal_lite_bitwise():
+    """(0, 1, 1, 0) weights give K~ = K^n and V~ = V^1 exactly (also after the
+    bf16 rounding of the fused tiles), so the fused kernel must equal the Lite
+    kernel bit for bit."""
+    say("prefill selector weights vs lite")
+    L = inputs.make_layer(1, 333, 333, 8, 4, 80, torch.bfloat16, 600, DEV, decode=False)
+    z = torch.zeros_like(L.weights[0])
+    o = torch.ones_like(L.weights[0])
+    L.weights = (z, o, o, z)
+    of, lf = run_prefill(L, fused=True)
+    ol, ll = run_prefill(L, fused=False)
+    assert torch.equal(of, ol) and torch.equal(lf, ll)
+
+
+def test_vanilla_control_on_own_caches():
+    say("prefill vanilla control (K1, V1)")
+    L = inputs.make_layer(1, 257, 257, 16, 8, 128, torch.bfloat16, 700, DEV, decode=False)
+    check(L, fused=False, single=("k1", "v1"))
+
+
+def _sample_rows(B, Hq, S, bm, rng, per_bh=16):
+    """Stratified rows: first/last rows, rows around tile boundaries and
+    random rows for a few (b, h) pairs."""
+    rows = []
+    bhs = [(0, 0), (B - 1, Hq - 1), (int(rng.integers(B)), int(rng.integers(Hq)))]
+    for b, h in bhs:
+        ps = {0, 1, S - 1, S - 2}
+        for t in range(bm, S, bm * 7):
+            ps.update({t - 1, t})
+        ps.update(int(x) for x in rng.integers(0, S, size=per_bh))
+        rows += [(b * Hq + h) * S + p for p in sorted(ps) if 0 <= p < S]
+    return np.array(sorted(set(rows)), dtype=np.int64)
+
+
+def _full_size(B, S, Hq, Hkv, D, seed):
+    say("prefill full size B=%d S=%d Hq=%d Hkv=%d D=%d seed=%#x (sampled rows)" % (B, S, Hq, Hkv, D, seed))
+    L = inputs.make_layer(B, S, S, Hq, Hkv, D, torch.bfloat16, seed, DEV, decode=False)
+    rng = np.random.default_rng(seed)
+    rows = _sample_rows(B, Hq, S, 256 // (Hq // Hkv), rng)
+    for fused in (True, False):
+        out, lse = run_prefill(L, fused=fused)
+        assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+        ro, rl = oracle_layer(L, fused=fused, causal=True, rows=rows)
+        got = gpu_rows(out, B, Hq, S, D)[rows]
+        e = rel_err(got, ro)
+        el = lse_err(lse.cpu().numpy().reshape(-1)[rows], rl)
+        say("  fused=%s rows=%d err=%.3e lse_err=%.3e" % (fused, rows.size, e, el))
+        assert e <= TOL and el <= TOL
+    del L
+    torch.cuda.empty_cache()
+
+
+def test_full_size_1p5b_prefill():
+    """1.5B shape: B=4, S=8192, 16/8 heads, D=128 (the benchmarked launch)."""
+    _full_size(4, 8192, 16, 8, 128, 0xF0003)
+
+
+def test_full_size_4b_prefill():
+    """4B shape: B=1, S=16384, 32/16 heads, D=80."""
+    _full_size(1, 16384, 32, 16, 80, 0xF0004)
