@@ -3,7 +3,7 @@
 // only the host-side parameter structs and pointer values, so an invalid call
 // returns before anything is enqueued.  The device work is in
 // fkv_decode.hip / fkv_prefill.hip.
-#include "../../include/fusedkv.h"
+#include "fusedkv.h"
 #include "fkv_internal.h"
 
 #include <cmath>
@@ -91,31 +91,30 @@ float scale_log2_of(const fkv_params* p)
     return (float)(s * 1.4426950408889634); // log2(e)
 }
 
-// Split plan for decode.  Every split covers a multiple of 64 tokens (one
-// workgroup iteration).  The workgroup count aims at one resident wave of
-// workgroups on a 256-CU part: the four-source kernel keeps 3 workgroups per
-// CU resident, the two-source kernel 5, so all splits run at once and no
-// tail round is left.  The count is capped at 256 splits so the merge stays
-// cheap.  The plan depends on the parameters only (no device query), so the
-// workspace size is a pure function of them.  FKV_DECODE_SPLITS overrides the
-// split count, FKV_DECODE_WGS the workgroup target.
+// Split plan for decode.  A workgroup of `waves` waves (decode_waves) fills
+// one compute unit, so the plan aims at one workgroup per CU of a 256-CU
+// part: one split per (batch, KV head) when there are at least 256 of them,
+// otherwise enough splits of the key axis to reach 256 workgroups, each split
+// covering at least one workgroup iteration (waves * 16 tokens).  Splits are
+// multiples of 64 tokens and at most 256.  The plan depends on the
+// parameters only (no device query), so the workspace size is a pure function
+// of them.  FKV_DECODE_SPLITS overrides the split count (tuning and tests).
 fkv::DecodePlan plan_decode(const fkv_params* p, bool fused)
 {
     fkv::DecodePlan pl{};
+    const int64_t G = p->num_q_heads / p->num_kv_heads;
+    pl.waves = fkv::decode_waves(p->dtype == FKV_F32, fused, (int)G);
     const int64_t units = (int64_t)p->batch * p->num_kv_heads;
     const int64_t S = p->seqlen_k;
-    const int64_t max_splits = S > 0 ? (S + 63) / 64 : 1;
-    int64_t target = fused ? 768 : 1280;
-    if (const char* env = std::getenv("FKV_DECODE_WGS")) {
-        const long v = std::strtol(env, nullptr, 10);
-        if (v > 0) target = v;
-    }
-    int64_t ns = units > 0 ? (target + units - 1) / units : 1;
+    const int64_t iter = (int64_t)pl.waves * 16;
+    const int64_t max_splits = S > 0 ? (S + iter - 1) / iter : 1;
+    int64_t ns = units > 0 ? (256 + units - 1) / units : 1;
     if (const char* env = std::getenv("FKV_DECODE_SPLITS")) {
         const long v = std::strtol(env, nullptr, 10);
         if (v > 0) ns = v;
+    } else if (ns > max_splits) {
+        ns = max_splits;
     }
-    if (ns > max_splits) ns = max_splits;
     if (ns > 256) ns = 256;
     if (ns < 1) ns = 1;
     int64_t chunk = S > 0 ? (S + ns - 1) / ns : 64;
@@ -123,11 +122,11 @@ fkv::DecodePlan plan_decode(const fkv_params* p, bool fused)
     ns = S > 0 ? (S + chunk - 1) / chunk : 1;
     pl.n_splits = (int32_t)ns;
     pl.chunk = (int32_t)chunk;
-    const int64_t G = p->num_q_heads / p->num_kv_heads;
-    pl.counters_bytes = (size_t)((units * 4 + 255) / 256 * 256);
-    pl.ml_bytes = (size_t)((units * ns * G * 2 * 4 + 255) / 256 * 256);
-    pl.part_bytes = (size_t)(units * ns * G * p->head_dim * 4);
-    pl.total_bytes = pl.counters_bytes + pl.ml_bytes + pl.part_bytes;
+    if (ns > 1) {
+        pl.ml_bytes = (size_t)((units * ns * G * 2 * 4 + 255) / 256 * 256);
+        pl.part_bytes = (size_t)(units * ns * G * p->head_dim * 4);
+    }
+    pl.total_bytes = pl.ml_bytes + pl.part_bytes;
     return pl;
 }
 
@@ -156,13 +155,14 @@ fkv_status decode_common(const fkv_params* p, const void* q, const fkv_cache* ca
             !aligned16(fusion->v_wn))
             return fail(FKV_ERROR_INVALID_VALUE, "fusion weights are not 16-byte aligned");
     }
-    const bool fused_plan = ncaches == 4;
-    const fkv::DecodePlan pl = plan_decode(p, fused_plan);
-    if (!workspace || workspace_bytes < pl.total_bytes)
-        return fail(FKV_ERROR_WORKSPACE, "workspace needs %zu bytes (got %zu)", pl.total_bytes,
-                    workspace ? workspace_bytes : (size_t)0);
-    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
-        return fail(FKV_ERROR_WORKSPACE, "workspace is not 256-byte aligned");
+    const fkv::DecodePlan pl = plan_decode(p, fused);
+    if (pl.total_bytes > 0) {
+        if (!workspace || workspace_bytes < pl.total_bytes)
+            return fail(FKV_ERROR_WORKSPACE, "workspace needs %zu bytes (got %zu)", pl.total_bytes,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+            return fail(FKV_ERROR_WORKSPACE, "workspace is not 256-byte aligned");
+    }
 
     fkv::DecodeArgs a{};
     a.q = q;
@@ -180,9 +180,8 @@ fkv_status decode_common(const fkv_params* p, const void* q, const fkv_cache* ca
     a.out = out;
     a.lse = lse;
     char* ws = static_cast<char*>(workspace);
-    a.counters = reinterpret_cast<unsigned*>(ws);
-    a.ml = reinterpret_cast<float*>(ws + pl.counters_bytes);
-    a.part = reinterpret_cast<float*>(ws + pl.counters_bytes + pl.ml_bytes);
+    a.ml = pl.total_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+    a.part = pl.total_bytes ? reinterpret_cast<float*>(ws + pl.ml_bytes) : nullptr;
     a.B = p->batch;
     a.Sk = p->seqlen_k;
     a.Hq = p->num_q_heads;
@@ -193,9 +192,9 @@ fkv_status decode_common(const fkv_params* p, const void* q, const fkv_cache* ca
     a.chunk = pl.chunk;
     a.scale_log2 = scale_log2_of(p);
     if (std::getenv("FKV_TRACE"))
-        std::fprintf(stderr, "libfusedkv: decode %s B=%d Sk=%d Hq=%d Hkv=%d D=%d splits=%d chunk=%d\n",
-                     fused ? "fused" : "single", a.B, a.Sk, a.Hq, a.Hkv, a.D, a.n_splits, a.chunk);
-    const int rc = fkv::launch_decode(a, fused, p->dtype, stream);
+        std::fprintf(stderr, "libfusedkv: decode %s B=%d Sk=%d Hq=%d Hkv=%d D=%d waves=%d splits=%d chunk=%d\n",
+                     fused ? "fused" : "single", a.B, a.Sk, a.Hq, a.Hkv, a.D, pl.waves, a.n_splits, a.chunk);
+    const int rc = fkv::launch_decode(a, fused, p->dtype, pl.waves, stream);
     if (rc) return fail(FKV_ERROR_LAUNCH, "decode launch failed (HIP error %d)", rc);
     return ok();
 }

@@ -16,21 +16,24 @@
 // Decode is bound by HBM: every cached element is read once and used for a
 // handful of flops ([Deck] frame "Decode cost depends on the inference
 // regime": memory-bound TPOT of FusedKV is about 1.5x vanilla over a model).
-// The design therefore aims only at streaming the four source caches at full
+// The design therefore aims only at streaming the source caches at full
 // bandwidth with little VALU work per byte:
-//   * work unit = (batch, KV head, split of the key axis); all G query heads
-//     of the KV head live in the same lanes, so each fused element is built
-//     once and used G times;
+//   * a workgroup owns one (batch, KV head) -- or a split of its key axis
+//     when there are too few of them to fill the chip -- and all G query heads
+//     of that KV head, so each fused element is built once and used G times;
+//     its waves stream consecutive 16-token slices;
 //   * a lane owns 8 channels (one 16-byte bf16 load, two for f32) of one
-//     token; the D/8 lanes of a token form a 8- or 16-lane group, and the
+//     token; the D/8 lanes of a token form an 8- or 16-lane group, and the
 //     score of that token is a DPP butterfly sum inside the group;
 //   * each lane runs its own online softmax over the tokens its group sees;
-//     groups, waves and finally splits are merged with the usual
-//     (max, sum) rescaling, all in the log2 domain (scale * log2 e is folded
+//     groups (lane exchanges), waves (LDS) and splits are merged with the
+//     usual (max, sum) rescaling, in the log2 domain (scale * log2 e is folded
 //     into the query);
-//   * the last workgroup of a (batch, KV head) to finish -- found with a
-//     completion counter in the workspace -- merges the splits and writes O
-//     and LSE, so one call is one kernel launch.  It resets the counter.
+//   * with one split per (batch, KV head) the workgroup writes O and LSE
+//     directly; otherwise a second, small kernel merges the splits.  No
+//     workgroup waits on another, and no device-scope fence is needed: on
+//     this part such a fence writes back the L2, and one per workgroup cost
+//     more than a third of the kernel's time when it was measured.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -40,9 +43,8 @@
 namespace fkv {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kIterTokens = 64;  // tokens per workgroup iteration
+constexpr int kWaveTokens = 16;  // tokens per wave per iteration
+constexpr int kCombineThreads = 256;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -91,10 +93,11 @@ __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x)
 {
-    // round to nearest even; NaN stays a quiet NaN
-    const uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    bf16x2 v;
+    v[0] = (__bf16)x;  // round to nearest even
+    v[1] = (__bf16)0.0f;
+    return (uint16_t)(__builtin_bit_cast(uint32_t, v) & 0xffffu);
 }
 
 // Sum over the LPT lanes of a token group with DPP lane permutations:
@@ -117,20 +120,17 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // Weight of a partial (max m) relative to a common max M; 0 for an empty one.
 __device__ __forceinline__ float rel(float m, float M) { return m == -INFINITY ? 0.0f : exp2_fast(m - M); }
 
-template <typename T, int D, bool FUSED, int G>
-__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
+template <typename T, int D, bool FUSED, int G, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_kernel(const DecodeArgs a)
 {
+    constexpr int NT = 64 * NW;
     constexpr int NP = D / 8;              // 8-channel pieces per row
     constexpr int LPT = NP <= 8 ? 8 : 16;  // lanes per token group
     constexpr int TPW = 64 / LPT;          // tokens per wave step
-    constexpr int U = kIterTokens / (kWaves * TPW);  // steps per iteration
+    constexpr int U = kWaveTokens / TPW;   // steps per iteration
 
-    __shared__ float s_acc[kWaves][G][D];
-    __shared__ float s_ml[kWaves][G][2];
-    __shared__ float s_w[256 * G];
-    __shared__ float4 s_red[kThreads];
-    __shared__ float s_M[G], s_L[G];
-    __shared__ int s_last;
+    __shared__ float s_acc[NW][G][D];
+    __shared__ float s_ml[NW][G][2];
 
     const int split = blockIdx.x;
     const int bg = blockIdx.y;  // b * Hkv + g
@@ -190,12 +190,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
         for (int c = 0; c < 8; ++c) acc[hh][c] = 0.0f;
     }
 
-    for (int t0 = t_begin; t0 < t_end; t0 += kIterTokens) {
+    for (int t0 = t_begin + wave * kWaveTokens; t0 < t_end; t0 += NW * kWaveTokens) {
         Raw8<T> rk1[U], rkn[U], rv1[U], rvn[U];
         bool ok[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int t = t0 + (wave * U + u) * TPW + grp;
+            const int t = t0 + u * TPW + grp;
             ok[u] = t < t_end;
             const bool pr = active && ok[u];
             load8(rk1[u], k1p + (int64_t)t * a.k1.ss, pr);
@@ -292,39 +292,51 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
     }
     __syncthreads();
 
-    // merge the waves; write this split's partial (unnormalised) result
+    // merge the waves; write O/LSE (one split) or this split's partial row
+    const bool final_out = a.n_splits == 1;
     const int64_t slot = (int64_t)bg * a.n_splits + split;
-    for (int e = tid; e < G * D; e += kThreads) {
+    for (int e = tid; e < G * D; e += NT) {
         const int hh = e / D, d = e - (e / D) * D;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][hh][0]);
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, s_ml[w][hh][0]);
         float o = 0.0f, ls = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < NW; ++w) {
             const float f = rel(s_ml[w][hh][0], M);
             o += s_acc[w][hh][d] * f;
             ls += s_ml[w][hh][1] * f;
         }
-        a.part[slot * G * D + e] = o;
-        if (d == 0) {
-            a.ml[(slot * G + hh) * 2 + 0] = M;
-            a.ml[(slot * G + hh) * 2 + 1] = ls;
+        if (final_out) {
+            const int64_t row = (int64_t)b * a.Hq + (int64_t)g * G + hh;
+            static_cast<T*>(a.out)[row * D + d] = from_f32<T>(ls > 0.0f ? o / ls : 0.0f);
+            if (d == 0 && a.lse) a.lse[row] = ls > 0.0f ? (M + log2f(ls)) * kLn2 : -INFINITY;
+        } else {
+            a.part[slot * G * D + e] = o;
+            if (d == 0) {
+                a.ml[(slot * G + hh) * 2 + 0] = M;
+                a.ml[(slot * G + hh) * 2 + 1] = ls;
+            }
         }
     }
+}
 
-    // completion counter: the last split of this (b, g) merges all splits
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&a.counters[bg], 1u) == (unsigned)(a.n_splits - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-
+// Merge of the split partials of one (batch, KV head) per workgroup:
+// M = max_s m_s, w_s = 2^(m_s - M), L = sum_s w_s l_s, O = sum_s w_s o_s / L.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const DecodeArgs a)
+{
+    __shared__ float s_w[256 * G];
+    __shared__ float4 s_red[kCombineThreads];
+    __shared__ float s_M[G], s_L[G];
+    const int bg = blockIdx.x;
+    const int b = bg / a.Hkv, g = bg - (bg / a.Hkv) * a.Hkv;
+    const int tid = threadIdx.x;
     const int ns = a.n_splits;
     const float* mlp = a.ml + (int64_t)bg * ns * G * 2;
     const float* pp = a.part + (int64_t)bg * ns * G * D;
-    for (int i = tid; i < ns * G; i += kThreads) s_w[i] = mlp[2 * i];
+
+    for (int i = tid; i < ns * G; i += kCombineThreads) s_w[i] = mlp[2 * i];
     __syncthreads();
     if (tid < G) {
         float M = -INFINITY;
@@ -332,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
         s_M[tid] = M;
     }
     __syncthreads();
-    for (int i = tid; i < ns * G; i += kThreads) s_w[i] = rel(s_w[i], s_M[i % G]);
+    for (int i = tid; i < ns * G; i += kCombineThreads) s_w[i] = rel(s_w[i], s_M[i % G]);
     __syncthreads();
     if (tid < G) {
         float L = 0.0f;
@@ -341,11 +353,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
     }
     __syncthreads();
 
-    // O = sum_s w_s * part_s / L over float4 columns; the splits are spread
-    // over NSUB threads per column so that many loads are in flight.
+    // float4 columns; the splits are spread over NSUB threads per column so
+    // that many loads are in flight
     constexpr int NE4 = G * D / 4;
-    constexpr int NSUB = kThreads / NE4;
-    static_assert(NE4 <= kThreads && NSUB >= 1, "merge layout");
+    constexpr int NSUB = kCombineThreads / NE4;
+    static_assert(NE4 <= kCombineThreads && NSUB >= 1, "merge layout");
     if (tid < NSUB * NE4) {
         const int sub = tid / NE4, e4 = tid - (tid / NE4) * NE4;
         const int hh = (e4 * 4) / D;
@@ -375,53 +387,62 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
         const int hh = (tid * 4) / D, d = tid * 4 - hh * D;
         const float L = s_L[hh];
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-        T* op = static_cast<T*>(a.out) + ((int64_t)b * a.Hq + (int64_t)g * G + hh) * D + d;
+        const int64_t row = (int64_t)b * a.Hq + (int64_t)g * G + hh;
+        T* op = static_cast<T*>(a.out) + row * D + d;
         op[0] = from_f32<T>(o.x * inv);
         op[1] = from_f32<T>(o.y * inv);
         op[2] = from_f32<T>(o.z * inv);
         op[3] = from_f32<T>(o.w * inv);
-        if (d == 0 && a.lse)
-            a.lse[(int64_t)b * a.Hq + (int64_t)g * G + hh] =
-                L > 0.0f ? (s_M[hh] + log2f(L)) * kLn2 : -INFINITY;
+        if (d == 0 && a.lse) a.lse[row] = L > 0.0f ? (s_M[hh] + log2f(L)) * kLn2 : -INFINITY;
     }
-    if (tid == 0) atomicExch(&a.counters[bg], 0u);
 }
 
-template <typename T, int D, bool FUSED>
-int launch_g(const DecodeArgs& a, hipStream_t st)
+template <typename T, int D, bool FUSED, int G>
+int launch_one(const DecodeArgs& a, int waves, hipStream_t st)
 {
+    constexpr int NW = decode_waves(sizeof(T) == 4, FUSED, G);
+    if (waves != NW) return (int)hipErrorInvalidValue;
     const dim3 grid(a.n_splits, a.B * a.Hkv);
-    switch (a.G) {
-    case 1: hipLaunchKernelGGL((decode_kernel<T, D, FUSED, 1>), grid, dim3(kThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<T, D, FUSED, 2>), grid, dim3(kThreads), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<T, D, FUSED, 4>), grid, dim3(kThreads), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<T, D, FUSED, 8>), grid, dim3(kThreads), 0, st, a); break;
-    default: return (int)hipErrorInvalidValue;
-    }
+    hipLaunchKernelGGL((decode_kernel<T, D, FUSED, G, NW>), grid, dim3(64 * NW), 0, st, a);
+    int rc = (int)hipGetLastError();
+    if (rc || a.n_splits == 1) return rc;
+    hipLaunchKernelGGL((combine_kernel<T, D, G>), dim3(a.B * a.Hkv), dim3(kCombineThreads), 0, st, a);
     return (int)hipGetLastError();
 }
 
+template <typename T, int D, bool FUSED>
+int launch_g(const DecodeArgs& a, int waves, hipStream_t st)
+{
+    switch (a.G) {
+    case 1: return launch_one<T, D, FUSED, 1>(a, waves, st);
+    case 2: return launch_one<T, D, FUSED, 2>(a, waves, st);
+    case 4: return launch_one<T, D, FUSED, 4>(a, waves, st);
+    case 8: return launch_one<T, D, FUSED, 8>(a, waves, st);
+    default: return (int)hipErrorInvalidValue;
+    }
+}
+
 template <typename T, bool FUSED>
-int launch_d(const DecodeArgs& a, hipStream_t st)
+int launch_d(const DecodeArgs& a, int waves, hipStream_t st)
 {
     switch (a.D) {
-    case 64: return launch_g<T, 64, FUSED>(a, st);
-    case 80: return launch_g<T, 80, FUSED>(a, st);
-    case 96: return launch_g<T, 96, FUSED>(a, st);
-    case 128: return launch_g<T, 128, FUSED>(a, st);
+    case 64: return launch_g<T, 64, FUSED>(a, waves, st);
+    case 80: return launch_g<T, 80, FUSED>(a, waves, st);
+    case 96: return launch_g<T, 96, FUSED>(a, waves, st);
+    case 128: return launch_g<T, 128, FUSED>(a, waves, st);
     default: return (int)hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-int launch_decode(const DecodeArgs& a, bool fused, int dtype, void* stream)
+int launch_decode(const DecodeArgs& a, bool fused, int dtype, int waves, void* stream)
 {
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (a.B == 0) return 0;
-    if (a.n_splits > 256 || (int64_t)a.B * a.Hkv > 65535) return (int)hipErrorInvalidValue;
-    if (dtype == 0) return fused ? launch_d<float, true>(a, st) : launch_d<float, false>(a, st);
-    return fused ? launch_d<uint16_t, true>(a, st) : launch_d<uint16_t, false>(a, st);
+    if (a.n_splits < 1 || a.n_splits > 256 || (int64_t)a.B * a.Hkv > 65535) return (int)hipErrorInvalidValue;
+    if (dtype == 0) return fused ? launch_d<float, true>(a, waves, st) : launch_d<float, false>(a, waves, st);
+    return fused ? launch_d<uint16_t, true>(a, waves, st) : launch_d<uint16_t, false>(a, waves, st);
 }
 
 }  // namespace fkv

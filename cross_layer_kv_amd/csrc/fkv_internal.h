@@ -14,9 +14,10 @@ struct View {
     int64_t sb, ss, sh;
 };
 
-// Decode (S_q = 1), split over the key axis.  One workgroup per
-// (batch, kv head, split); the last workgroup of each (batch, kv head) to
-// finish merges the splits (completion counter in the workspace).
+// Decode (S_q = 1).  One workgroup per (batch, kv head, split of the key
+// axis); the waves of a workgroup share its tokens and merge in LDS.  With one
+// split the workgroup writes O and LSE itself; with several it writes
+// partial (max, sum, unnormalised O) rows and a second kernel merges them.
 struct DecodeArgs {
     const void* q;          // [B, 1, Hq, D]
     View k1, kn, v1, vn;    // kn / vn unused for single-source calls
@@ -27,7 +28,6 @@ struct DecodeArgs {
     const int32_t* seqlens; // [B] or nullptr
     void* out;              // [B, 1, Hq, D]
     float* lse;             // [B, Hq] or nullptr
-    unsigned* counters;     // [B * Hkv], zero between calls
     float* ml;              // [B * Hkv, n_splits, G, 2]  (running max, sum)
     float* part;            // [B * Hkv, n_splits, G, D]  (unnormalised sums)
     int32_t B, Sk, Hq, Hkv, D, G;
@@ -36,9 +36,24 @@ struct DecodeArgs {
 };
 
 struct DecodePlan {
-    int32_t n_splits, chunk;
-    size_t counters_bytes, ml_bytes, part_bytes, total_bytes;
+    int32_t waves, n_splits, chunk;
+    size_t ml_bytes, part_bytes, total_bytes;
 };
+
+// Waves per decode workgroup.  Chosen so that one workgroup fills a compute
+// unit at the occupancy the kernel's register count allows (4 SIMDs x waves
+// per SIMD): e.g. the bf16 four-source kernel with G <= 2 uses ~155 VGPRs,
+// 3 waves per SIMD, 12 waves.  The kernels are compiled with the matching
+// launch bound, so the register budget is enforced.
+constexpr int decode_waves(int dtype_f32, bool fused, int G)
+{
+    if (!dtype_f32) {
+        if (fused) return G <= 2 ? 12 : (G == 4 ? 8 : 4);
+        return G <= 2 ? 16 : (G == 4 ? 12 : 8);
+    }
+    if (fused) return G <= 4 ? 8 : 4;
+    return G <= 2 ? 12 : (G == 4 ? 8 : 4);
+}
 
 // Prefill (S_q == S_k), bf16 only.
 struct PrefillArgs {
@@ -58,7 +73,7 @@ struct PrefillArgs {
 
 // Launchers (device code units).  They return 0 on success, else the HIP
 // error code of the failed launch.
-int launch_decode(const DecodeArgs& a, bool fused, int dtype, void* stream);
+int launch_decode(const DecodeArgs& a, bool fused, int dtype, int waves, void* stream);
 int launch_prefill(const PrefillArgs& a, bool fused, void* stream);
 // Query rows per prefill workgroup for a GQA ratio (0 when unsupported).
 int prefill_rows_per_tile(int G);

@@ -112,13 +112,12 @@ const char* fkv_status_string(fkv_status status);
 const char* fkv_last_error(void);
 
 /*
- * Bytes of device workspace fkv_decode / fkv_lite_decode need for `params`
- * (split-K partial results and per-(batch, KV head) completion counters);
- * the size covers both entry points.
- * Returns 0 when params is invalid.  The caller allocates it and fills it
- * with zeros ONCE; every call leaves the counters at zero again, so the same
- * workspace may be reused by later calls on the same stream.  Calls that run
- * concurrently need separate workspaces.
+ * Bytes of device workspace fkv_decode / fkv_lite_decode need for `params`:
+ * the split-K partial results when the key axis is split across workgroups
+ * (few batch rows x KV heads, long caches), otherwise 0.  The size covers
+ * both entry points.  Returns 0 also when params is invalid.  The workspace
+ * needs no initialisation; it only carries data between the two kernels of
+ * one call, so calls that may run concurrently need separate workspaces.
  */
 size_t fkv_decode_workspace_size(const fkv_params* params);
 
@@ -141,8 +140,8 @@ size_t fkv_decode_workspace_size(const fkv_params* params);
  *   seqlens_k  device int32 [B] or NULL
  *   out        device [B, 1, H_q, D], data dtype
  *   lse        device float32 [B, H_q] or NULL
- *   workspace  device, >= fkv_decode_workspace_size(params) bytes, 256-byte
- *              aligned, zero-filled before its first use
+ *   workspace  device, >= fkv_decode_workspace_size(params) bytes and
+ *              256-byte aligned; may be NULL when that size is 0
  */
 fkv_status fkv_decode(const fkv_params* params, const void* q,
                       fkv_cache k1, fkv_cache kn, fkv_cache v1, fkv_cache vn,

@@ -103,8 +103,9 @@ def test_decode_validation_codes(lib, B):
     assert _decode(lib, B, _params(B), caches=[B.fkv_cache(0, 0, 64, 0)] * 4) == INV
     # a NULL cache is accepted only when it holds no tokens (it is never read)
     assert _decode(lib, B, _params(B, batch=0, sk=0), caches=[B.fkv_cache(0, 0, 64, 0)] * 4) == B.FKV_SUCCESS
-    p = _params(B)
+    p = _params(B, sk=8192)   # 4 (batch, kv head) units: the key axis is split, a workspace is needed
     need = lib.fkv_decode_workspace_size(ctypes.byref(p))
+    assert need > 0
     assert _decode(lib, B, p, ws_bytes=need - 1) == WS
     assert _decode(lib, B, p, ws=0) == WS
     assert _decode(lib, B, p, ws=FAKE + 16) == WS                  # not 256-byte aligned
@@ -141,17 +142,18 @@ def test_workspace_size(lib, B):
     assert lib.fkv_decode_workspace_size(None) == 0
     p = _params(B, sq=2)
     assert lib.fkv_decode_workspace_size(ctypes.byref(p)) == 0
-    # 650M-shape decode: B=32, Hkv=8, S=8192, D=96, G=2
+    # 650M-shape decode: 32 x 8 = 256 (batch, kv head) units fill the chip with
+    # one workgroup each, so no split and no workspace
     p = _params(B, batch=32, sk=8192, hq=16, hkv=8, d=96)
-    n = lib.fkv_decode_workspace_size(ctypes.byref(p))
-    units, G, D = 32 * 8, 2, 96
-    # splits of the two-source plan: 1280 workgroups / 256 units -> 5 splits of 1664 tokens
-    ns = 5
-    expect = 1024 + math.ceil(units * ns * G * 2 * 4 / 256) * 256 + units * ns * G * D * 4
-    assert n == expect
-    # empty cache still gets room for one (empty) split per unit
+    assert lib.fkv_decode_workspace_size(ctypes.byref(p)) == 0
+    # long context, batch 1: 8 units x 32 splits of 4096 tokens, G = 2, D = 128
+    p = _params(B, batch=1, sk=131072, hq=16, hkv=8, d=128)
+    units, ns, G, D = 8, 32, 2, 128
+    expect = math.ceil(units * ns * G * 2 * 4 / 256) * 256 + units * ns * G * D * 4
+    assert lib.fkv_decode_workspace_size(ctypes.byref(p)) == expect
+    # an empty cache needs no workspace
     p = _params(B, sk=0)
-    assert lib.fkv_decode_workspace_size(ctypes.byref(p)) > 0
+    assert lib.fkv_decode_workspace_size(ctypes.byref(p)) == 0
 
 
 def test_check_tied(lib, B):

@@ -87,34 +87,40 @@ def test_forced_split_counts(splits, monkeypatch):
     check(L, fused=False)
 
 
-def test_selector_weights_equal_lite_bitwise(monkeypatch):
+def test_selector_weights_match_lite(monkeypatch):
     """(a, a', b, b') = (0, 1, 1, 0) makes the fused kernel read exactly K^n
-    and V^1; with the same split plan it must agree with the Lite kernel bit
-    for bit ([Deck] frame "Lite separates the key source from the value
-    source", Eq. (6))."""
+    and V^1 ([Deck] frame "Lite separates the key source from the value
+    source", Eq. (6)).  The two kernels split the tokens over different wave
+    counts, so they agree up to float32 summation order: O within one bf16
+    rounding, LSE within 1e-5; both also match the oracle."""
     monkeypatch.setenv("FKV_DECODE_SPLITS", "5")
     say("decode selector weights vs lite")
     L = inputs.make_layer(3, 1, 1000, 8, 4, 80, torch.bfloat16, 12, DEV)
     z = torch.zeros_like(L.weights[0])
     o = torch.ones_like(L.weights[0])
     L.weights = (z, o, o, z)
-    of, lf = run_decode(L, fused=True)
-    ol, ll = run_decode(L, fused=False, single=("kn", "v1"))
-    assert torch.equal(of, ol) and torch.equal(lf, ll)
+    of, lf = check(L, fused=True)
+    ol, ll = check(L, fused=False, single=("kn", "v1"))
+    B, _, Hq, D = L.q.shape
+    assert rel_err(gpu_rows(of, B, Hq, 1, D), gpu_rows(ol, B, Hq, 1, D)) <= 2 ** -8
+    assert lse_err(lf.cpu().numpy(), ll.cpu().numpy()) <= 1e-5
 
 
-def test_workspace_reuse_is_deterministic():
+def test_workspace_reuse_is_deterministic(monkeypatch):
+    """Repeated calls on one workspace (split path and direct path) give
+    identical results; the workspace needs no initialisation."""
     say("decode repeated calls on one workspace")
     L = inputs.make_layer(4, 1, 2000, 16, 8, 128, torch.bfloat16, 13, DEV)
-    ws = binding.decode_workspace(L.q, L.k1)
-    a = run_decode(L, ws=ws)
-    b = run_decode(L, ws=ws)
-    c = run_decode(L, fused=False, ws=ws)
-    d = run_decode(L, ws=ws)
-    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[0], d[0])
-    assert not torch.equal(a[0], c[0])
-    # counters are back at zero after every call
-    assert int(ws[:4 * 4 * 8].view(torch.int32).abs().sum()) == 0
+    for splits in ("5", "1"):
+        monkeypatch.setenv("FKV_DECODE_SPLITS", splits)
+        ws = torch.full((max(256, binding.fkv_decode_workspace_size(binding.make_params(L.q, L.k1))),),
+                        255, dtype=torch.uint8, device=DEV)   # garbage on purpose
+        a = run_decode(L, ws=ws)
+        b = run_decode(L, ws=ws)
+        c = run_decode(L, fused=False, ws=ws)
+        d = run_decode(L, ws=ws)
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[0], d[0])
+        assert not torch.equal(a[0], c[0])
 
 
 def test_vanilla_control_on_own_caches():
