@@ -18,6 +18,7 @@ Inputs are synthetic and seeded (see cross_layer_kv_amd/inputs.py) and
 resident in HBM before timing starts.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -34,6 +35,28 @@ DECODE = dict(name="650M-shape FusedKV decode, layers 9-16 fused from layers 1 a
               B=32, S=8192, Hq=16, Hkv=8, D=96, layers=8, seed=0xF0002)
 PREFILL = dict(name="1.5B-shape FusedKV causal prefill, layers 13-24 fused from layers 1 and 12",
                B=4, S=8192, Hq=16, Hkv=8, D=128, layers=12, seed=0xF0003)
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the four-source decode kernel, from the
+    committed counter summary (FETCH_SIZE and WRITE_SIZE runs scaled by a
+    copy kernel of known size); None when the kernel source has changed
+    since the counters were taken, or when there is no summary."""
+    path = os.path.join(ROOT, "profiles", "decode_650m_bf16_hbm_traffic.txt")
+    src = os.path.join(ROOT, "cross_layer_kv_amd", "csrc", "fkv_decode.hip")
+    try:
+        text = open(path, encoding="utf-8").read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    fields = {}
+    for ln in text.splitlines():
+        if ln and not ln.startswith("#") and ":" in ln:
+            k, v = ln.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("source_sha256_16") != sha or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def decode_bytes(B, S, Hq, Hkv, D, sources, elt=2):
@@ -160,6 +183,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--part", choices=["all", "decode", "prefill"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="also run a plain float32 copy kernel over BYTES bytes (reads BYTES, writes BYTES), "
+                         "used to scale the FETCH_SIZE / WRITE_SIZE counters of a profiler run")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run its own "
@@ -190,7 +216,7 @@ def main():
                             "achieved": round(f["bytes_per_layer"] / (f["ms_per_layer"] * 1e-3) / 1e9, 2),
                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(f["bytes_per_layer"] / (f["ms_per_layer"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                            "traffic": None,
+                            "traffic": recorded_traffic(),
                             "bytes_per_launch": f["bytes_per_layer"],
                             "avg_launch_us": round(f["ms_per_layer"] * 1e3, 2)}
         line["decode_variants"] = {k: {"GB/s": round(v["gbs"], 2), "us_per_layer": round(v["ms_per_layer"] * 1e3, 2),
@@ -216,6 +242,18 @@ def main():
             line.update(value=round(pre["fused"]["tflops"], 2), unit="TFLOP/s",
                         ms_per_step=round(pre["fused"]["ms_per_step"], 4),
                         config={"workload": PREFILL["name"]})
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = n * 4
+        del src, dst
+    props = torch.cuda.get_device_properties(0)
+    line["device"] = {"name": props.name, "compute_units": props.multi_processor_count,
+                      "arch": getattr(props, "gcnArchName", ""), "hip": torch.version.hip}
     print(json.dumps(line), flush=True)
 
 

@@ -1,0 +1,52 @@
+"""Why prefill rounds its matrix-core operands to binary16, not bfloat16.
+
+A CPU model of the prefill kernel's rounding points (fused K tile, softmax
+probabilities P, fused V tile, bf16 output), evaluated against the fp64
+oracle with the parity metric of the GPU tests, on the same kind of inputs.
+With bfloat16 operands the three roundings alone exceed the 1e-2 tolerance;
+with binary16 operands the error is dominated by the unavoidable bf16 output
+rounding and stays well inside it.  This is an analysis of rounding, not a
+second implementation the kernels are compared with.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from cross_layer_kv_amd import inputs
+from parity import rel_err
+
+
+def _round(x, dtype):
+    return torch.as_tensor(np.asarray(x, np.float32)).to(dtype).to(torch.float64).numpy()
+
+
+def _model(orc, seed, operand_dtype, S=200, Hq=4, Hkv=2, D=128):
+    L = inputs.make_layer(1, S, S, Hq, Hkv, D, torch.bfloat16, seed, "cpu", decode=False)
+    h = inputs.host_array
+    w = [x.numpy() for x in L.weights]
+    ro, _ = orc.attend(h(L.q), h(L.k1), h(L.v1), h(L.kn), h(L.vn), k_w1=w[0], k_wn=w[1], v_w1=w[2],
+                       v_wn=w[3], causal=True)
+    f = [t.to(torch.float64).numpy() for t in (L.q, L.k1, L.kn, L.v1, L.vn)]
+    q, k1, kn, v1, vn = f
+    w = [x.astype(np.float64) for x in w]
+    kf = _round(w[0] * k1 + w[1] * kn, operand_dtype)
+    vf = _round(w[2] * v1 + w[3] * vn, operand_dtype)
+    G = Hq // Hkv
+    out = np.zeros((Hq, S, D))
+    mask = np.tril(np.ones((S, S))) > 0
+    for hh in range(Hq):
+        s = np.where(mask, q[0, :, hh] @ kf[0, :, hh // G].T / math.sqrt(D), -np.inf)
+        p = np.exp(s - s.max(-1, keepdims=True))
+        o = (_round(p, operand_dtype) @ vf[0, :, hh // G]) / p.sum(-1, keepdims=True)
+        out[hh] = _round(o, torch.bfloat16)
+    return rel_err(out.reshape(-1, D), ro)
+
+
+@pytest.mark.parametrize("seed", [8, 9])
+def test_binary16_operands_fit_the_tolerance_bfloat16_do_not(orc, seed):
+    e_bf16 = _model(orc, seed, torch.bfloat16)
+    e_f16 = _model(orc, seed, torch.float16)
+    assert e_bf16 > 1e-2
+    assert e_f16 < 6e-3
