@@ -95,6 +95,26 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 int rows_per_tile(int G) { return (G == 1 || G == 2 || G == 4 || G == 8) ? 256 / G : 0; }
 
+// Buffer descriptor over one (batch, KV head) slab of a cache: base at token 0
+// of that head, size up to the end of row S-1.  A load at an offset past the
+// size returns zeros (hardware range check), which is how rows past the end
+// of the sequence read as 0 without per-load predicates.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t kOffNone = 0x80000000u;  // always past the descriptor's size
+
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint32_t ld4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
 template <int D, bool FUSED, int G>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
 {
@@ -102,6 +122,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
     constexpr int WPH = kWaves / G;      // waves per query head
     constexpr int DP = (D + 31) / 32 * 32;
     constexpr int KS = D / 16;           // k-steps of the score product
+    constexpr int NDB = DP / 32;         // 32-channel blocks of the output
     constexpr int KROW = D + 8;          // LDS row pitch of K~ (elements)
     constexpr int VROW = BN + 8;         // LDS row pitch of V~^T
     constexpr int CPR = D / 8;           // 16-byte chunks per key row
@@ -154,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
         }
     }
 
-    // ---- tile loaders ----
+    // ---- tile loaders: buffer descriptors over this (b, g) slab ----
     const int kc = tid % CPR, kr = tid / CPR;  // key chunk column / first row
     const bool k_active = kr < RPP;
     const int vj = tid % (D / 2), vo = tid / (D / 2);  // channel pair, key octet
@@ -174,41 +195,49 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
             wb2[c] = v_active ? a.vwn[g * D + 2 * vj + c] : 0.0f;
         }
     }
-    const uint16_t* k1p = static_cast<const uint16_t*>(a.k1.data) + (int64_t)b * a.k1.sb + (int64_t)g * a.k1.sh;
-    const uint16_t* v1p = static_cast<const uint16_t*>(a.v1.data) + (int64_t)b * a.v1.sb + (int64_t)g * a.v1.sh;
-    const uint16_t* knp = k1p;
-    const uint16_t* vnp = v1p;
+    auto rsrc_of = [&](const View& v) {
+        const uint16_t* base = static_cast<const uint16_t*>(v.data) + (int64_t)b * v.sb + (int64_t)g * v.sh;
+        return slab_rsrc(base, (uint32_t)(((int64_t)(S - 1) * v.ss + D) * 2));
+    };
+    const __amdgpu_buffer_rsrc_t rk1 = rsrc_of(a.k1), rv1 = rsrc_of(a.v1);
+    __amdgpu_buffer_rsrc_t rkn = rk1, rvn = rv1;
     if constexpr (FUSED) {
-        knp = static_cast<const uint16_t*>(a.kn.data) + (int64_t)b * a.kn.sb + (int64_t)g * a.kn.sh;
-        vnp = static_cast<const uint16_t*>(a.vn.data) + (int64_t)b * a.vn.sb + (int64_t)g * a.vn.sh;
+        rkn = rsrc_of(a.kn);
+        rvn = rsrc_of(a.vn);
     }
+    // byte offsets of this thread's rows inside a tile (kOffNone when idle);
+    // all caches of a call share the token stride only if their views do, so
+    // each source keeps its own
+    uint32_t koff1[KPASS], koffn[KPASS], voff1, voffn;
+#pragma unroll
+    for (int p = 0; p < KPASS; ++p) {
+        const int row = kr + p * RPP;
+        const bool ok = k_active && row < BN;
+        koff1[p] = ok ? (uint32_t)(row * a.k1.ss * 2 + kc * 16) : kOffNone;
+        koffn[p] = ok ? (uint32_t)(row * a.kn.ss * 2 + kc * 16) : kOffNone;
+    }
+    voff1 = v_active ? (uint32_t)(vkey0 * a.v1.ss * 2 + vj * 4) : kOffNone;
+    voffn = v_active ? (uint32_t)(vkey0 * a.vn.ss * 2 + vj * 4) : kOffNone;
+    const uint32_t kstep1 = (uint32_t)(BN * a.k1.ss * 2), kstepn = (uint32_t)(BN * a.kn.ss * 2);
+    const uint32_t vstep1 = (uint32_t)(BN * a.v1.ss * 2), vstepn = (uint32_t)(BN * a.vn.ss * 2);
+    const uint32_t vrow1 = (uint32_t)(a.v1.ss * 2), vrown = (uint32_t)(a.vn.ss * 2);
 
-    uint4 rk1[KPASS], rkn[KPASS];
-    uint32_t rv1[8], rvn[8];
+    uint4 xk1[KPASS], xkn[KPASS];
+    uint32_t xv1[8], xvn[8];
 
     auto issue_loads = [&](int j) {
+        const uint32_t jk1 = (uint32_t)j * kstep1, jkn = (uint32_t)j * kstepn;
+        const uint32_t jv1 = (uint32_t)j * vstep1, jvn = (uint32_t)j * vstepn;
 #pragma unroll
         for (int p = 0; p < KPASS; ++p) {
-            const int row = kr + p * RPP;
-            const int key = j * BN + row;
-            const bool ok = k_active && row < BN && key < S;
-            rk1[p] = make_uint4(0u, 0u, 0u, 0u);
-            rkn[p] = make_uint4(0u, 0u, 0u, 0u);
-            if (ok) {
-                rk1[p] = *reinterpret_cast<const uint4*>(k1p + (int64_t)key * a.k1.ss + kc * 8);
-                if constexpr (FUSED) rkn[p] = *reinterpret_cast<const uint4*>(knp + (int64_t)key * a.kn.ss + kc * 8);
-            }
+            xk1[p] = ld16(rk1, koff1[p] == kOffNone ? kOffNone : koff1[p] + jk1);
+            if constexpr (FUSED) xkn[p] = ld16(rkn, koffn[p] == kOffNone ? kOffNone : koffn[p] + jkn);
         }
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            const int key = j * BN + vkey0 + (s & 3) + (s >> 2) * 8;
-            const bool ok = v_active && key < S;
-            rv1[s] = 0u;
-            rvn[s] = 0u;
-            if (ok) {
-                rv1[s] = *reinterpret_cast<const uint32_t*>(v1p + (int64_t)key * a.v1.ss + 2 * vj);
-                if constexpr (FUSED) rvn[s] = *reinterpret_cast<const uint32_t*>(vnp + (int64_t)key * a.vn.ss + 2 * vj);
-            }
+            const uint32_t r = (uint32_t)((s & 3) + (s >> 2) * 8);
+            xv1[s] = ld4(rv1, voff1 == kOffNone ? kOffNone : voff1 + jv1 + r * vrow1);
+            if constexpr (FUSED) xvn[s] = ld4(rvn, voffn == kOffNone ? kOffNone : voffn + jvn + r * vrown);
         }
     };
 
@@ -220,8 +249,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
             if (k_active && row < BN) {
                 uint4 o;
                 if constexpr (FUSED) {
-                    const uint32_t x1[4] = {rk1[p].x, rk1[p].y, rk1[p].z, rk1[p].w};
-                    const uint32_t xn[4] = {rkn[p].x, rkn[p].y, rkn[p].z, rkn[p].w};
+                    const uint32_t x1[4] = {xk1[p].x, xk1[p].y, xk1[p].z, xk1[p].w};
+                    const uint32_t xn[4] = {xkn[p].x, xkn[p].y, xkn[p].z, xkn[p].w};
                     uint32_t r[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -231,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
                     }
                     o = make_uint4(r[0], r[1], r[2], r[3]);
                 } else {
-                    o = bf16x8_to_f16x8(rk1[p]);
+                    o = bf16x8_to_f16x8(xk1[p]);
                 }
                 *reinterpret_cast<uint4*>(&Kt[nb][row * KROW + kc * 8]) = o;
             }
@@ -241,15 +270,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if constexpr (FUSED) {
-                    const float a0 = wb[0] * bf16_lo(rv1[2 * i]) + wb2[0] * bf16_lo(rvn[2 * i]);
-                    const float a1 = wb[0] * bf16_lo(rv1[2 * i + 1]) + wb2[0] * bf16_lo(rvn[2 * i + 1]);
-                    const float c0 = wb[1] * bf16_hi(rv1[2 * i]) + wb2[1] * bf16_hi(rvn[2 * i]);
-                    const float c1 = wb[1] * bf16_hi(rv1[2 * i + 1]) + wb2[1] * bf16_hi(rvn[2 * i + 1]);
+                    const float a0 = wb[0] * bf16_lo(xv1[2 * i]) + wb2[0] * bf16_lo(xvn[2 * i]);
+                    const float a1 = wb[0] * bf16_lo(xv1[2 * i + 1]) + wb2[0] * bf16_lo(xvn[2 * i + 1]);
+                    const float c0 = wb[1] * bf16_hi(xv1[2 * i]) + wb2[1] * bf16_hi(xvn[2 * i]);
+                    const float c1 = wb[1] * bf16_hi(xv1[2 * i + 1]) + wb2[1] * bf16_hi(xvn[2 * i + 1]);
                     lo[i] = pack2(a0, a1);
                     hv[i] = pack2(c0, c1);
                 } else {
-                    lo[i] = pack2(bf16_lo(rv1[2 * i]), bf16_lo(rv1[2 * i + 1]));
-                    hv[i] = pack2(bf16_hi(rv1[2 * i]), bf16_hi(rv1[2 * i + 1]));
+                    lo[i] = pack2(bf16_lo(xv1[2 * i]), bf16_lo(xv1[2 * i + 1]));
+                    hv[i] = pack2(bf16_hi(xv1[2 * i]), bf16_hi(xv1[2 * i + 1]));
                 }
             }
             *reinterpret_cast<uint4*>(&Vt[nb][(2 * vj) * VROW + vo * 8]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
@@ -261,9 +290,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
     const int kend = a.causal ? min(S, q0 + BM) : S;
     const int nt = (kend + BN - 1) / BN;
 
-    f32x16 oacc[DP / 32];
+    f32x16 oacc[NDB];
 #pragma unroll
-    for (int i = 0; i < DP / 32; ++i) oacc[i] = f32x16{};
+    for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
     float m_run = -INFINITY, l_run = 0.0f;
     const int qrow = r0 + l32;
     const float sl2 = a.scale_log2;
@@ -279,17 +308,36 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
         const int kbase = j * BN;
         const bool wave_live = !a.causal || kbase <= r0 + 31;
         if (wave_live) {
-            // S^T = K~ Q^T : two 32-key blocks
+            // S^T = K~ Q^T over two 32-key blocks; LDS fragments are read two
+            // k-steps ahead of the matrix-core instructions that use them
             f32x16 sacc[2] = {f32x16{}, f32x16{}};
-            const uint16_t* kt = &Kt[buf][0];
+            const uint16_t* kt = &Kt[buf][0] + l32 * KROW + hi * 8;
+            uint4 kf[KS][2];
+#pragma unroll
+            for (int ks = 0; ks < KS && ks < 2; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    kf[ks][kb] = *reinterpret_cast<const uint4*>(kt + kb * 32 * KROW + ks * 16);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
+                if (ks + 2 < KS) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const uint4 av = *reinterpret_cast<const uint4*>(kt + (kb * 32 + l32) * KROW + ks * 16 + hi * 8);
-                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(av), qreg[ks], sacc[kb], 0, 0, 0);
+                    for (int kb = 0; kb < 2; ++kb)
+                        kf[ks + 2][kb] = *reinterpret_cast<const uint4*>(kt + kb * 32 * KROW + (ks + 2) * 16);
                 }
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(kf[ks][kb]), qreg[ks], sacc[kb], 0, 0, 0);
             }
+            // V~^T fragments for the first 32-key block, read while softmax runs
+            const uint16_t* vt = &Vt[buf][0] + l32 * VROW + hi * 8;
+            uint4 vf[4][NDB];
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int d = 0; d < NDB; ++d)
+                    vf[c][d] = *reinterpret_cast<const uint4*>(vt + d * 32 * VROW + c * 16);
+
             // mask: causal diagonal and keys past the end
             const bool need_mask = (a.causal && kbase + BN - 1 > r0) || kbase + BN > S;
             if (need_mask) {
@@ -314,16 +362,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
                 const float corr = m_run == -INFINITY ? 0.0f : exp2_fast(m_run - m_new);
                 l_run *= corr;
 #pragma unroll
-                for (int d = 0; d < DP / 32; ++d)
+                for (int d = 0; d < NDB; ++d)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) oacc[d][i] *= corr;
                 m_run = m_new;
             }
             const float msub = m_run == -INFINITY ? 0.0f : m_run;
-            // probabilities -> fp16 B operands of O^T += V~^T P^T
-            f16x8 pb[4];
+            // per 32-key block: probabilities -> fp16 B operands, then
+            // O^T += V~^T P^T; the second block's exponentials overlap the
+            // first block's matrix-core work
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
+                f16x8 pb[2];
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     uint32_t w[4];
@@ -334,17 +384,21 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
                         l_run += p0 + p1;
                         w[i] = pack2(p0, p1);
                     }
-                    pb[kb * 2 + half] = as_f16x8(make_uint4(w[0], w[1], w[2], w[3]));
+                    pb[half] = as_f16x8(make_uint4(w[0], w[1], w[2], w[3]));
                 }
-            }
-            const uint16_t* vt = &Vt[buf][0];
+                if (kb == 0) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
+                    for (int c = 2; c < 4; ++c)
 #pragma unroll
-                for (int d = 0; d < DP / 32; ++d) {
-                    const uint4 av = *reinterpret_cast<const uint4*>(vt + (d * 32 + l32) * VROW + c * 16 + hi * 8);
-                    oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(av), pb[c], oacc[d], 0, 0, 0);
+                        for (int d = 0; d < NDB; ++d)
+                            vf[c][d] = *reinterpret_cast<const uint4*>(vt + d * 32 * VROW + c * 16);
                 }
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int d = 0; d < NDB; ++d)
+                        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vf[kb * 2 + half][d]), pb[half],
+                                                                         oacc[d], 0, 0, 0);
             }
         }
         if (j + 1 < nt) store_tile(buf ^ 1);
@@ -357,7 +411,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
     if (qrow < S) {
         uint16_t* op = static_cast<uint16_t*>(a.out) + (((int64_t)b * S + qrow) * a.Hq + h) * D;
 #pragma unroll
-        for (int d = 0; d < DP / 32; ++d) {
+        for (int d = 0; d < NDB; ++d) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int ch = d * 32 + r * 8 + hi * 4;
