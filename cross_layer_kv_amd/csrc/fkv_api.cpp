@@ -225,6 +225,13 @@ fkv_status prefill_common(const fkv_params* p, const void* q, const fkv_cache* c
             !aligned16(fusion->v_wn))
             return fail(FKV_ERROR_INVALID_VALUE, "fusion weights are not 16-byte aligned");
     }
+    for (int i = 0; i < ncaches; ++i) {
+        // each (batch, KV head) slab is read through a 32-bit buffer range
+        const int64_t span = ((int64_t)(p->seqlen_k - 1) * caches[i].stride_s + p->head_dim) * 2;
+        if (span >= ((int64_t)1 << 31))
+            return fail(FKV_ERROR_UNSUPPORTED, "%s: one head's rows span %lld bytes (limit 2^31)", names[i],
+                        (long long)span);
+    }
     const int G = p->num_q_heads / p->num_kv_heads;
     const int bm = fkv::prefill_rows_per_tile(G);
     if (bm <= 0) return fail(FKV_ERROR_UNSUPPORTED, "GQA ratio %d not supported by prefill", G);

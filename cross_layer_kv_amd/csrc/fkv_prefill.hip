@@ -31,7 +31,9 @@
 //     flight while tile j is multiplied, and fused into the other buffer
 //     afterwards (one barrier per tile).
 //   * Softmax is in the log2 domain with scale * log2 e folded into one FMA;
-//     the accumulator is rescaled only when a running max rises.
+//     a row's reference max is raised only when a tile max exceeds it by more
+//     than 8, so the accumulator is rarely rescaled, and the row sums are
+//     packed fp16 dot products of the probabilities the products consume.
 //   * Matrix-core operands are IEEE binary16: bf16 inputs (Q, unfused K/V)
 //     convert to it exactly inside its range, and the float32 fused tiles and
 //     probabilities keep 11 significant bits instead of bf16's 8.  The
@@ -90,6 +92,8 @@ __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 u)
 }
 
 __device__ __forceinline__ f16x8 as_f16x8(uint4 u) { return __builtin_bit_cast(f16x8, u); }
+
+__device__ constexpr f16x2 kOnes2 = {(_Float16)1.0f, (_Float16)1.0f};
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -195,20 +199,25 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
             wb2[c] = v_active ? a.vwn[g * D + 2 * vj + c] : 0.0f;
         }
     }
-    auto rsrc_of = [&](const View& v) {
-        const uint16_t* base = static_cast<const uint16_t*>(v.data) + (int64_t)b * v.sb + (int64_t)g * v.sh;
-        return slab_rsrc(base, (uint32_t)(((int64_t)(S - 1) * v.ss + D) * 2));
-    };
-    const __amdgpu_buffer_rsrc_t rk1 = rsrc_of(a.k1), rv1 = rsrc_of(a.v1);
-    __amdgpu_buffer_rsrc_t rkn = rk1, rvn = rv1;
+    // Per-tile buffer descriptors: the base advances by one tile of rows per
+    // tile (scalar work) and the size shrinks with it, so the lanes keep
+    // fixed offsets and rows past S-1 read as zero.
+    const uint16_t* b_k1 = static_cast<const uint16_t*>(a.k1.data) + (int64_t)b * a.k1.sb + (int64_t)g * a.k1.sh;
+    const uint16_t* b_v1 = static_cast<const uint16_t*>(a.v1.data) + (int64_t)b * a.v1.sb + (int64_t)g * a.v1.sh;
+    const uint16_t* b_kn = b_k1;
+    const uint16_t* b_vn = b_v1;
     if constexpr (FUSED) {
-        rkn = rsrc_of(a.kn);
-        rvn = rsrc_of(a.vn);
+        b_kn = static_cast<const uint16_t*>(a.kn.data) + (int64_t)b * a.kn.sb + (int64_t)g * a.kn.sh;
+        b_vn = static_cast<const uint16_t*>(a.vn.data) + (int64_t)b * a.vn.sb + (int64_t)g * a.vn.sh;
     }
-    // byte offsets of this thread's rows inside a tile (kOffNone when idle);
-    // all caches of a call share the token stride only if their views do, so
-    // each source keeps its own
-    uint32_t koff1[KPASS], koffn[KPASS], voff1, voffn;
+    auto tile_rsrc = [&](const uint16_t* base, int64_t ss, int j) {
+        const int64_t total = ((int64_t)(S - 1) * ss + D) * 2;
+        const int64_t skip = (int64_t)j * BN * ss * 2;
+        const int64_t left = total - skip;
+        return slab_rsrc(base + (int64_t)j * BN * ss, (uint32_t)(left > 0 ? left : 0));
+    };
+    // byte offsets of this thread's rows inside a tile (kOffNone when idle)
+    uint32_t koff1[KPASS], koffn[KPASS], voff1[8], voffn[8];
 #pragma unroll
     for (int p = 0; p < KPASS; ++p) {
         const int row = kr + p * RPP;
@@ -216,28 +225,33 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
         koff1[p] = ok ? (uint32_t)(row * a.k1.ss * 2 + kc * 16) : kOffNone;
         koffn[p] = ok ? (uint32_t)(row * a.kn.ss * 2 + kc * 16) : kOffNone;
     }
-    voff1 = v_active ? (uint32_t)(vkey0 * a.v1.ss * 2 + vj * 4) : kOffNone;
-    voffn = v_active ? (uint32_t)(vkey0 * a.vn.ss * 2 + vj * 4) : kOffNone;
-    const uint32_t kstep1 = (uint32_t)(BN * a.k1.ss * 2), kstepn = (uint32_t)(BN * a.kn.ss * 2);
-    const uint32_t vstep1 = (uint32_t)(BN * a.v1.ss * 2), vstepn = (uint32_t)(BN * a.vn.ss * 2);
-    const uint32_t vrow1 = (uint32_t)(a.v1.ss * 2), vrown = (uint32_t)(a.vn.ss * 2);
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) {
+        const int row = vkey0 + (s8 & 3) + (s8 >> 2) * 8;
+        voff1[s8] = v_active ? (uint32_t)(row * a.v1.ss * 2 + vj * 4) : kOffNone;
+        voffn[s8] = v_active ? (uint32_t)(row * a.vn.ss * 2 + vj * 4) : kOffNone;
+    }
 
     uint4 xk1[KPASS], xkn[KPASS];
     uint32_t xv1[8], xvn[8];
 
     auto issue_loads = [&](int j) {
-        const uint32_t jk1 = (uint32_t)j * kstep1, jkn = (uint32_t)j * kstepn;
-        const uint32_t jv1 = (uint32_t)j * vstep1, jvn = (uint32_t)j * vstepn;
-#pragma unroll
-        for (int p = 0; p < KPASS; ++p) {
-            xk1[p] = ld16(rk1, koff1[p] == kOffNone ? kOffNone : koff1[p] + jk1);
-            if constexpr (FUSED) xkn[p] = ld16(rkn, koffn[p] == kOffNone ? kOffNone : koffn[p] + jkn);
+        const __amdgpu_buffer_rsrc_t rk1 = tile_rsrc(b_k1, a.k1.ss, j);
+        const __amdgpu_buffer_rsrc_t rv1 = tile_rsrc(b_v1, a.v1.ss, j);
+        __amdgpu_buffer_rsrc_t rkn = rk1, rvn = rv1;
+        if constexpr (FUSED) {
+            rkn = tile_rsrc(b_kn, a.kn.ss, j);
+            rvn = tile_rsrc(b_vn, a.vn.ss, j);
         }
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const uint32_t r = (uint32_t)((s & 3) + (s >> 2) * 8);
-            xv1[s] = ld4(rv1, voff1 == kOffNone ? kOffNone : voff1 + jv1 + r * vrow1);
-            if constexpr (FUSED) xvn[s] = ld4(rvn, voffn == kOffNone ? kOffNone : voffn + jvn + r * vrown);
+        for (int p = 0; p < KPASS; ++p) {
+            xk1[p] = ld16(rk1, koff1[p]);
+            if constexpr (FUSED) xkn[p] = ld16(rkn, koffn[p]);
+        }
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8) {
+            xv1[s8] = ld4(rv1, voff1[s8]);
+            if constexpr (FUSED) xvn[s8] = ld4(rvn, voffn[s8]);
         }
     };
 
@@ -357,8 +371,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx * sl2);
-            if (__any(m_new > m_run)) {
+            // The reference max is raised only when a tile max exceeds it by
+            // more than 8 (log2 units): the probabilities then stay <= 2^8,
+            // exact in fp16, and the accumulator is rescaled on few tiles.
+            const float m_tile = mx * sl2;
+            if (__any(m_tile > m_run + 8.0f)) {
+                const float m_new = fmaxf(m_run, m_tile);
                 const float corr = m_run == -INFINITY ? 0.0f : exp2_fast(m_run - m_new);
                 l_run *= corr;
 #pragma unroll
@@ -381,8 +399,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
                     for (int i = 0; i < 4; ++i) {
                         const float p0 = exp2_fast(sacc[kb][half * 8 + 2 * i] * sl2 - msub);
                         const float p1 = exp2_fast(sacc[kb][half * 8 + 2 * i + 1] * sl2 - msub);
-                        l_run += p0 + p1;
                         w[i] = pack2(p0, p1);
+                        // row sum of the rounded probabilities the products use
+                        l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[i]), kOnes2, l_run, false);
                     }
                     pb[half] = as_f16x8(make_uint4(w[0], w[1], w[2], w[3]));
                 }
