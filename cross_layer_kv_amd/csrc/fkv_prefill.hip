@@ -93,6 +93,22 @@ __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 u)
 
 __device__ __forceinline__ f16x8 as_f16x8(uint4 u) { return __builtin_bit_cast(f16x8, u); }
 
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
+
+// (source 1, source n) bf16 pairs of the low / high element of two packed
+// words: low half from u1, high half from un.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t u1, uint32_t un) { return __builtin_amdgcn_perm(un, u1, 0x05040100u); }
+__device__ __forceinline__ uint32_t pair_hi(uint32_t u1, uint32_t un) { return __builtin_amdgcn_perm(un, u1, 0x07060302u); }
+
+// w1 * x1 + wn * xn for a (x1, xn) bf16 pair and weights split as bf16
+// (hi, lo) pairs: two dot products with float32 accumulation.
+__device__ __forceinline__ float fuse_pair(uint32_t pair, uint32_t w_hi, uint32_t w_lo)
+{
+    const bf16x2v x = __builtin_bit_cast(bf16x2v, pair);
+    const float lo = __builtin_amdgcn_fdot2_f32_bf16(x, __builtin_bit_cast(bf16x2v, w_lo), 0.0f, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(x, __builtin_bit_cast(bf16x2v, w_hi), lo, false);
+}
+
 __device__ constexpr f16x2 kOnes2 = {(_Float16)1.0f, (_Float16)1.0f};
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -186,17 +202,24 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
     const bool v_active = tid < NVITEM;
     const int vkey0 = (vo >> 1) * 16 + (vo & 1) * 4;   // octet's first key
 
-    float wa[8], wa2[8], wb[2], wb2[2];
+    // Fusion weights as bf16 pairs (w1 in the low half, w2 in the high half)
+    // split into hi + lo parts: w = hi + lo to ~2^-16 relative, so a fused
+    // element is two bf16 dot products of its (source 1, source n) pair.
+    uint32_t wk_hi[8], wk_lo[8], wv_hi[2], wv_lo[2];
     if constexpr (FUSED) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            wa[c] = k_active ? a.kw1[g * D + kc * 8 + c] : 0.0f;
-            wa2[c] = k_active ? a.kwn[g * D + kc * 8 + c] : 0.0f;
+            const float x = k_active ? a.kw1[g * D + kc * 8 + c] : 0.0f;
+            const float y = k_active ? a.kwn[g * D + kc * 8 + c] : 0.0f;
+            wk_hi[c] = pack2_bf16(x, y);
+            wk_lo[c] = pack2_bf16(x - bf16_lo(wk_hi[c]), y - bf16_hi(wk_hi[c]));
         }
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            wb[c] = v_active ? a.vw1[g * D + 2 * vj + c] : 0.0f;
-            wb2[c] = v_active ? a.vwn[g * D + 2 * vj + c] : 0.0f;
+            const float x = v_active ? a.vw1[g * D + 2 * vj + c] : 0.0f;
+            const float y = v_active ? a.vwn[g * D + 2 * vj + c] : 0.0f;
+            wv_hi[c] = pack2_bf16(x, y);
+            wv_lo[c] = pack2_bf16(x - bf16_lo(wv_hi[c]), y - bf16_hi(wv_hi[c]));
         }
     }
     // Per-tile buffer descriptors: the base advances by one tile of rows per
@@ -267,11 +290,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
                     const uint32_t xn[4] = {xkn[p].x, xkn[p].y, xkn[p].z, xkn[p].w};
                     uint32_t r[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float lo = wa[2 * i] * bf16_lo(x1[i]) + wa2[2 * i] * bf16_lo(xn[i]);
-                        const float hi2 = wa[2 * i + 1] * bf16_hi(x1[i]) + wa2[2 * i + 1] * bf16_hi(xn[i]);
-                        r[i] = pack2(lo, hi2);
-                    }
+                    for (int i = 0; i < 4; ++i)
+                        r[i] = pack2(fuse_pair(pair_lo(x1[i], xn[i]), wk_hi[2 * i], wk_lo[2 * i]),
+                                     fuse_pair(pair_hi(x1[i], xn[i]), wk_hi[2 * i + 1], wk_lo[2 * i + 1]));
                     o = make_uint4(r[0], r[1], r[2], r[3]);
                 } else {
                     o = bf16x8_to_f16x8(xk1[p]);
@@ -284,12 +305,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if constexpr (FUSED) {
-                    const float a0 = wb[0] * bf16_lo(xv1[2 * i]) + wb2[0] * bf16_lo(xvn[2 * i]);
-                    const float a1 = wb[0] * bf16_lo(xv1[2 * i + 1]) + wb2[0] * bf16_lo(xvn[2 * i + 1]);
-                    const float c0 = wb[1] * bf16_hi(xv1[2 * i]) + wb2[1] * bf16_hi(xvn[2 * i]);
-                    const float c1 = wb[1] * bf16_hi(xv1[2 * i + 1]) + wb2[1] * bf16_hi(xvn[2 * i + 1]);
-                    lo[i] = pack2(a0, a1);
-                    hv[i] = pack2(c0, c1);
+                    lo[i] = pack2(fuse_pair(pair_lo(xv1[2 * i], xvn[2 * i]), wv_hi[0], wv_lo[0]),
+                                  fuse_pair(pair_lo(xv1[2 * i + 1], xvn[2 * i + 1]), wv_hi[0], wv_lo[0]));
+                    hv[i] = pack2(fuse_pair(pair_hi(xv1[2 * i], xvn[2 * i]), wv_hi[1], wv_lo[1]),
+                                  fuse_pair(pair_hi(xv1[2 * i + 1], xvn[2 * i + 1]), wv_hi[1], wv_lo[1]));
                 } else {
                     lo[i] = pack2(bf16_lo(xv1[2 * i]), bf16_lo(xv1[2 * i + 1]));
                     hv[i] = pack2(bf16_hi(xv1[2 * i]), bf16_hi(xv1[2 * i + 1]));
