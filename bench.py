@@ -16,6 +16,15 @@ Algorithmic work (what the method must move or compute, per layer call):
   prefill flops = 2*D*S*(S+1)*B*Hq (QK^T and PV over the causal triangle)
 Inputs are synthetic and seeded (see cross_layer_kv_amd/inputs.py) and
 resident in HBM before timing starts.
+
+`--workload NAME` measures one of the other configured workloads instead and
+prints one JSON line for it: tiny-decode (fp32, cache-resident correctness
+shape), 4b-decode, 4b-prefill, 1.5b-prefill, long-decode-b1 / long-decode-b8
+(131072 cached tokens; the whole 24-layer stack: 12 storage layers of plain
+attention plus 12 reconstruction layers, FusedKV vs Lite vs an all-vanilla
+model), and 1.5b-ttft (time to first token over the attention of all 24
+layers: the storage layers run causal prefill, the reconstruction layers only
+the final query row, a decode at S, against 24 layers of causal prefill).
 """
 import argparse
 import hashlib
@@ -35,6 +44,24 @@ DECODE = dict(name="650M-shape FusedKV decode, layers 9-16 fused from layers 1 a
               B=32, S=8192, Hq=16, Hkv=8, D=96, layers=8, seed=0xF0002)
 PREFILL = dict(name="1.5B-shape FusedKV causal prefill, layers 13-24 fused from layers 1 and 12",
                B=4, S=8192, Hq=16, Hkv=8, D=128, layers=12, seed=0xF0003)
+
+
+WORKLOADS = {
+    "tiny-decode": dict(kind="decode", name="tiny FusedKV decode (fp32, one layer, cache-resident)",
+                        B=1, S=1024, Hq=4, Hkv=2, D=64, layers=1, seed=0xF0001, dtype="f32"),
+    "650m-decode": dict(kind="decode", **DECODE),
+    "4b-decode": dict(kind="decode", name="4B-shape FusedKV decode, layers 19-36 fused from layers 1 and 18",
+                      B=16, S=32768, Hq=32, Hkv=16, D=80, layers=18, seed=0xF0004),
+    "1.5b-prefill": dict(kind="prefill", **PREFILL),
+    "4b-prefill": dict(kind="prefill", name="4B-shape FusedKV causal prefill, layers 19-36 fused from layers 1 and 18",
+                       B=1, S=16384, Hq=32, Hkv=16, D=80, layers=18, seed=0xF0004),
+    "long-decode-b1": dict(kind="stack", name="1.5B-shape long-context decode, whole 24-layer stack, batch 1",
+                           B=1, S=131072, Hq=16, Hkv=8, D=128, layers=12, seed=0xF0005),
+    "long-decode-b8": dict(kind="stack", name="1.5B-shape long-context decode, whole 24-layer stack, batch 8",
+                           B=8, S=131072, Hq=16, Hkv=8, D=128, layers=12, seed=0xF0005),
+    "1.5b-ttft": dict(kind="ttft", name="1.5B-shape attention time to first token, 24 layers, 8192-token prompt",
+                      B=1, S=8192, Hq=16, Hkv=8, D=128, layers=12, seed=0xF0003),
+}
 
 
 def recorded_traffic():
@@ -87,8 +114,9 @@ def run_decode(cfg, steps, warmup, stream):
     from cross_layer_kv_amd import binding, inputs
     dev = "cuda:0"
     B, S, Hq, Hkv, D, nl = cfg["B"], cfg["S"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["layers"]
-    base = inputs.make_layer(B, 1, S, Hq, Hkv, D, torch.bfloat16, cfg["seed"], dev)
-    qs = [inputs.make_queries(B, 1, Hq, D, torch.bfloat16, cfg["seed"] * 97 + i, dev,
+    dt = torch.float32 if cfg.get("dtype") == "f32" else torch.bfloat16
+    base = inputs.make_layer(B, 1, S, Hq, Hkv, D, dt, cfg["seed"], dev)
+    qs = [inputs.make_queries(B, 1, Hq, D, dt, cfg["seed"] * 97 + i, dev,
                               positions=torch.full((1,), S - 1)) for i in range(nl)]
     ws_list = [inputs.make_weights(Hkv, D, cfg["seed"] * 89 + i, device=dev) for i in range(nl)]
     outs = [torch.empty_like(q) for q in qs]
@@ -109,9 +137,10 @@ def run_decode(cfg, steps, warmup, stream):
             binding.fkv_lite_decode(qs[i], k, v, out=outs[i], workspace=ws, stream=stream)
 
     res = {}
+    elt = 4 if dt == torch.float32 else 2
     for name, fn, src in (("fused", fused_step, 4), ("lite", lite_step, 2), ("vanilla", vanilla_step, 2)):
         ms = _time_region(fn, steps, warmup, stream)
-        byts = decode_bytes(B, S, Hq, Hkv, D, src) * nl
+        byts = decode_bytes(B, S, Hq, Hkv, D, src, elt) * nl
         res[name] = dict(ms_per_step=ms, ms_per_layer=ms / nl, gbs=byts / (ms * 1e-3) / 1e9,
                          bytes_per_layer=byts // nl)
     return res, base
@@ -149,6 +178,94 @@ def run_prefill(cfg, steps, warmup, stream):
     return res
 
 
+def run_stack(cfg, steps, warmup, stream):
+    """One decode step through the whole 2n-layer stack: n storage layers of
+    plain attention over their own caches, then n reconstruction layers
+    (FusedKV or Lite), against an all-vanilla model of 2n plain layers.
+    Storage layers rotate over four distinct cache pairs (each far larger
+    than the 256 MB last-level cache), so every layer streams from HBM."""
+    import torch
+    from cross_layer_kv_amd import binding, inputs
+    dev = "cuda:0"
+    B, S, Hq, Hkv, D, nl = cfg["B"], cfg["S"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["layers"]
+    base = inputs.make_layer(B, 1, S, Hq, Hkv, D, torch.bfloat16, cfg["seed"], dev)
+    extra = [(inputs.make_cache(B, S, Hkv, D, torch.bfloat16, cfg["seed"] * 31 + 2 * i, dev),
+              inputs.make_cache(B, S, Hkv, D, torch.bfloat16, cfg["seed"] * 31 + 2 * i + 1, dev, rotate=False))
+             for i in range(2)]
+    pairs = [(base.k1, base.v1), (base.kn, base.vn)] + extra
+    qs = [inputs.make_queries(B, 1, Hq, D, torch.bfloat16, cfg["seed"] * 97 + i, dev,
+                              positions=torch.full((1,), S - 1)) for i in range(2 * nl)]
+    ws_list = [inputs.make_weights(Hkv, D, cfg["seed"] * 89 + i, device=dev) for i in range(nl)]
+    out = torch.empty_like(qs[0])
+    ws = binding.decode_workspace(qs[0], base.k1)
+
+    def storage(i):
+        k, v = pairs[i % 4]
+        binding.fkv_lite_decode(qs[i], k, v, out=out, workspace=ws, stream=stream)
+
+    def fused_model():
+        for i in range(nl):
+            storage(i)
+        for i in range(nl):
+            binding.fkv_decode(qs[nl + i], base.k1, base.kn, base.v1, base.vn, ws_list[i], out=out,
+                               workspace=ws, stream=stream)
+
+    def lite_model():
+        for i in range(nl):
+            storage(i)
+        for i in range(nl):
+            binding.fkv_lite_decode(qs[nl + i], base.kn, base.v1, out=out, workspace=ws, stream=stream)
+
+    def vanilla_model():
+        for i in range(2 * nl):
+            storage(i)
+
+    per_layer = decode_bytes(B, S, Hq, Hkv, D, 2)
+    res = {}
+    for name, fn, byts in (("fused", fused_model, nl * per_layer + nl * decode_bytes(B, S, Hq, Hkv, D, 4)),
+                           ("lite", lite_model, 2 * nl * per_layer),
+                           ("vanilla", vanilla_model, 2 * nl * per_layer)):
+        ms = _time_region(fn, steps, warmup, stream)
+        res[name] = dict(ms_per_step=ms, gbs=byts / (ms * 1e-3) / 1e9, bytes=byts)
+    return res
+
+
+def run_ttft(cfg, steps, warmup, stream):
+    """Attention time to first token of a 2n-layer model: storage layers run
+    causal prefill over the prompt; FusedKV reconstruction layers need only
+    the final prompt position, i.e. one decode at S per layer.  The plain
+    model runs causal prefill in all 2n layers."""
+    import torch
+    from cross_layer_kv_amd import binding, inputs
+    dev = "cuda:0"
+    B, S, Hq, Hkv, D, nl = cfg["B"], cfg["S"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["layers"]
+    base = inputs.make_layer(B, S, S, Hq, Hkv, D, torch.bfloat16, cfg["seed"], dev, decode=False)
+    qfull = base.q
+    qlast = qfull[:, S - 1:S].contiguous()
+    out_full = torch.empty_like(qfull)
+    out_last = torch.empty_like(qlast)
+    ws = binding.decode_workspace(qlast, base.k1)
+    pairs = [(base.k1, base.v1), (base.kn, base.vn)]
+
+    def vanilla_model():
+        for i in range(2 * nl):
+            k, v = pairs[i % 2]
+            binding.fkv_lite_prefill(qfull, k, v, out=out_full, causal=True, stream=stream)
+
+    def fused_model():
+        for i in range(nl):
+            k, v = pairs[i % 2]
+            binding.fkv_lite_prefill(qfull, k, v, out=out_full, causal=True, stream=stream)
+        for i in range(nl):
+            binding.fkv_decode(qlast, base.k1, base.kn, base.v1, base.vn, base.weights, out=out_last,
+                               workspace=ws, stream=stream)
+
+    res = {}
+    for name, fn in (("vanilla", vanilla_model), ("fused", fused_model)):
+        res[name] = dict(ms=_time_region(fn, max(1, steps // 2), max(1, warmup // 2), stream))
+    return res
+
+
 def cpu_baseline(cfg, base, budget_s=12.0):
     """The fp64 oracle (unchanged) on the host cores, on whole layers of the
     decode workload: one layer at a time until ~budget_s seconds have passed."""
@@ -182,6 +299,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--part", choices=["all", "decode", "prefill"], default="all")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default=None,
+                    help="measure one other configured workload instead of the default step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="also run a plain float32 copy kernel over BYTES bytes (reads BYTES, writes BYTES), "
@@ -202,6 +321,9 @@ def main():
             "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic (seeded N(0,1) post-RoPE caches, N(0.5,0.25) tied fusion weights)"}
+    if args.workload:
+        other_workload(args, line, stream)
+        return
     dec = None
     if args.part in ("all", "decode"):
         print("bench: decode %s" % DECODE["name"], file=sys.stderr, flush=True)
@@ -251,10 +373,70 @@ def main():
         torch.cuda.synchronize()
         line["copy_calibration_bytes"] = n * 4
         del src, dst
+    finish(line)
+
+
+def finish(line):
+    import torch
     props = torch.cuda.get_device_properties(0)
     line["device"] = {"name": props.name, "compute_units": props.multi_processor_count,
                       "arch": getattr(props, "gcnArchName", ""), "hip": torch.version.hip}
     print(json.dumps(line), flush=True)
+
+
+def other_workload(args, line, stream):
+    cfg = WORKLOADS[args.workload]
+    kind = cfg["kind"]
+    print("bench: %s" % cfg["name"], file=sys.stderr, flush=True)
+    shape = {"workload": cfg["name"], "batch": cfg["B"], "seq_len": cfg["S"], "q_heads": cfg["Hq"],
+             "kv_heads": cfg["Hkv"], "head_dim": cfg["D"]}
+    if kind == "decode":
+        res, _ = run_decode(cfg, args.steps, args.warmup, stream)
+        f = res["fused"]
+        line.update(value=round(f["gbs"], 2), ms_per_step=round(f["ms_per_step"], 4),
+                    dtype="f32" if cfg.get("dtype") == "f32" else "bf16",
+                    config=dict(shape, layers_per_step=cfg["layers"]))
+        line["roofline"] = {"bound": "hbm", "achieved": round(f["gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(f["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                            "bytes_per_launch": f["bytes_per_layer"], "avg_launch_us": round(f["ms_per_layer"] * 1e3, 2)}
+        line["decode_variants"] = {k: {"GB/s": round(v["gbs"], 2), "us_per_layer": round(v["ms_per_layer"] * 1e3, 2),
+                                       "frac": round(v["gbs"] / HBM_PEAK_GBS, 4)} for k, v in res.items()}
+        line["decode_variants"]["fused_over_vanilla_time"] = round(res["fused"]["ms_per_layer"] /
+                                                                   res["vanilla"]["ms_per_layer"], 3)
+    elif kind == "prefill":
+        res = run_prefill(cfg, args.steps, args.warmup, stream)
+        f = res["fused"]
+        line.update(value=round(f["tflops"], 2), unit="TFLOP/s", ms_per_step=round(f["ms_per_step"], 4),
+                    metric="fused-KV causal prefill TFLOP/s (% MFMA)",
+                    config=dict(shape, layers_per_step=cfg["layers"]))
+        line["roofline"] = {"bound": "mfma", "achieved": round(f["tflops"], 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(f["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                            "flops_per_launch": prefill_flops(cfg["B"], cfg["S"], cfg["Hq"], cfg["D"]),
+                            "avg_launch_us": round(f["ms_per_layer"] * 1e3, 2)}
+        line["prefill_variants"] = {k: {"TFLOP/s": round(v["tflops"], 2), "ms_per_layer": round(v["ms_per_layer"], 4),
+                                        "frac": round(v["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)} for k, v in res.items()}
+    elif kind == "stack":
+        res = run_stack(cfg, args.steps, args.warmup, stream)
+        f = res["fused"]
+        line.update(value=round(f["gbs"], 2), ms_per_step=round(f["ms_per_step"], 4),
+                    metric="whole-stack decode attention HBM GB/s (% peak)",
+                    config=dict(shape, layers=2 * cfg["layers"]))
+        line["roofline"] = {"bound": "hbm", "achieved": round(f["gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(f["gbs"] / HBM_PEAK_GBS, 4), "traffic": None}
+        line["stack"] = {k: {"ms": round(v["ms_per_step"], 4), "GB/s": round(v["gbs"], 2), "bytes": v["bytes"]}
+                         for k, v in res.items()}
+        line["stack"]["time_over_vanilla"] = {k: round(res[k]["ms_per_step"] / res["vanilla"]["ms_per_step"], 3)
+                                              for k in ("fused", "lite")}
+        line["stack"]["bytes_over_vanilla"] = {k: round(res[k]["bytes"] / res["vanilla"]["bytes"], 3)
+                                               for k in ("fused", "lite")}
+    else:  # ttft
+        res = run_ttft(cfg, args.steps, args.warmup, stream)
+        line.update(value=round(res["fused"]["ms"], 4), unit="ms", higher_is_better=False,
+                    metric="attention time to first token (ms), FusedKV schedule",
+                    ms_per_step=round(res["fused"]["ms"], 4), config=dict(shape, layers=2 * cfg["layers"]))
+        line["ttft"] = {"fused_ms": round(res["fused"]["ms"], 4), "vanilla_ms": round(res["vanilla"]["ms"], 4),
+                        "fused_over_vanilla": round(res["fused"]["ms"] / res["vanilla"]["ms"], 3)}
+    finish(line)
 
 
 if __name__ == "__main__":

@@ -129,3 +129,33 @@ def test_full_size_1p5b_prefill():
 def test_full_size_4b_prefill():
     """4B shape: B=1, S=16384, 32/16 heads, D=80."""
     _full_size(1, 16384, 32, 16, 80, 0xF0004)
+
+
+@pytest.mark.parametrize("S", [200, 4100])
+def test_first_token_row_equals_decode(S):
+    """Time to first token needs only the final prompt position of a
+    reconstruction layer.  Under the causal mask that row sees every cached
+    token, so a decode with the same query (position S-1) over the S-token
+    caches must reproduce the final prefill row and its LSE; both are checked
+    against the oracle's causal row S-1 and against each other."""
+    say("ttft: decode at S=%d vs causal prefill row S-1 (B=2 16/8 D=128)" % S)
+    B, Hq, Hkv, D = 2, 16, 8, 128
+    L = inputs.make_layer(B, S, S, Hq, Hkv, D, torch.bfloat16, 800 + S, DEV, decode=False)
+    out_p, lse_p = run_prefill(L, fused=True)
+    qlast = L.q[:, S - 1:S].contiguous()
+    out_d = torch.full_like(qlast, float("nan"))
+    lse_d = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=DEV)
+    binding.fkv_decode(qlast, L.k1, L.kn, L.v1, L.vn, L.weights, out=out_d, lse=lse_d,
+                       workspace=binding.decode_workspace(qlast, L.k1))
+    torch.cuda.synchronize()
+    rows = np.array([(b * Hq + h) * S + S - 1 for b in range(B) for h in range(Hq)], dtype=np.int64)
+    ro, rl = oracle_layer(L, fused=True, causal=True, rows=rows)
+    got_d = gpu_rows(out_d, B, Hq, 1, D)
+    got_p = gpu_rows(out_p[:, S - 1:S], B, Hq, 1, D)
+    e_d, e_p = rel_err(got_d, ro), rel_err(got_p, ro)
+    el_d = lse_err(lse_d.cpu().numpy().reshape(-1), rl)
+    el_p = lse_err(lse_p[:, :, S - 1].cpu().numpy().reshape(-1), rl)
+    e_pd = rel_err(got_p, got_d)
+    say("  decode err=%.3e lse=%.3e  prefill err=%.3e lse=%.3e  prefill-vs-decode %.3e"
+        % (e_d, el_d, e_p, el_p, e_pd))
+    assert e_d <= TOL and el_d <= TOL and e_p <= TOL and el_p <= TOL and e_pd <= TOL
