@@ -102,11 +102,14 @@ __device__ __forceinline__ uint32_t pair_hi(uint32_t u1, uint32_t un) { return _
 
 // w1 * x1 + wn * xn for a (x1, xn) bf16 pair and weights split as bf16
 // (hi, lo) pairs: two dot products with float32 accumulation.
+// The first product is the three-operand form with a zero addend (the
+// builtin is lowered to the accumulate-in-place form plus a register clear).
 __device__ __forceinline__ float fuse_pair(uint32_t pair, uint32_t w_hi, uint32_t w_lo)
 {
-    const bf16x2v x = __builtin_bit_cast(bf16x2v, pair);
-    const float lo = __builtin_amdgcn_fdot2_f32_bf16(x, __builtin_bit_cast(bf16x2v, w_lo), 0.0f, false);
-    return __builtin_amdgcn_fdot2_f32_bf16(x, __builtin_bit_cast(bf16x2v, w_hi), lo, false);
+    float lo;
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(lo) : "v"(pair), "v"(w_lo));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, pair), __builtin_bit_cast(bf16x2v, w_hi), lo,
+                                           false);
 }
 
 __device__ constexpr f16x2 kOnes2 = {(_Float16)1.0f, (_Float16)1.0f};
@@ -155,7 +158,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
     __shared__ __attribute__((aligned(16))) uint16_t Vt[2][DP * VROW];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    // the wave index is uniform: keep it (and all that derives from it) in
+    // scalar registers so that per-wave branches are real branches
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hi = lane >> 5;
 
     // ---- work item: XCD-aware, heaviest causal tile first ----
@@ -374,14 +380,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
             // mask: causal diagonal and keys past the end
             const bool need_mask = (a.causal && kbase + BN - 1 > r0) || kbase + BN > S;
             if (need_mask) {
+                // key kbase + off is visible iff off <= lim; a lane's keys sit
+                // at offsets kb*32 + (i/4)*8 + hi*4 + i%4
+                const int lim = (a.causal ? min(qrow, S - 1) : S - 1) - kbase - hi * 4;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = kbase + kb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
-                        const bool dead = key >= S || (a.causal && key > qrow);
-                        if (dead) sacc[kb][i] = -INFINITY;
-                    }
+                    for (int i = 0; i < 16; ++i)
+                        if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) sacc[kb][i] = -INFINITY;
             }
             // running max (log2 domain)
             float mx = -INFINITY;
