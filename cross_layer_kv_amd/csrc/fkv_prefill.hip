@@ -102,14 +102,28 @@ __device__ __forceinline__ uint32_t pair_hi(uint32_t u1, uint32_t un) { return _
 
 // w1 * x1 + wn * xn for a (x1, xn) bf16 pair and weights split as bf16
 // (hi, lo) pairs: two dot products with float32 accumulation.
-// The first product is the three-operand form with a zero addend (the
-// builtin is lowered to the accumulate-in-place form plus a register clear).
+// The compiler emits the accumulate-in-place form of the product plus a
+// register clear; that pair issues faster than the three-operand form with a
+// zero addend, which measured at well under half rate on gfx950.
 __device__ __forceinline__ float fuse_pair(uint32_t pair, uint32_t w_hi, uint32_t w_lo)
 {
-    float lo;
-    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(lo) : "v"(pair), "v"(w_lo));
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, pair), __builtin_bit_cast(bf16x2v, w_hi), lo,
-                                           false);
+    const bf16x2v x = __builtin_bit_cast(bf16x2v, pair);
+    const float lo = __builtin_amdgcn_fdot2_f32_bf16(x, __builtin_bit_cast(bf16x2v, w_lo), 0.0f, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(x, __builtin_bit_cast(bf16x2v, w_hi), lo, false);
+}
+
+// max / sum of a value and its copy in the lane 32 apart (v_permlane32_swap:
+// the upper half of the first operand trades places with the lower half of
+// the second), a VALU exchange instead of an LDS permute round trip
+__device__ __forceinline__ float halves_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ constexpr f16x2 kOnes2 = {(_Float16)1.0f, (_Float16)1.0f};
@@ -264,6 +278,33 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
     uint4 xk1[KPASS], xkn[KPASS];
     uint32_t xv1[8], xvn[8];
 
+    // The loads of the next tile, one at a time (index i < NKL: key loads).
+    // They are spread over the k-steps of the score product instead of being
+    // issued together at the start of a tile, where all waves of the
+    // workgroup would stall on the vector-memory queue at once.
+    constexpr int NSRCK = FUSED ? 2 : 1;
+    constexpr int NKL = KPASS * NSRCK, NL = NKL + 8 * NSRCK;
+    __amdgpu_buffer_rsrc_t nk1, nkn, nv1, nvn;
+    auto next_rsrc = [&](int j) {
+        nk1 = tile_rsrc(b_k1, a.k1.ss, j);
+        nv1 = tile_rsrc(b_v1, a.v1.ss, j);
+        nkn = nk1; nvn = nv1;
+        if constexpr (FUSED) {
+            nkn = tile_rsrc(b_kn, a.kn.ss, j);
+            nvn = tile_rsrc(b_vn, a.vn.ss, j);
+        }
+    };
+    auto load_one = [&](int i) {
+        if (i < NKL) {
+            const int p = i / NSRCK, s = i % NSRCK;
+            if (s == 0) xk1[p] = ld16(nk1, koff1[p]);
+            else xkn[p] = ld16(nkn, koffn[p]);
+        } else {
+            const int s8 = (i - NKL) / NSRCK, s = (i - NKL) % NSRCK;
+            if (s == 0) xv1[s8] = ld4(nv1, voff1[s8]);
+            else xvn[s8] = ld4(nvn, voffn[s8]);
+        }
+    };
     auto issue_loads = [&](int j) {
         const __amdgpu_buffer_rsrc_t rk1 = tile_rsrc(b_k1, a.k1.ss, j);
         const __amdgpu_buffer_rsrc_t rv1 = tile_rsrc(b_v1, a.v1.ss, j);
@@ -332,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
     f32x16 oacc[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f, l_run2 = 0.0f;  // two row-sum chains
     const int qrow = r0 + l32;
     const float sl2 = a.scale_log2;
 
@@ -342,10 +383,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
 
     for (int j = 0; j < nt; ++j) {
         const int buf = j & 1;
-        if (j + 1 < nt) issue_loads(j + 1);
+        const bool more = j + 1 < nt;
+        if (more) next_rsrc(j + 1);
 
         const int kbase = j * BN;
         const bool wave_live = !a.causal || kbase <= r0 + 31;
+        if (!wave_live && more) {
+#pragma unroll
+            for (int i = 0; i < NL; ++i) load_one(i);
+        }
         if (wave_live) {
             // S^T = K~ Q^T over two 32-key blocks; LDS fragments are read two
             // k-steps ahead of the matrix-core instructions that use them
@@ -359,6 +405,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
                     kf[ks][kb] = *reinterpret_cast<const uint4*>(kt + kb * 32 * KROW + ks * 16);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
+                if (more) {
+#pragma unroll
+                    for (int i = ks * NL / KS; i < (ks + 1) * NL / KS; ++i) load_one(i);
+                }
                 if (ks + 2 < KS) {
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
@@ -390,12 +440,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
                         if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) sacc[kb][i] = -INFINITY;
             }
             // running max (log2 domain)
-            float mx = -INFINITY;
+            float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            for (int i = 0; i < 16; ++i) {
+                mx0 = fmaxf(mx0, sacc[0][i]);
+                mx1 = fmaxf(mx1, sacc[1][i]);
+            }
+            const float mx = halves_max(fmaxf(mx0, mx1));
             // The reference max is raised only when a tile max exceeds it by
             // more than 8 (log2 units): the probabilities then stay <= 2^8,
             // exact in fp16, and the accumulator is rescaled on few tiles.
@@ -404,6 +455,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
                 const float m_new = fmaxf(m_run, m_tile);
                 const float corr = m_run == -INFINITY ? 0.0f : exp2_fast(m_run - m_new);
                 l_run *= corr;
+                l_run2 *= corr;
 #pragma unroll
                 for (int d = 0; d < NDB; ++d)
 #pragma unroll
@@ -426,7 +478,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
                         const float p1 = exp2_fast(sacc[kb][half * 8 + 2 * i + 1] * sl2 - msub);
                         w[i] = pack2(p0, p1);
                         // row sum of the rounded probabilities the products use
-                        l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[i]), kOnes2, l_run, false);
+                        if (i & 1)
+                            l_run2 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[i]), kOnes2, l_run2, false);
+                        else
+                            l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[i]), kOnes2, l_run, false);
                     }
                     pb[half] = as_f16x8(make_uint4(w[0], w[1], w[2], w[3]));
                 }
@@ -450,7 +505,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
     }
 
     // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l) ----
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = halves_sum(l_run + l_run2);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     if (qrow < S) {
         uint16_t* op = static_cast<uint16_t*>(a.out) + (((int64_t)b * S + qrow) * a.Hq + h) * D;
