@@ -19,7 +19,8 @@ resident in HBM before timing starts.
 
 `--workload NAME` measures one of the other configured workloads instead and
 prints one JSON line for it: tiny-decode (fp32, cache-resident correctness
-shape), 4b-decode, 4b-prefill, 1.5b-prefill, long-decode-b1 / long-decode-b8
+shape), 4b-decode, hgqa-decode (64 query heads per KV head, matrix-core
+kernel), 4b-prefill, 1.5b-prefill, long-decode-b1 / long-decode-b8
 (131072 cached tokens; the whole 24-layer stack: 12 storage layers of plain
 attention plus 12 reconstruction layers, FusedKV vs Lite vs an all-vanilla
 model), and 1.5b-ttft (time to first token over the attention of all 24
@@ -52,6 +53,8 @@ WORKLOADS = {
     "650m-decode": dict(kind="decode", **DECODE),
     "4b-decode": dict(kind="decode", name="4B-shape FusedKV decode, layers 19-36 fused from layers 1 and 18",
                       B=16, S=32768, Hq=32, Hkv=16, D=80, layers=18, seed=0xF0004),
+    "hgqa-decode": dict(kind="decode", name="high-GQA FusedKV decode (128 query heads over 2 KV heads, G=64), 8 layers",
+                        B=16, S=32768, Hq=128, Hkv=2, D=128, layers=8, seed=0xF0006),
     "1.5b-prefill": dict(kind="prefill", **PREFILL),
     "4b-prefill": dict(kind="prefill", name="4B-shape FusedKV causal prefill, layers 19-36 fused from layers 1 and 18",
                        B=1, S=16384, Hq=32, Hkv=16, D=80, layers=18, seed=0xF0004),

@@ -37,7 +37,9 @@ size_t elt_size(int32_t dtype) { return dtype == FKV_F32 ? 4 : 2; }
 
 bool supported_head_dim(int32_t d) { return d == 64 || d == 80 || d == 96 || d == 128; }
 
-bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+// GQA ratios: 1, 2, 4, 8 (all kernels) and 64 (decode on the matrix cores,
+// bfloat16 only; prefill rejects it).
+bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == fkv::kHighGqa; }
 
 // Shape checks common to decode and prefill.
 fkv_status check_shape(const fkv_params* p)
@@ -57,7 +59,7 @@ fkv_status check_shape(const fkv_params* p)
     if (!supported_head_dim(p->head_dim))
         return fail(FKV_ERROR_UNSUPPORTED, "head_dim %d not in {64, 80, 96, 128}", p->head_dim);
     if (!supported_group(p->num_q_heads / p->num_kv_heads))
-        return fail(FKV_ERROR_UNSUPPORTED, "GQA ratio %d not in {1, 2, 4, 8}",
+        return fail(FKV_ERROR_UNSUPPORTED, "GQA ratio %d not in {1, 2, 4, 8, 64}",
                     p->num_q_heads / p->num_kv_heads);
     return FKV_SUCCESS;
 }
@@ -106,9 +108,13 @@ fkv::DecodePlan plan_decode(const fkv_params* p, bool fused)
     pl.waves = fkv::decode_waves(p->dtype == FKV_F32, fused, (int)G);
     const int64_t units = (int64_t)p->batch * p->num_kv_heads;
     const int64_t S = p->seqlen_k;
-    const int64_t iter = (int64_t)pl.waves * 16;
+    // G = 64 runs the matrix-core kernel: 64-token tiles, and it aims at two
+    // workgroups per CU
+    const bool wide = G == fkv::kHighGqa;
+    const int64_t iter = wide ? 64 : (int64_t)pl.waves * 16;
+    const int64_t target = wide ? 512 : 256;
     const int64_t max_splits = S > 0 ? (S + iter - 1) / iter : 1;
-    int64_t ns = units > 0 ? (256 + units - 1) / units : 1;
+    int64_t ns = units > 0 ? (target + units - 1) / units : 1;
     if (const char* env = std::getenv("FKV_DECODE_SPLITS")) {
         const long v = std::strtol(env, nullptr, 10);
         if (v > 0) ns = v;
@@ -148,6 +154,9 @@ fkv_status decode_common(const fkv_params* p, const void* q, const fkv_cache* ca
     for (int i = 0; i < ncaches; ++i)
         if ((s = check_cache(p, caches[i], names[i]))) return s;
     const bool fused = ncaches == 4;
+    const bool wide = p->num_q_heads / p->num_kv_heads == fkv::kHighGqa;
+    if (wide && p->dtype != FKV_BF16)
+        return fail(FKV_ERROR_UNSUPPORTED, "GQA ratio %d decode runs on the matrix cores: bfloat16 only", fkv::kHighGqa);
     if (fused) {
         if (!fusion || !fusion->k_w1 || !fusion->k_wn || !fusion->v_w1 || !fusion->v_wn)
             return fail(FKV_ERROR_INVALID_VALUE, "fusion weights missing");
@@ -194,7 +203,8 @@ fkv_status decode_common(const fkv_params* p, const void* q, const fkv_cache* ca
     if (std::getenv("FKV_TRACE"))
         std::fprintf(stderr, "libfusedkv: decode %s B=%d Sk=%d Hq=%d Hkv=%d D=%d waves=%d splits=%d chunk=%d\n",
                      fused ? "fused" : "single", a.B, a.Sk, a.Hq, a.Hkv, a.D, pl.waves, a.n_splits, a.chunk);
-    const int rc = fkv::launch_decode(a, fused, p->dtype, pl.waves, stream);
+    const int rc = wide ? fkv::launch_decode_hgqa(a, fused, stream)
+                        : fkv::launch_decode(a, fused, p->dtype, pl.waves, stream);
     if (rc) return fail(FKV_ERROR_LAUNCH, "decode launch failed (HIP error %d)", rc);
     return ok();
 }
@@ -218,6 +228,9 @@ fkv_status prefill_common(const fkv_params* p, const void* q, const fkv_cache* c
     for (int i = 0; i < ncaches; ++i)
         if ((s = check_cache(p, caches[i], names[i]))) return s;
     const bool fused = ncaches == 4;
+    const bool wide = p->num_q_heads / p->num_kv_heads == fkv::kHighGqa;
+    if (wide && p->dtype != FKV_BF16)
+        return fail(FKV_ERROR_UNSUPPORTED, "GQA ratio %d decode runs on the matrix cores: bfloat16 only", fkv::kHighGqa);
     if (fused) {
         if (!fusion || !fusion->k_w1 || !fusion->k_wn || !fusion->v_w1 || !fusion->v_wn)
             return fail(FKV_ERROR_INVALID_VALUE, "fusion weights missing");

@@ -45,8 +45,12 @@ struct DecodePlan {
 // per SIMD): e.g. the bf16 four-source kernel with G <= 2 uses ~155 VGPRs,
 // 3 waves per SIMD, 12 waves.  The kernels are compiled with the matching
 // launch bound, so the register budget is enforced.
+// Query heads per KV head served by the matrix-core decode kernel.
+constexpr int kHighGqa = 64;
+
 constexpr int decode_waves(int dtype_f32, bool fused, int G)
 {
+    if (G == kHighGqa) return 4;  // 2 key halves x 2 blocks of 32 heads
     if (!dtype_f32) {
         if (fused) return G <= 2 ? 12 : (G == 4 ? 8 : 4);
         return G <= 2 ? 16 : (G == 4 ? 12 : 8);
@@ -74,6 +78,8 @@ struct PrefillArgs {
 // Launchers (device code units).  They return 0 on success, else the HIP
 // error code of the failed launch.
 int launch_decode(const DecodeArgs& a, bool fused, int dtype, int waves, void* stream);
+// Decode with G == kHighGqa query heads per KV head (bfloat16, matrix cores).
+int launch_decode_hgqa(const DecodeArgs& a, bool fused, void* stream);
 int launch_prefill(const PrefillArgs& a, bool fused, void* stream);
 // Query rows per prefill workgroup for a GQA ratio (0 when unsupported).
 int prefill_rows_per_tile(int G);

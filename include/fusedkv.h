@@ -85,7 +85,7 @@ typedef struct {
     int32_t batch;        /* B >= 0 */
     int32_t seqlen_q;     /* S_q: 1 for decode; S_k for prefill */
     int32_t seqlen_k;     /* S_k >= 0: cached tokens (the cache's token extent) */
-    int32_t num_q_heads;  /* H_q, a multiple of num_kv_heads */
+    int32_t num_q_heads;  /* H_q = G * H_kv, G in {1, 2, 4, 8}; decode also G = 64 */
     int32_t num_kv_heads; /* H_kv >= 1 */
     int32_t head_dim;     /* D in {64, 80, 96, 128} */
     int32_t dtype;        /* fkv_dtype */
@@ -132,6 +132,13 @@ size_t fkv_decode_workspace_size(const fkv_params* params);
  * upper layers run ([Notes] section 2.3).  Keys are a (.) K1 + a' (.) Kn and
  * values b (.) V1 + b' (.) Vn, formed in float32 in registers and never
  * stored.  An empty row yields O = 0 and LSE = -inf.
+ *
+ * With G = 64 query heads per KV head (bfloat16 only; float32 returns
+ * FKV_ERROR_UNSUPPORTED) the dot products run on the matrix cores: the
+ * many-heads decode regime of [Deck] frame "Decode cost depends on the
+ * inference regime" (Fig. 5, right).  Each token is fused once for all 64
+ * heads, and the fused tiles and probabilities are rounded to IEEE binary16
+ * for the products, as in fkv_prefill.
  *
  *   q          device [B, 1, H_q, D]
  *   k1, kn     caches of layers 1 and n (post-RoPE keys)

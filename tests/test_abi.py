@@ -112,6 +112,9 @@ def test_decode_validation_codes(lib, B):
     # an empty batch is a valid no-op: nothing is launched
     assert _decode(lib, B, _params(B, batch=0)) == B.FKV_SUCCESS
     assert lib.fkv_last_error() == b""
+    # G = 64 runs on the matrix cores: bfloat16 only; G = 32 is not served
+    assert _decode(lib, B, _params(B, hq=128, hkv=2, dtype=0)) == UNS
+    assert _decode(lib, B, _params(B, hq=64, hkv=2)) == UNS
 
 
 def test_lite_decode_validation_codes(lib, B):
@@ -133,6 +136,7 @@ def test_prefill_validation_codes(lib, B):
     assert _prefill(lib, B, _params(B, sq=64, sk=64), q=FAKE + 4) == INV
     assert _prefill(lib, B, _params(B, batch=0, sq=64, sk=64)) == B.FKV_SUCCESS
     assert _prefill(lib, B, _params(B, sq=0, sk=0)) == B.FKV_SUCCESS
+    assert _prefill(lib, B, _params(B, sq=64, sk=64, hq=128, hkv=2)) == UNS  # G = 64: decode only
     p = _params(B, sq=64, sk=64)
     c = _cache(B)
     assert lib.fkv_lite_prefill(ctypes.byref(p), FAKE, c, B.fkv_cache(0, 0, 64, 0), FAKE, None, None) == INV
@@ -149,6 +153,12 @@ def test_workspace_size(lib, B):
     # long context, batch 1: 8 units x 32 splits of 4096 tokens, G = 2, D = 128
     p = _params(B, batch=1, sk=131072, hq=16, hkv=8, d=128)
     units, ns, G, D = 8, 32, 2, 128
+    expect = math.ceil(units * ns * G * 2 * 4 / 256) * 256 + units * ns * G * D * 4
+    assert lib.fkv_decode_workspace_size(ctypes.byref(p)) == expect
+    # G = 64 (matrix-core decode) aims at 512 workgroups of 64-token tiles:
+    # 32 units x 16 splits of 2048 tokens, D = 128
+    p = _params(B, batch=16, sk=32768, hq=128, hkv=2, d=128)
+    units, ns, G, D = 32, 16, 64, 128
     expect = math.ceil(units * ns * G * 2 * 4 / 256) * 256 + units * ns * G * D * 4
     assert lib.fkv_decode_workspace_size(ctypes.byref(p)) == expect
     # an empty cache needs no workspace

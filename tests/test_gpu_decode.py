@@ -164,3 +164,47 @@ def test_full_size_4b_decode():
 def test_full_size_long_context_decode(B):
     """Long context: S=131072, 16/8 heads, D=128, batch 1 and 8."""
     _sampled(B, 131072, 16, 8, 128, 0xF0005, n_batches=2)
+
+
+# ---- high GQA ratio: 64 query heads per KV head (matrix-core kernel) ----
+
+@pytest.mark.parametrize("D", [64, 80, 96, 128])
+def test_high_gqa_head_dims(D):
+    """G = 64 ([Deck] frame "Decode cost depends on the inference regime",
+    Fig. 5 right): 128 query heads over 2 KV heads, ragged tile tail."""
+    say("decode high-GQA D=%d B=2 S=333 Hq=128 Hkv=2" % D)
+    L = inputs.make_layer(2, 1, 333, 128, 2, D, torch.bfloat16, 900 + D, DEV)
+    check(L, fused=True)
+    check(L, fused=False)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 17])
+def test_high_gqa_splits_and_ragged(splits, monkeypatch):
+    """Forced split counts (1: direct write, else partials + merge) with
+    ragged lengths, including an empty sequence and a single token."""
+    monkeypatch.setenv("FKV_DECODE_SPLITS", str(splits))
+    say("decode high-GQA splits=%d ragged seqlens" % splits)
+    L = inputs.make_layer(4, 1, 2100, 64, 1, 128, torch.bfloat16, 950 + splits, DEV,
+                          seqlens_k=[2100, 0, 1, 777])
+    out, lse = check(L, fused=True)
+    assert torch.all(out[1] == 0) and torch.all(torch.isneginf(lse[1]))
+    check(L, fused=False)
+
+
+def test_high_gqa_selector_weights_match_lite():
+    """(a, a', b, b') = (0, 1, 1, 0): the fused kernel reads exactly K^n and
+    V^1 and its fp16 tiles equal the Lite kernel's, bit for bit."""
+    say("decode high-GQA selector weights vs lite")
+    L = inputs.make_layer(2, 1, 1000, 128, 2, 80, torch.bfloat16, 960, DEV)
+    z = torch.zeros_like(L.weights[0])
+    o = torch.ones_like(L.weights[0])
+    L.weights = (z, o, o, z)
+    of, lf = run_decode(L, fused=True)
+    ol, ll = run_decode(L, fused=False)
+    assert torch.equal(of, ol) and torch.equal(lf, ll)
+
+
+def test_full_size_high_gqa_decode():
+    """High-GQA shape: B=16, S=32768, 128/2 heads, D=128 (the benchmarked
+    launch); oracle on every head of sampled batch rows."""
+    _sampled(16, 32768, 128, 2, 128, 0xF0006, n_batches=2)
