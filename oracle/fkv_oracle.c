@@ -60,16 +60,18 @@ typedef struct {
 
 typedef struct {
     int32_t batch, seqlen_q, seqlen_k, num_q_heads, num_kv_heads, head_dim;
-    int32_t dtype;  /* 0: values stored as float32, 1: stored as bfloat16 bits */
+    int32_t dtype;  /* 0: float32, 1: bfloat16 bits, 2: float64 (dequantised
+                       caches, which need more than float32 to hold exactly) */
     int32_t causal; /* 0: every cached token visible, 1: causal mask */
     double scale;   /* softmax scale applied to q.k */
 } orc_shape;
 
 /* Exact widening of one stored value to double.  A bfloat16 value is the
- * upper half of the float32 with the same bits. */
+ * upper half of the float32 with the same bits; float64 is read as is. */
 static double widen(const void* base, int32_t dtype, int64_t idx)
 {
     if (dtype == 0) return (double)((const float*)base)[idx];
+    if (dtype == 2) return ((const double*)base)[idx];
     uint32_t bits = ((uint32_t)((const uint16_t*)base)[idx]) << 16;
     float f;
     memcpy(&f, &bits, sizeof f);

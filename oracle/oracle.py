@@ -30,7 +30,7 @@ _SO_DEFAULT = os.path.join(_HERE, "liboracle.so")
 _SO = os.environ.get("FKV_ORACLE_SO", _SO_DEFAULT)
 _lib = None
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 
 
 def build(force: bool = True) -> str:
@@ -89,7 +89,9 @@ def _dtype_code(a: np.ndarray) -> int:
         return F32
     if a.dtype == np.uint16:
         return BF16
-    raise TypeError("oracle inputs are float32 or bfloat16 bit patterns (uint16), got %s" % a.dtype)
+    if a.dtype == np.float64:
+        return F64
+    raise TypeError("oracle inputs are float32, bfloat16 bit patterns (uint16) or float64, got %s" % a.dtype)
 
 
 def _view(a: np.ndarray | None, code: int) -> _View:
