@@ -62,6 +62,8 @@ WORKLOADS = {
                            B=1, S=131072, Hq=16, Hkv=8, D=128, layers=12, seed=0xF0005),
     "long-decode-b8": dict(kind="stack", name="1.5B-shape long-context decode, whole 24-layer stack, batch 8",
                            B=8, S=131072, Hq=16, Hkv=8, D=128, layers=12, seed=0xF0005),
+    "kivi-decode": dict(kind="kivi", name="650M-shape FusedKV decode over 4-bit (KIVI-style) source caches, 8 layers",
+                        B=32, S=8192, Hq=16, Hkv=8, D=96, layers=8, seed=0xF0007),
     "1.5b-ttft": dict(kind="ttft", name="1.5B-shape attention time to first token, 24 layers, 8192-token prompt",
                       B=1, S=8192, Hq=16, Hkv=8, D=128, layers=12, seed=0xF0003),
 }
@@ -91,6 +93,18 @@ def recorded_traffic():
 
 def decode_bytes(B, S, Hq, Hkv, D, sources, elt=2):
     return sources * B * S * Hkv * D * elt + 2 * B * Hq * D * elt + (16 * Hkv * D if sources == 4 else 0)
+
+
+def kivi_decode_bytes(B, S, Hq, Hkv, D, sources):
+    """Algorithmic bytes of one 4-bit decode launch: per source the codes
+    (D/2 bytes a token) and fp16 scale + minimum (keys per 32-token group
+    and channel, values per token and 32-channel group), plus Q and O
+    (bf16) and, fused, the four float32 weight vectors."""
+    codes = B * Hkv * S * D // 2
+    kmeta = B * Hkv * ((S + 31) // 32) * D * 4
+    vmeta = B * Hkv * S * ((D + 31) // 32) * 4
+    per_pair = 2 * codes + kmeta + vmeta
+    return per_pair * (sources // 2) + 2 * B * Hq * D * 2 + (16 * Hkv * D if sources == 4 else 0)
 
 
 def prefill_flops(B, S, Hq, D):
@@ -147,6 +161,54 @@ def run_decode(cfg, steps, warmup, stream):
         res[name] = dict(ms_per_step=ms, ms_per_layer=ms / nl, gbs=byts / (ms * 1e-3) / 1e9,
                          bytes_per_layer=byts // nl)
     return res, base
+
+
+def run_kivi(cfg, steps, warmup, stream):
+    """4-bit decode: the caches are quantised once (outside the timed
+    region, as a prefill would write them); one step is `layers` fused
+    decode launches.  The bf16 fused decode on the same sources is timed
+    beside it."""
+    import torch
+    from cross_layer_kv_amd import binding, inputs
+    dev = "cuda:0"
+    B, S, Hq, Hkv, D, nl = cfg["B"], cfg["S"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["layers"]
+    base = inputs.make_layer(B, 1, S, Hq, Hkv, D, torch.bfloat16, cfg["seed"], dev)
+    names = ("k1", "kn", "v1", "vn")
+    q4 = {n: binding.fkv_kivi_quantize(getattr(base, n), n in ("v1", "vn")) for n in names}
+    qs = [inputs.make_queries(B, 1, Hq, D, torch.bfloat16, cfg["seed"] * 97 + i, dev,
+                              positions=torch.full((1,), S - 1)) for i in range(nl)]
+    ws_list = [inputs.make_weights(Hkv, D, cfg["seed"] * 89 + i, device=dev) for i in range(nl)]
+    outs = [torch.empty_like(q) for q in qs]
+    ws = binding.decode_workspace(qs[0], base.k1)
+
+    def quantise_step():
+        for n in names:
+            binding.fkv_kivi_quantize(getattr(base, n), n in ("v1", "vn"), dst=q4[n], stream=stream)
+
+    def fused_step():
+        for i in range(nl):
+            binding.fkv_kivi_decode(qs[i], q4["k1"], q4["kn"], q4["v1"], q4["vn"], ws_list[i], out=outs[i],
+                                    workspace=ws, stream=stream)
+
+    def lite_step():
+        for i in range(nl):
+            binding.fkv_kivi_lite_decode(qs[i], q4["kn"], q4["v1"], out=outs[i], workspace=ws, stream=stream)
+
+    def bf16_step():
+        for i in range(nl):
+            binding.fkv_decode(qs[i], base.k1, base.kn, base.v1, base.vn, ws_list[i], out=outs[i],
+                               workspace=ws, stream=stream)
+
+    res = {}
+    for name, fn, byts in (("fused", fused_step, kivi_decode_bytes(B, S, Hq, Hkv, D, 4) * nl),
+                           ("lite", lite_step, kivi_decode_bytes(B, S, Hq, Hkv, D, 2) * nl),
+                           ("bf16_fused", bf16_step, decode_bytes(B, S, Hq, Hkv, D, 4) * nl)):
+        ms = _time_region(fn, steps, warmup, stream)
+        res[name] = dict(ms_per_step=ms, ms_per_layer=ms / nl, gbs=byts / (ms * 1e-3) / 1e9,
+                         bytes_per_layer=byts // nl)
+    ms = _time_region(quantise_step, 2, 1, stream)
+    res["quantise"] = dict(ms_per_source=ms / 4, gbs=B * S * Hkv * D * 2 / (ms / 4 * 1e-3) / 1e9)
+    return res
 
 
 def run_prefill(cfg, steps, warmup, stream):
@@ -432,6 +494,19 @@ def other_workload(args, line, stream):
                                               for k in ("fused", "lite")}
         line["stack"]["bytes_over_vanilla"] = {k: round(res[k]["bytes"] / res["vanilla"]["bytes"], 3)
                                                for k in ("fused", "lite")}
+    elif kind == "kivi":
+        res = run_kivi(cfg, args.steps, args.warmup, stream)
+        f = res["fused"]
+        line.update(value=round(f["gbs"], 2), ms_per_step=round(f["ms_per_step"], 4),
+                    metric="4-bit fused-KV decode HBM GB/s (% peak)", config=dict(shape, layers_per_step=cfg["layers"]))
+        line["roofline"] = {"bound": "hbm", "achieved": round(f["gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(f["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                            "bytes_per_launch": f["bytes_per_layer"], "avg_launch_us": round(f["ms_per_layer"] * 1e3, 2)}
+        line["kivi"] = {k: {"GB/s": round(v["gbs"], 2), "us_per_layer": round(v["ms_per_layer"] * 1e3, 2),
+                            "frac": round(v["gbs"] / HBM_PEAK_GBS, 4)} for k, v in res.items() if k != "quantise"}
+        line["kivi"]["bf16_over_4bit_time"] = round(res["bf16_fused"]["ms_per_layer"] / f["ms_per_layer"], 3)
+        line["kivi"]["quantise"] = {"us_per_source": round(res["quantise"]["ms_per_source"] * 1e3, 2),
+                                    "bf16_read_GB/s": round(res["quantise"]["gbs"], 2)}
     else:  # ttft
         res = run_ttft(cfg, args.steps, args.warmup, stream)
         line.update(value=round(res["fused"]["ms"], 4), unit="ms", higher_is_better=False,

@@ -40,13 +40,19 @@ class fkv_params(ctypes.Structure):
                 ("causal", ctypes.c_int32)]
 
 
+class fkv_q4_cache(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("minv", ctypes.c_void_p)]
+
+
 class fkv_fusion(ctypes.Structure):
     _fields_ = [("k_w1", ctypes.c_void_p), ("k_wn", ctypes.c_void_p),
                 ("v_w1", ctypes.c_void_p), ("v_wn", ctypes.c_void_p)]
 
 
 EXPORTS = ["fkv_abi_version", "fkv_status_string", "fkv_last_error", "fkv_decode_workspace_size",
-           "fkv_decode", "fkv_lite_decode", "fkv_prefill", "fkv_lite_prefill", "fkv_check_tied"]
+           "fkv_decode", "fkv_lite_decode", "fkv_prefill", "fkv_lite_prefill", "fkv_check_tied",
+           "fkv_kivi_codes_bytes", "fkv_kivi_meta_bytes", "fkv_kivi_quantize", "fkv_kivi_decode",
+           "fkv_kivi_lite_decode"]
 
 _lib = None
 
@@ -82,7 +88,19 @@ def load_library(path: str = LIB_PATH):
     lib.fkv_lite_prefill.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, vp, vp, vp]
     lib.fkv_check_tied.restype = ctypes.c_int
     lib.fkv_check_tied.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float]
-    if lib.fkv_abi_version() != 1:
+    lib.fkv_kivi_codes_bytes.restype = ctypes.c_size_t
+    lib.fkv_kivi_codes_bytes.argtypes = [P(fkv_params)]
+    lib.fkv_kivi_meta_bytes.restype = ctypes.c_size_t
+    lib.fkv_kivi_meta_bytes.argtypes = [P(fkv_params), ctypes.c_int32]
+    lib.fkv_kivi_quantize.restype = ctypes.c_int
+    lib.fkv_kivi_quantize.argtypes = [P(fkv_params), fkv_cache, ctypes.c_int32, fkv_q4_cache, vp]
+    lib.fkv_kivi_decode.restype = ctypes.c_int
+    lib.fkv_kivi_decode.argtypes = [P(fkv_params), vp, fkv_q4_cache, fkv_q4_cache, fkv_q4_cache, fkv_q4_cache,
+                                    P(fkv_fusion), vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fkv_kivi_lite_decode.restype = ctypes.c_int
+    lib.fkv_kivi_lite_decode.argtypes = [P(fkv_params), vp, fkv_q4_cache, fkv_q4_cache, vp, vp, vp, vp,
+                                         ctypes.c_size_t, vp]
+    if lib.fkv_abi_version() != 2:
         raise RuntimeError("libfusedkv ABI version mismatch")
     _lib = lib
     return lib
@@ -205,3 +223,68 @@ def fkv_check_tied(k_w: torch.Tensor, pairing: str = "interleaved", tol: float =
         return False
     _check(st)
     return False
+
+
+# ---- KIVI-style 4-bit source caches ----
+
+class Q4Cache:
+    """Device arrays of one 4-bit source (layout in include/fusedkv.h):
+    codes uint8 [B, Hkv, S, D/2], scale and minv float16 (keys
+    [B, Hkv, ceil(S/32), D], values [B, Hkv, S, ceil(D/32)])."""
+
+    def __init__(self, codes, scale, minv, is_value):
+        self.codes, self.scale, self.minv, self.is_value = codes, scale, minv, bool(is_value)
+
+    def view(self) -> fkv_q4_cache:
+        return fkv_q4_cache(_dev(self.codes, "codes"), _dev(self.scale, "scale"), _dev(self.minv, "minv"))
+
+    @property
+    def seqlen(self):
+        return self.codes.shape[2]
+
+
+def kivi_empty(B, S, Hkv, D, is_value, device="cuda"):
+    """Uninitialised 4-bit cache arrays of the library's layout."""
+    ng = (D + 31) // 32 if is_value else (S + 31) // 32
+    meta = (B, Hkv, S, ng) if is_value else (B, Hkv, ng, D)
+    return Q4Cache(torch.empty((B, Hkv, S, D // 2), dtype=torch.uint8, device=device),
+                   torch.empty(meta, dtype=torch.float16, device=device),
+                   torch.empty(meta, dtype=torch.float16, device=device), is_value)
+
+
+def fkv_kivi_quantize(src: torch.Tensor, is_value: bool, *, dst: Q4Cache | None = None, num_q_heads=None,
+                      stream=None) -> Q4Cache:
+    """4-bit cache of a bf16 source [B, S, Hkv, D] (keys: is_value False)."""
+    lib = load_library()
+    B, S, Hkv, D = src.shape
+    if dst is None:
+        dst = kivi_empty(B, S, Hkv, D, is_value, src.device)
+    p = fkv_params(B, 1, S, num_q_heads or Hkv, Hkv, D, _dtype(src), 0.0, 0)
+    _check(lib.fkv_kivi_quantize(ctypes.byref(p), cache_view(src), 1 if is_value else 0, dst.view(), _stream(stream)))
+    return dst
+
+
+def _kivi_params(q, c: Q4Cache, softmax_scale):
+    B, Sq, Hq, D = q.shape
+    return fkv_params(B, Sq, c.seqlen, Hq, c.codes.shape[1], D, _dtype(q), float(softmax_scale), 0)
+
+
+def fkv_kivi_decode(q, k1: Q4Cache, kn: Q4Cache, v1: Q4Cache, vn: Q4Cache, weights, *, out, workspace, lse=None,
+                    seqlens_k=None, softmax_scale=0.0, stream=None):
+    """FusedKV decode over 4-bit sources (fkv_kivi_decode in fusedkv.h)."""
+    lib = load_library()
+    p = _kivi_params(q, k1, softmax_scale)
+    f = _fusion(weights)
+    _check(lib.fkv_kivi_decode(ctypes.byref(p), _dev(q, "q"), k1.view(), kn.view(), v1.view(), vn.view(),
+                               ctypes.byref(f), _dev(seqlens_k, "seqlens_k"), _dev(out, "out"), _dev(lse, "lse"),
+                               _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
+
+
+def fkv_kivi_lite_decode(q, k_src: Q4Cache, v_src: Q4Cache, *, out, workspace, lse=None, seqlens_k=None,
+                         softmax_scale=0.0, stream=None):
+    """Single-source decode over 4-bit sources (FusedKV-Lite: K^n, V^1)."""
+    lib = load_library()
+    p = _kivi_params(q, k_src, softmax_scale)
+    _check(lib.fkv_kivi_lite_decode(ctypes.byref(p), _dev(q, "q"), k_src.view(), v_src.view(),
+                                    _dev(seqlens_k, "seqlens_k"), _dev(out, "out"), _dev(lse, "lse"),
+                                    _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))

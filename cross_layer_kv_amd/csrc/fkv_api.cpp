@@ -101,11 +101,11 @@ float scale_log2_of(const fkv_params* p)
 // multiples of 64 tokens and at most 256.  The plan depends on the
 // parameters only (no device query), so the workspace size is a pure function
 // of them.  FKV_DECODE_SPLITS overrides the split count (tuning and tests).
-fkv::DecodePlan plan_decode(const fkv_params* p, bool fused)
+fkv::DecodePlan plan_decode(const fkv_params* p, bool fused, bool kivi = false)
 {
     fkv::DecodePlan pl{};
     const int64_t G = p->num_q_heads / p->num_kv_heads;
-    pl.waves = fkv::decode_waves(p->dtype == FKV_F32, fused, (int)G);
+    pl.waves = kivi ? fkv::kivi_waves(fused, (int)G) : fkv::decode_waves(p->dtype == FKV_F32, fused, (int)G);
     const int64_t units = (int64_t)p->batch * p->num_kv_heads;
     const int64_t S = p->seqlen_k;
     // G = 64 runs the matrix-core kernel: 64-token tiles, and it aims at two
@@ -280,6 +280,93 @@ fkv_status prefill_common(const fkv_params* p, const void* q, const fkv_cache* c
     return ok();
 }
 
+// ---- KIVI-style 4-bit caches ----
+
+int64_t kivi_key_groups(int64_t S) { return (S + 31) / 32; }
+int64_t kivi_value_groups(int64_t D) { return (D + 31) / 32; }
+
+fkv_status check_q4(const fkv_params* p, const fkv_q4_cache& c, const char* name)
+{
+    if (p->seqlen_k == 0) return FKV_SUCCESS;  // an empty cache is never read
+    if (!c.codes || !c.scale || !c.minv) return fail(FKV_ERROR_INVALID_VALUE, "%s has a NULL array", name);
+    if (!aligned16(c.codes) || !aligned16(c.scale) || !aligned16(c.minv))
+        return fail(FKV_ERROR_INVALID_VALUE, "%s arrays are not 16-byte aligned", name);
+    return FKV_SUCCESS;
+}
+
+fkv::Q4View q4_of(const fkv_q4_cache& c) { return fkv::Q4View{c.codes, c.scale, c.minv}; }
+
+fkv_status kivi_decode_common(const fkv_params* p, const void* q, const fkv_q4_cache* caches,
+                              const char* const* names, int ncaches, const fkv_fusion* fusion,
+                              const int32_t* seqlens_k, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream)
+{
+    fkv_status s = check_shape(p);
+    if (s) return s;
+    if (p->dtype != FKV_BF16) return fail(FKV_ERROR_UNSUPPORTED, "4-bit decode takes bfloat16 queries and outputs");
+    if (p->num_q_heads / p->num_kv_heads == fkv::kHighGqa)
+        return fail(FKV_ERROR_UNSUPPORTED, "4-bit decode supports GQA ratios 1, 2, 4, 8");
+    if (p->seqlen_q != 1) return fail(FKV_ERROR_INVALID_VALUE, "decode needs seqlen_q == 1 (got %d)", p->seqlen_q);
+    if (p->batch == 0) return ok();
+    if (!q || !out) return fail(FKV_ERROR_INVALID_VALUE, "q or out is NULL");
+    if (!aligned16(q) || !aligned16(out)) return fail(FKV_ERROR_INVALID_VALUE, "q or out is not 16-byte aligned");
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return fail(FKV_ERROR_INVALID_VALUE, "lse is not 4-byte aligned");
+    if (seqlens_k && (reinterpret_cast<uintptr_t>(seqlens_k) & 3u))
+        return fail(FKV_ERROR_INVALID_VALUE, "seqlens_k is not 4-byte aligned");
+    for (int i = 0; i < ncaches; ++i)
+        if ((s = check_q4(p, caches[i], names[i]))) return s;
+    const bool fused = ncaches == 4;
+    if (fused) {
+        if (!fusion || !fusion->k_w1 || !fusion->k_wn || !fusion->v_w1 || !fusion->v_wn)
+            return fail(FKV_ERROR_INVALID_VALUE, "fusion weights missing");
+        if (!aligned16(fusion->k_w1) || !aligned16(fusion->k_wn) || !aligned16(fusion->v_w1) ||
+            !aligned16(fusion->v_wn))
+            return fail(FKV_ERROR_INVALID_VALUE, "fusion weights are not 16-byte aligned");
+    }
+    const fkv::DecodePlan pl = plan_decode(p, fused, true);
+    if (pl.total_bytes > 0) {
+        if (!workspace || workspace_bytes < pl.total_bytes)
+            return fail(FKV_ERROR_WORKSPACE, "workspace needs %zu bytes (got %zu)", pl.total_bytes,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+            return fail(FKV_ERROR_WORKSPACE, "workspace is not 256-byte aligned");
+    }
+    fkv::KiviDecodeArgs a{};
+    a.q = q;
+    a.qk1 = q4_of(caches[0]);
+    a.qv1 = q4_of(caches[fused ? 2 : 1]);
+    if (fused) {
+        a.qkn = q4_of(caches[1]);
+        a.qvn = q4_of(caches[3]);
+        a.kw1 = fusion->k_w1;
+        a.kwn = fusion->k_wn;
+        a.vw1 = fusion->v_w1;
+        a.vwn = fusion->v_wn;
+    }
+    a.seqlens = seqlens_k;
+    a.out = out;
+    a.lse = lse;
+    char* ws = static_cast<char*>(workspace);
+    a.ml = pl.total_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+    a.part = pl.total_bytes ? reinterpret_cast<float*>(ws + pl.ml_bytes) : nullptr;
+    a.B = p->batch;
+    a.Sk = p->seqlen_k;
+    a.Hq = p->num_q_heads;
+    a.Hkv = p->num_kv_heads;
+    a.D = p->head_dim;
+    a.G = p->num_q_heads / p->num_kv_heads;
+    a.n_splits = pl.n_splits;
+    a.chunk = pl.chunk;
+    a.scale_log2 = scale_log2_of(p);
+    if (std::getenv("FKV_TRACE"))
+        std::fprintf(stderr, "libfusedkv: 4-bit decode %s B=%d Sk=%d Hq=%d Hkv=%d D=%d waves=%d splits=%d chunk=%d\n",
+                     fused ? "fused" : "single", a.B, a.Sk, a.Hq, a.Hkv, a.D, pl.waves, a.n_splits, a.chunk);
+    const int rc = fkv::launch_kivi_decode(a, fused, pl.waves, stream);
+    if (rc) return fail(FKV_ERROR_LAUNCH, "4-bit decode launch failed (HIP error %d)", rc);
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -303,9 +390,13 @@ const char* fkv_last_error(void) { return g_last_error; }
 size_t fkv_decode_workspace_size(const fkv_params* params)
 {
     if (check_shape(params) != FKV_SUCCESS || params->seqlen_q != 1) return 0;
-    const size_t f = plan_decode(params, true).total_bytes;
-    const size_t s = plan_decode(params, false).total_bytes;
-    return f > s ? f : s;
+    size_t w = 0;
+    for (int kivi = 0; kivi < 2; ++kivi)
+        for (int fused = 0; fused < 2; ++fused) {
+            const size_t b = plan_decode(params, fused != 0, kivi != 0).total_bytes;
+            if (b > w) w = b;
+        }
+    return w;
 }
 
 fkv_status fkv_decode(const fkv_params* params, const void* q, fkv_cache k1, fkv_cache kn,
@@ -363,6 +454,69 @@ fkv_status fkv_check_tied(const float* host_k_w, int32_t h_kv, int32_t d, int32_
         }
     }
     return ok();
+}
+
+size_t fkv_kivi_codes_bytes(const fkv_params* params)
+{
+    if (!params || params->batch < 0 || params->seqlen_k < 0 || params->num_kv_heads < 1 ||
+        !supported_head_dim(params->head_dim))
+        return 0;
+    return (size_t)params->batch * params->num_kv_heads * params->seqlen_k * (params->head_dim / 2);
+}
+
+size_t fkv_kivi_meta_bytes(const fkv_params* params, int32_t is_value)
+{
+    if (!params || params->batch < 0 || params->seqlen_k < 0 || params->num_kv_heads < 1 ||
+        !supported_head_dim(params->head_dim))
+        return 0;
+    const int64_t bh = (int64_t)params->batch * params->num_kv_heads;
+    const int64_t n = is_value ? bh * params->seqlen_k * kivi_value_groups(params->head_dim)
+                               : bh * kivi_key_groups(params->seqlen_k) * params->head_dim;
+    return (size_t)n * 2;
+}
+
+fkv_status fkv_kivi_quantize(const fkv_params* params, fkv_cache src, int32_t is_value, fkv_q4_cache dst,
+                             void* stream)
+{
+    fkv_status s = check_shape(params);
+    if (s) return s;
+    if (params->dtype != FKV_BF16) return fail(FKV_ERROR_UNSUPPORTED, "the 4-bit quantiser reads bfloat16 caches");
+    if (is_value != 0 && is_value != 1) return fail(FKV_ERROR_INVALID_VALUE, "is_value must be 0 or 1");
+    if (params->batch == 0 || params->seqlen_k == 0) return ok();
+    if ((s = check_cache(params, src, "src"))) return s;
+    if ((s = check_q4(params, dst, "dst"))) return s;
+    fkv::KiviQuantArgs a{};
+    a.src = view_of(src);
+    a.codes = const_cast<void*>(dst.codes);
+    a.scale = const_cast<void*>(dst.scale);
+    a.minv = const_cast<void*>(dst.minv);
+    a.B = params->batch;
+    a.S = params->seqlen_k;
+    a.H = params->num_kv_heads;
+    a.D = params->head_dim;
+    a.is_value = is_value;
+    const int rc = fkv::launch_kivi_quantize(a, stream);
+    if (rc) return fail(FKV_ERROR_LAUNCH, "4-bit quantiser launch failed (HIP error %d)", rc);
+    return ok();
+}
+
+fkv_status fkv_kivi_decode(const fkv_params* params, const void* q, fkv_q4_cache k1, fkv_q4_cache kn,
+                           fkv_q4_cache v1, fkv_q4_cache vn, const fkv_fusion* fusion,
+                           const int32_t* seqlens_k, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream)
+{
+    const fkv_q4_cache c[4] = {k1, kn, v1, vn};
+    static const char* const n[4] = {"k1", "kn", "v1", "vn"};
+    return kivi_decode_common(params, q, c, n, 4, fusion, seqlens_k, out, lse, workspace, workspace_bytes, stream);
+}
+
+fkv_status fkv_kivi_lite_decode(const fkv_params* params, const void* q, fkv_q4_cache k_src, fkv_q4_cache v_src,
+                                const int32_t* seqlens_k, void* out, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream)
+{
+    const fkv_q4_cache c[2] = {k_src, v_src};
+    static const char* const n[2] = {"k_src", "v_src"};
+    return kivi_decode_common(params, q, c, n, 2, nullptr, seqlens_k, out, lse, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -436,6 +436,25 @@ int launch_d(const DecodeArgs& a, int waves, hipStream_t st)
 
 }  // namespace
 
+int launch_decode_combine_bf16(const DecodeArgs& a, void* stream)
+{
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (a.n_splits <= 1) return 0;
+    switch (a.D * 16 + a.G) {
+#define FKV_COMBINE_CASE(DD, GG)                                                                                 \
+    case DD * 16 + GG:                                                                                           \
+        hipLaunchKernelGGL((combine_kernel<uint16_t, DD, GG>), dim3(a.B * a.Hkv), dim3(kCombineThreads), 0, st, a); \
+        break;
+        FKV_COMBINE_CASE(64, 1) FKV_COMBINE_CASE(64, 2) FKV_COMBINE_CASE(64, 4) FKV_COMBINE_CASE(64, 8)
+        FKV_COMBINE_CASE(80, 1) FKV_COMBINE_CASE(80, 2) FKV_COMBINE_CASE(80, 4) FKV_COMBINE_CASE(80, 8)
+        FKV_COMBINE_CASE(96, 1) FKV_COMBINE_CASE(96, 2) FKV_COMBINE_CASE(96, 4) FKV_COMBINE_CASE(96, 8)
+        FKV_COMBINE_CASE(128, 1) FKV_COMBINE_CASE(128, 2) FKV_COMBINE_CASE(128, 4) FKV_COMBINE_CASE(128, 8)
+#undef FKV_COMBINE_CASE
+    default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}
+
 int launch_decode(const DecodeArgs& a, bool fused, int dtype, int waves, void* stream)
 {
     hipStream_t st = static_cast<hipStream_t>(stream);

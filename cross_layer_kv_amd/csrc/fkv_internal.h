@@ -59,6 +59,14 @@ constexpr int decode_waves(int dtype_f32, bool fused, int G)
     return G <= 2 ? 12 : (G == 4 ? 8 : 4);
 }
 
+// Waves per workgroup of the 4-bit decode kernel: its group coefficients
+// need more registers than the bf16 kernel, so fewer waves share a CU.
+constexpr int kivi_waves(bool fused, int G)
+{
+    if (fused) return G <= 4 ? 8 : 4;
+    return G <= 2 ? 12 : (G == 4 ? 8 : 4);
+}
+
 // Prefill (S_q == S_k), bf16 only.
 struct PrefillArgs {
     const void* q;          // [B, S, Hq, D] bf16
@@ -75,11 +83,41 @@ struct PrefillArgs {
     float scale_log2;
 };
 
+// KIVI-style 4-bit cache of one source, contiguous (see fusedkv.h):
+//   codes [B, Hkv, S, D/2] bytes (channel 2i low nibble, 2i+1 high)
+//   scale / minv fp16: keys [B, Hkv, ceil(S/32), D], values [B, Hkv, S, ceil(D/32)]
+struct Q4View {
+    const void* codes;
+    const void* scale;
+    const void* minv;
+};
+
+// Decode over 4-bit sources: the decode arguments (q, out, lse, workspace,
+// weights, shape, split plan; the View members are unused) plus the sources.
+struct KiviDecodeArgs : DecodeArgs {
+    Q4View qk1, qkn, qv1, qvn;  // qkn / qvn unused for single-source calls
+};
+
+// Quantisation of one bf16 source into a 4-bit cache.
+struct KiviQuantArgs {
+    View src;       // [B, S, H, D] bf16
+    void* codes;
+    void* scale;
+    void* minv;
+    int32_t B, S, H, D;
+    int32_t is_value;  // 0: per-channel groups of 32 tokens, 1: per-token groups of 32 channels
+};
+
 // Launchers (device code units).  They return 0 on success, else the HIP
 // error code of the failed launch.
 int launch_decode(const DecodeArgs& a, bool fused, int dtype, int waves, void* stream);
 // Decode with G == kHighGqa query heads per KV head (bfloat16, matrix cores).
 int launch_decode_hgqa(const DecodeArgs& a, bool fused, void* stream);
+// Merge of decode split partials (bfloat16 output); used by the 4-bit decode.
+int launch_decode_combine_bf16(const DecodeArgs& a, void* stream);
+// 4-bit KIVI-style sources: quantiser and decode (bfloat16 queries/outputs).
+int launch_kivi_quantize(const KiviQuantArgs& a, void* stream);
+int launch_kivi_decode(const KiviDecodeArgs& a, bool fused, int waves, void* stream);
 int launch_prefill(const PrefillArgs& a, bool fused, void* stream);
 // Query rows per prefill workgroup for a GQA ratio (0 when unsupported).
 int prefill_rows_per_tile(int G);

@@ -1,6 +1,7 @@
-// fkv_mfma_common.h -- device helpers shared by the matrix-core kernels
-// (causal prefill and high-GQA decode): fp16 / bf16 packing, the two-source
-// fusion dot products, half-wave exchanges and buffer-descriptor loads.
+// fkv_mfma_common.h -- device helpers shared by the kernels that are not the
+// plain decode (causal prefill, high-GQA decode, 4-bit decode and its
+// quantiser): fp16 / bf16 packing, the two-source fusion dot products,
+// half-wave and token-group exchanges and buffer-descriptor loads.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -82,6 +83,23 @@ __device__ __forceinline__ float halves_sum(float x)
 __device__ constexpr f16x2 kOnes2 = {(_Float16)1.0f, (_Float16)1.0f};
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Weight 2^(m - M) of a partial with max m against a common max M; 0 for an
+// empty partial (m = -inf).
+__device__ __forceinline__ float rel_weight(float m, float M) { return m == -INFINITY ? 0.0f : exp2_fast(m - M); }
+
+// Sum over the LPT (8 or 16) lanes of a token group with DPP permutations:
+// xor 1, xor 2 (quad permutes), then mirror within 8 and within 16 lanes.
+template <int LPT>
+__device__ __forceinline__ float token_group_sum(float v)
+{
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    if constexpr (LPT == 16)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    return v;
+}
 
 
 // Buffer descriptor over one (batch, KV head) slab of a cache: base at token 0

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define FKV_ABI_VERSION 1
+#define FKV_ABI_VERSION 2
 
 typedef enum {
     FKV_SUCCESS = 0,
@@ -209,6 +209,69 @@ fkv_status fkv_lite_prefill(const fkv_params* params, const void* q,
  */
 fkv_status fkv_check_tied(const float* host_k_w, int32_t h_kv, int32_t d,
                           int32_t pairing, float tol);
+
+/*
+ * ---- KIVI-style 4-bit source caches ----
+ * [Deck] frame "Four-bit KV quantization is the stronger combination"
+ * (Tables 14-15); [Notes] section A.6.5: FusedKV composed with 4-bit KIVI
+ * caches cuts the payload 4-fold on top of FusedKV's halving (1/8 of an FP16
+ * vanilla cache, metadata excluded).  The pages print no format; this one is
+ * the published KIVI scheme at 4 bits:
+ *   keys   grouped per channel over 32 consecutive tokens,
+ *   values grouped per token over 32 consecutive channels (the last group of
+ *          an axis may be shorter, e.g. 16 channels for D = 80);
+ *   a group keeps its minimum and scale = (max - min) / 15 as IEEE binary16;
+ *   code = rint((x - min) * (1 / scale)) clamped to 0..15 (0 if scale == 0),
+ *   decided in float32 with the rounded min and scale; x ~ min + scale*code.
+ * Arrays of one quantised source, contiguous, S = params->seqlen_k:
+ *   codes  uint8    [B, H_kv, S, D/2]  channel 2i in the low nibble, 2i+1 high
+ *   scale  binary16 keys [B, H_kv, ceil(S/32), D]; values [B, H_kv, S, ceil(D/32)]
+ *   minv   binary16 same shape as scale
+ * All three device pointers 16-byte aligned; the caller owns them.
+ */
+typedef struct {
+    const void* codes;
+    const void* scale;
+    const void* minv;
+} fkv_q4_cache;
+
+/* Bytes of codes of one quantised source, and of its scale (or minv) array
+ * (is_value 0: keys, 1: values).  0 for invalid params. */
+size_t fkv_kivi_codes_bytes(const fkv_params* params);
+size_t fkv_kivi_meta_bytes(const fkv_params* params, int32_t is_value);
+
+/*
+ * fkv_kivi_quantize -- write the 4-bit cache of one bfloat16 source: all
+ * seqlen_k tokens of every (batch row, KV head); dst arrays are overwritten.
+ * params: batch, seqlen_k, num_kv_heads, head_dim and dtype = FKV_BF16 are
+ * used (num_q_heads must still be a valid multiple).  src any strides with
+ * 16-byte aligned rows, as fkv_cache.  Asynchronous on `stream`.
+ */
+fkv_status fkv_kivi_quantize(const fkv_params* params, fkv_cache src,
+                             int32_t is_value, fkv_q4_cache dst, void* stream);
+
+/*
+ * fkv_kivi_decode -- fkv_decode over 4-bit sources: each element is
+ * dequantised in float32 registers (min + scale * code) and then fused as in
+ * fkv_decode.  k1/kn are key caches, v1/vn value caches in the format above.
+ * bfloat16 queries and outputs, G in {1, 2, 4, 8}; other arguments,
+ * workspace (fkv_decode_workspace_size covers these calls) and errors as
+ * fkv_decode.
+ */
+fkv_status fkv_kivi_decode(const fkv_params* params, const void* q,
+                           fkv_q4_cache k1, fkv_q4_cache kn, fkv_q4_cache v1,
+                           fkv_q4_cache vn, const fkv_fusion* fusion,
+                           const int32_t* seqlens_k, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* fkv_kivi_lite_decode -- one 4-bit key and one 4-bit value source
+ * (FusedKV-Lite: K^n and V^1); otherwise as fkv_kivi_decode. */
+fkv_status fkv_kivi_lite_decode(const fkv_params* params, const void* q,
+                                fkv_q4_cache k_src, fkv_q4_cache v_src,
+                                const int32_t* seqlens_k, void* out,
+                                float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

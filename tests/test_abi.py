@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib, B):
     assert set(names) == set(B.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.fkv_abi_version() == 1
+    assert lib.fkv_abi_version() == 2
     for s in range(5):
         assert lib.fkv_status_string(s)
     assert lib.fkv_status_string(99) == b"unknown status"
@@ -106,7 +106,7 @@ def test_decode_validation_codes(lib, B):
     p = _params(B, sk=8192)   # 4 (batch, kv head) units: the key axis is split, a workspace is needed
     need = lib.fkv_decode_workspace_size(ctypes.byref(p))
     assert need > 0
-    assert _decode(lib, B, p, ws_bytes=need - 1) == WS
+    assert _decode(lib, B, p, ws_bytes=256) == WS
     assert _decode(lib, B, p, ws=0) == WS
     assert _decode(lib, B, p, ws=FAKE + 16) == WS                  # not 256-byte aligned
     # an empty batch is a valid no-op: nothing is launched
@@ -115,6 +115,57 @@ def test_decode_validation_codes(lib, B):
     # G = 64 runs on the matrix cores: bfloat16 only; G = 32 is not served
     assert _decode(lib, B, _params(B, hq=128, hkv=2, dtype=0)) == UNS
     assert _decode(lib, B, _params(B, hq=64, hkv=2)) == UNS
+
+
+def _q4(B, ptr=FAKE):
+    return B.fkv_q4_cache(ptr, ptr, ptr)
+
+
+def _kivi_decode(lib, B, p, q=FAKE, caches=None, fusion="ok", out=FAKE, ws=FAKE, ws_bytes=1 << 24, lite=False):
+    caches = caches or [_q4(B)] * 4
+    if lite:
+        return lib.fkv_kivi_lite_decode(ctypes.byref(p), q, caches[0], caches[1], None, out, None, ws, ws_bytes,
+                                        None)
+    f = _fusion(B) if fusion == "ok" else fusion
+    return lib.fkv_kivi_decode(ctypes.byref(p), q, *caches, ctypes.byref(f) if f is not None else None, None, out,
+                               None, ws, ws_bytes, None)
+
+
+def test_kivi_validation_codes(lib, B):
+    INV, UNS, WS = B.FKV_ERROR_INVALID_VALUE, B.FKV_ERROR_UNSUPPORTED, B.FKV_ERROR_WORKSPACE
+    assert _kivi_decode(lib, B, _params(B, dtype=0)) == UNS                 # f32 queries
+    assert _kivi_decode(lib, B, _params(B, hq=128, hkv=2)) == UNS           # G = 64
+    assert _kivi_decode(lib, B, _params(B, hq=6, hkv=2)) == UNS             # G = 3
+    assert _kivi_decode(lib, B, _params(B, d=72)) == UNS
+    assert _kivi_decode(lib, B, _params(B, sq=2)) == INV
+    assert _kivi_decode(lib, B, _params(B), fusion=None) == INV
+    assert _kivi_decode(lib, B, _params(B), q=FAKE + 8) == INV
+    assert _kivi_decode(lib, B, _params(B), caches=[B.fkv_q4_cache(FAKE, 0, FAKE)] * 4) == INV
+    assert _kivi_decode(lib, B, _params(B), caches=[B.fkv_q4_cache(FAKE, FAKE + 2, FAKE)] * 4) == INV
+    assert _kivi_decode(lib, B, _params(B, sq=2), lite=True) == INV
+    assert _kivi_decode(lib, B, _params(B, batch=0)) == B.FKV_SUCCESS
+    assert _kivi_decode(lib, B, _params(B, batch=0), lite=True) == B.FKV_SUCCESS
+    # the workspace size covers the 4-bit plans, whose eight-wave fused
+    # workgroups split this shape the finest: 4 units x 64 splits of 128 tokens
+    p = _params(B, sk=8192)
+    need = lib.fkv_decode_workspace_size(ctypes.byref(p))
+    units, ns, G, D = 4, 64, 2, 64
+    assert need == math.ceil(units * ns * G * 2 * 4 / 256) * 256 + units * ns * G * D * 4
+    assert _kivi_decode(lib, B, p, ws_bytes=need - 1) == WS
+    assert _kivi_decode(lib, B, p, ws=FAKE + 16) == WS
+    # quantiser: bfloat16 source only, is_value 0 or 1, an empty cache is a no-op
+    c = _cache(B)
+    p = _params(B)
+    assert lib.fkv_kivi_quantize(ctypes.byref(_params(B, dtype=0)), c, 0, _q4(B), None) == UNS
+    assert lib.fkv_kivi_quantize(ctypes.byref(p), c, 2, _q4(B), None) == INV
+    assert lib.fkv_kivi_quantize(ctypes.byref(p), c, 0, B.fkv_q4_cache(FAKE, None, FAKE), None) == INV
+    assert lib.fkv_kivi_quantize(ctypes.byref(_params(B, sk=0)), c, 1, _q4(B, 0), None) == B.FKV_SUCCESS
+    # array sizes: codes D/2 bytes per token; key metadata per 32-token group
+    # and channel, value metadata per token and 32-channel group (fp16)
+    p = _params(B, batch=3, sk=100, hkv=2, hq=4, d=80)
+    assert lib.fkv_kivi_codes_bytes(ctypes.byref(p)) == 3 * 2 * 100 * 40
+    assert lib.fkv_kivi_meta_bytes(ctypes.byref(p), 0) == 3 * 2 * 4 * 80 * 2
+    assert lib.fkv_kivi_meta_bytes(ctypes.byref(p), 1) == 3 * 2 * 100 * 3 * 2
 
 
 def test_lite_decode_validation_codes(lib, B):
