@@ -44,6 +44,16 @@ class fkv_q4_cache(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("minv", ctypes.c_void_p)]
 
 
+class fkv_grad(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
+                ("stride_s", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
+
+
+class fkv_fusion_grad(ctypes.Structure):
+    _fields_ = [("k_w1", ctypes.c_void_p), ("k_wn", ctypes.c_void_p),
+                ("v_w1", ctypes.c_void_p), ("v_wn", ctypes.c_void_p)]
+
+
 class fkv_fusion(ctypes.Structure):
     _fields_ = [("k_w1", ctypes.c_void_p), ("k_wn", ctypes.c_void_p),
                 ("v_w1", ctypes.c_void_p), ("v_wn", ctypes.c_void_p)]
@@ -52,7 +62,8 @@ class fkv_fusion(ctypes.Structure):
 EXPORTS = ["fkv_abi_version", "fkv_status_string", "fkv_last_error", "fkv_decode_workspace_size",
            "fkv_decode", "fkv_lite_decode", "fkv_prefill", "fkv_lite_prefill", "fkv_check_tied",
            "fkv_kivi_codes_bytes", "fkv_kivi_meta_bytes", "fkv_kivi_quantize", "fkv_kivi_decode",
-           "fkv_kivi_lite_decode"]
+           "fkv_kivi_lite_decode", "fkv_backward_workspace_size", "fkv_prefill_backward",
+           "fkv_lite_prefill_backward"]
 
 _lib = None
 
@@ -100,7 +111,16 @@ def load_library(path: str = LIB_PATH):
     lib.fkv_kivi_lite_decode.restype = ctypes.c_int
     lib.fkv_kivi_lite_decode.argtypes = [P(fkv_params), vp, fkv_q4_cache, fkv_q4_cache, vp, vp, vp, vp,
                                          ctypes.c_size_t, vp]
-    if lib.fkv_abi_version() != 2:
+    lib.fkv_backward_workspace_size.restype = ctypes.c_size_t
+    lib.fkv_backward_workspace_size.argtypes = [P(fkv_params)]
+    lib.fkv_prefill_backward.restype = ctypes.c_int
+    lib.fkv_prefill_backward.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, fkv_cache, fkv_cache,
+                                         P(fkv_fusion), vp, vp, vp, vp, fkv_grad, fkv_grad, fkv_grad, fkv_grad,
+                                         P(fkv_fusion_grad), vp, ctypes.c_size_t, vp]
+    lib.fkv_lite_prefill_backward.restype = ctypes.c_int
+    lib.fkv_lite_prefill_backward.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, vp, vp, vp, vp, fkv_grad,
+                                              fkv_grad, vp, ctypes.c_size_t, vp]
+    if lib.fkv_abi_version() != 3:
         raise RuntimeError("libfusedkv ABI version mismatch")
     _lib = lib
     return lib
@@ -288,3 +308,51 @@ def fkv_kivi_lite_decode(q, k_src: Q4Cache, v_src: Q4Cache, *, out, workspace, l
     _check(lib.fkv_kivi_lite_decode(ctypes.byref(p), _dev(q, "q"), k_src.view(), v_src.view(),
                                     _dev(seqlens_k, "seqlens_k"), _dev(out, "out"), _dev(lse, "lse"),
                                     _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
+
+
+# ---- backward pass ----
+
+def grad_view(t: torch.Tensor) -> fkv_grad:
+    """Writable fkv_grad of a logical [B, S, H, D] tensor (any strides, channel
+    axis contiguous)."""
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("a gradient is a [B, S, H, D] view with a contiguous channel axis")
+    _dev(t, "gradient")
+    return fkv_grad(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def backward_workspace(q: torch.Tensor, k: torch.Tensor) -> torch.Tensor:
+    """A workspace for backward calls with these shapes (contents ignored)."""
+    n = load_library().fkv_backward_workspace_size(ctypes.byref(make_params(q, k, causal=True)))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+
+
+def fkv_prefill_backward(q, k1, kn, v1, vn, weights, out, lse, dout, *, dq, dk1, dkn, dv1, dvn, dweights,
+                         workspace, causal=True, softmax_scale=0.0, stream=None):
+    """Gradients of one FusedKV prefill layer (fkv_prefill_backward in
+    fusedkv.h).  dweights: four contiguous float32 [Hkv, D] tensors written
+    with the gradients of (a, a', b, b')."""
+    lib = load_library()
+    p = make_params(q, k1, softmax_scale=softmax_scale, causal=causal)
+    f = _fusion(weights)
+    for w in dweights:
+        if w.dtype != torch.float32 or not w.is_contiguous():
+            raise TypeError("weight gradients must be contiguous float32")
+    df = fkv_fusion_grad(*[_dev(w, "weight gradient") for w in dweights])
+    _check(lib.fkv_prefill_backward(ctypes.byref(p), _dev(q, "q"), cache_view(k1), cache_view(kn), cache_view(v1),
+                                    cache_view(vn), ctypes.byref(f), _dev(out, "out"), _dev(lse, "lse"),
+                                    _dev(dout, "dout"), _dev(dq, "dq"), grad_view(dk1), grad_view(dkn),
+                                    grad_view(dv1), grad_view(dvn), ctypes.byref(df), _dev(workspace, "workspace"),
+                                    workspace.numel(), _stream(stream)))
+
+
+def fkv_lite_prefill_backward(q, k_src, v_src, out, lse, dout, *, dq, dk, dv, workspace, causal=True,
+                              softmax_scale=0.0, stream=None):
+    """Gradients of a single-source prefill layer (FusedKV-Lite with (K^n,
+    V^1), or the plain control): dk, dv are the gradients of k_src, v_src."""
+    lib = load_library()
+    p = make_params(q, k_src, softmax_scale=softmax_scale, causal=causal)
+    _check(lib.fkv_lite_prefill_backward(ctypes.byref(p), _dev(q, "q"), cache_view(k_src), cache_view(v_src),
+                                         _dev(out, "out"), _dev(lse, "lse"), _dev(dout, "dout"), _dev(dq, "dq"),
+                                         grad_view(dk), grad_view(dv), _dev(workspace, "workspace"),
+                                         workspace.numel(), _stream(stream)))

@@ -367,6 +367,126 @@ fkv_status kivi_decode_common(const fkv_params* p, const void* q, const fkv_q4_c
     return ok();
 }
 
+// ---- backward ----
+
+struct BwdLayout {
+    size_t lse2, delta, wpart, total;
+    int32_t nkt;
+};
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+BwdLayout backward_layout(const fkv_params* p)
+{
+    BwdLayout l{};
+    l.nkt = (p->seqlen_k + fkv::kBwdKeyTile - 1) / fkv::kBwdKeyTile;
+    const size_t rows = (size_t)p->batch * p->num_q_heads * p->seqlen_q * 4;
+    l.lse2 = 0;
+    l.delta = round256(rows);
+    l.wpart = l.delta + round256(rows);
+    l.total = l.wpart + round256((size_t)p->batch * p->num_kv_heads * l.nkt * 4 * p->head_dim * 4);
+    return l;
+}
+
+fkv_status check_grad(const fkv_params* p, const fkv_grad& c, const char* name)
+{
+    const fkv_cache v{c.data, c.stride_b, c.stride_s, c.stride_h};
+    if (!c.data) return fail(FKV_ERROR_INVALID_VALUE, "%s.data is NULL", name);
+    return check_cache(p, v, name);
+}
+
+fkv::OutView out_of(const fkv_grad& c) { return fkv::OutView{c.data, c.stride_b, c.stride_s, c.stride_h}; }
+
+fkv_status backward_common(const fkv_params* p, const void* q, const fkv_cache* caches, const char* const* names,
+                           int ncaches, const fkv_fusion* fusion, const void* out, const float* lse, const void* dout,
+                           void* dq, const fkv_grad* grads, const char* const* gnames, const fkv_fusion_grad* dfusion,
+                           void* workspace, size_t workspace_bytes, void* stream)
+{
+    fkv_status s = check_shape(p);
+    if (s) return s;
+    if (p->dtype != FKV_BF16) return fail(FKV_ERROR_UNSUPPORTED, "the backward pass supports bfloat16 data only");
+    if (p->seqlen_q != p->seqlen_k)
+        return fail(FKV_ERROR_UNSUPPORTED, "the backward pass needs seqlen_q == seqlen_k (got %d, %d)", p->seqlen_q,
+                    p->seqlen_k);
+    if (p->causal != 0 && p->causal != 1) return fail(FKV_ERROR_INVALID_VALUE, "causal must be 0 or 1");
+    const int G = p->num_q_heads / p->num_kv_heads;
+    if (G == fkv::kHighGqa) return fail(FKV_ERROR_UNSUPPORTED, "the backward pass supports GQA ratios 1, 2, 4, 8");
+    if (p->batch == 0 || p->seqlen_q == 0) return ok();
+    if (!q || !out || !dout || !dq || !lse) return fail(FKV_ERROR_INVALID_VALUE, "q, out, dout, dq or lse is NULL");
+    if (!aligned16(q) || !aligned16(out) || !aligned16(dout) || !aligned16(dq))
+        return fail(FKV_ERROR_INVALID_VALUE, "q, out, dout or dq is not 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(FKV_ERROR_INVALID_VALUE, "lse is not 4-byte aligned");
+    for (int i = 0; i < ncaches; ++i)
+        if ((s = check_cache(p, caches[i], names[i]))) return s;
+    for (int i = 0; i < ncaches; ++i)
+        if ((s = check_grad(p, grads[i], gnames[i]))) return s;
+    const bool fused = ncaches == 4;
+    if (fused) {
+        if (!fusion || !fusion->k_w1 || !fusion->k_wn || !fusion->v_w1 || !fusion->v_wn)
+            return fail(FKV_ERROR_INVALID_VALUE, "fusion weights missing");
+        if (!aligned16(fusion->k_w1) || !aligned16(fusion->k_wn) || !aligned16(fusion->v_w1) ||
+            !aligned16(fusion->v_wn))
+            return fail(FKV_ERROR_INVALID_VALUE, "fusion weights are not 16-byte aligned");
+        if (!dfusion || !dfusion->k_w1 || !dfusion->k_wn || !dfusion->v_w1 || !dfusion->v_wn)
+            return fail(FKV_ERROR_INVALID_VALUE, "fusion weight gradients missing");
+        const float* d4[4] = {dfusion->k_w1, dfusion->k_wn, dfusion->v_w1, dfusion->v_wn};
+        for (const float* d : d4)
+            if (reinterpret_cast<uintptr_t>(d) & 3u)
+                return fail(FKV_ERROR_INVALID_VALUE, "fusion weight gradients are not 4-byte aligned");
+    }
+    const BwdLayout lay = backward_layout(p);
+    if (!workspace || workspace_bytes < lay.total)
+        return fail(FKV_ERROR_WORKSPACE, "workspace needs %zu bytes (got %zu)", lay.total,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(FKV_ERROR_WORKSPACE, "workspace is not 256-byte aligned");
+
+    fkv::BwdArgs a{};
+    a.q = q;
+    a.k1 = view_of(caches[0]);
+    a.v1 = view_of(caches[fused ? 2 : 1]);
+    a.dk1 = out_of(grads[0]);
+    a.dv1 = out_of(grads[fused ? 2 : 1]);
+    if (fused) {
+        a.kn = view_of(caches[1]);
+        a.vn = view_of(caches[3]);
+        a.dkn = out_of(grads[1]);
+        a.dvn = out_of(grads[3]);
+        a.kw1 = fusion->k_w1;
+        a.kwn = fusion->k_wn;
+        a.vw1 = fusion->v_w1;
+        a.vwn = fusion->v_wn;
+        a.dkw1 = dfusion->k_w1;
+        a.dkwn = dfusion->k_wn;
+        a.dvw1 = dfusion->v_w1;
+        a.dvwn = dfusion->v_wn;
+    }
+    a.out = out;
+    a.lse = lse;
+    a.dout = dout;
+    a.dq = dq;
+    char* ws = static_cast<char*>(workspace);
+    a.lse2 = reinterpret_cast<float*>(ws + lay.lse2);
+    a.delta = reinterpret_cast<float*>(ws + lay.delta);
+    a.wpart = reinterpret_cast<float*>(ws + lay.wpart);
+    a.B = p->batch;
+    a.S = p->seqlen_q;
+    a.Hq = p->num_q_heads;
+    a.Hkv = p->num_kv_heads;
+    a.D = p->head_dim;
+    a.G = G;
+    a.causal = p->causal;
+    a.nkt = lay.nkt;
+    a.scale_log2 = scale_log2_of(p);
+    a.scale = (float)(p->softmax_scale != 0.0f ? (double)p->softmax_scale : 1.0 / std::sqrt((double)p->head_dim));
+    if (std::getenv("FKV_TRACE"))
+        std::fprintf(stderr, "libfusedkv: backward %s B=%d S=%d Hq=%d Hkv=%d D=%d causal=%d key tiles=%d\n",
+                     fused ? "fused" : "single", a.B, a.S, a.Hq, a.Hkv, a.D, a.causal, a.nkt);
+    const int rc = fkv::launch_backward(a, fused, stream);
+    if (rc) return fail(FKV_ERROR_LAUNCH, "backward launch failed (HIP error %d)", rc);
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -517,6 +637,38 @@ fkv_status fkv_kivi_lite_decode(const fkv_params* params, const void* q, fkv_q4_
     const fkv_q4_cache c[2] = {k_src, v_src};
     static const char* const n[2] = {"k_src", "v_src"};
     return kivi_decode_common(params, q, c, n, 2, nullptr, seqlens_k, out, lse, workspace, workspace_bytes, stream);
+}
+
+size_t fkv_backward_workspace_size(const fkv_params* params)
+{
+    if (check_shape(params) != FKV_SUCCESS || params->seqlen_q != params->seqlen_k) return 0;
+    if (params->batch == 0 || params->seqlen_q == 0) return 0;
+    return backward_layout(params).total;
+}
+
+fkv_status fkv_prefill_backward(const fkv_params* params, const void* q, fkv_cache k1, fkv_cache kn, fkv_cache v1,
+                                fkv_cache vn, const fkv_fusion* fusion, const void* out, const float* lse,
+                                const void* dout, void* dq, fkv_grad dk1, fkv_grad dkn, fkv_grad dv1, fkv_grad dvn,
+                                const fkv_fusion_grad* dfusion, void* workspace, size_t workspace_bytes, void* stream)
+{
+    const fkv_cache c[4] = {k1, kn, v1, vn};
+    const fkv_grad gr[4] = {dk1, dkn, dv1, dvn};
+    static const char* const n[4] = {"k1", "kn", "v1", "vn"};
+    static const char* const gn[4] = {"dk1", "dkn", "dv1", "dvn"};
+    return backward_common(params, q, c, n, 4, fusion, out, lse, dout, dq, gr, gn, dfusion, workspace,
+                           workspace_bytes, stream);
+}
+
+fkv_status fkv_lite_prefill_backward(const fkv_params* params, const void* q, fkv_cache k_src, fkv_cache v_src,
+                                     const void* out, const float* lse, const void* dout, void* dq, fkv_grad dk,
+                                     fkv_grad dv, void* workspace, size_t workspace_bytes, void* stream)
+{
+    const fkv_cache c[2] = {k_src, v_src};
+    const fkv_grad gr[2] = {dk, dv};
+    static const char* const n[2] = {"k_src", "v_src"};
+    static const char* const gn[2] = {"dk", "dv"};
+    return backward_common(params, q, c, n, 2, nullptr, out, lse, dout, dq, gr, gn, nullptr, workspace,
+                           workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -1,0 +1,669 @@
+// fkv_backward.hip -- backward pass of FusedKV reconstruction-layer attention
+// (causal or full, S_q == S_k) on gfx950 matrix cores, bf16 operands with
+// float32 accumulation.
+//
+// Pages cited (by title):
+//   [Deck]  "FusedKV: Reconstructing KV Caches with Cross-Layer Fusion",
+//           frame "FusedKV learns two-source, channel-wise fusion"
+//           (Eqs. (4)-(5)): the per-channel vectors are learned with the
+//           model, trained end to end, so a training step differentiates the
+//           fused attention with respect to the queries, the four source
+//           caches and the four vectors.  Frame "Lite separates the key
+//           source from the value source" (Eq. (6)) for one key and one value
+//           source.
+//   [Notes] "FusedKV:通过跨层融合重构 KV 缓存", sections 2.1-2.3.
+//
+// For a loss with output gradient dO (the chain rule through the fusion and
+// the softmax; Kf = a K1 + a' Kn, Vf = b V1 + b' Vn per channel):
+//   P = softmax(scale Q Kf^T) (recomputed from the forward LSE)
+//   dVf = sum_h P^T dO,  dP = dO Vf^T,  dS = P (dP - rowsum(dO O))
+//   dQ = scale dS Kf,  dKf = scale sum_h dS^T Q
+//   dK1 = a dKf, dKn = a' dKf, dV1 = b dVf, dVn = b' dVf
+//   da = sum_{b,t} dKf K1 (likewise a', b, b'): column sums over tokens.
+// The fused tiles are rebuilt in registers / LDS and never stored in HBM,
+// like the forward pass ([Notes] section 2.3: fusion on demand).
+//
+// Kernels
+//   1. prep: per (batch, head, row) the LSE in log2 units and
+//      rowsum(dO * O) (float32).
+//   2. key tiles: a workgroup of 4 waves owns 128 keys of one (batch, KV
+//      head); each wave keeps its 32 fused keys and values as matrix-core
+//      operands in registers and walks the query rows of all G heads of the
+//      group in 64-row LDS tiles, accumulating dKf and dVf.  It writes the
+//      four source gradients and its partial column sums for the weight
+//      gradients.
+//   3. query tiles: a workgroup of 4 waves owns 128 (query row, head)
+//      columns and walks the fused key/value tiles (built in LDS once per
+//      workgroup) accumulating dQ.  dQ is thus written once, with no float
+//      atomics, and every result is run-to-run deterministic.
+//   4. reduce: the weight-gradient partials summed in a fixed order.
+//
+// Operand layouts (v_mfma_f32_32x32x16_bf16, A 32x16, B 16x32, C 32x32): a
+// lane (l32 = lane % 32, hi = lane / 32) holds row l32 of A / column l32 of B
+// with K elements 8*hi .. 8*hi+7, and C entries (rows 8j + 4hi + i, column
+// l32) for j, i in 0..3.  A C tile therefore serves directly as the A (or B)
+// operand of the next product when that product's K index is the C row
+// index, taken in the order 16c + 4hi + (e%4) + 8(e/4) for element e of
+// k-step c.  The other operand of such a product reads its K rows in that
+// order from a row-major LDS tile with two transposing reads
+// (ds_read_b64_tr_b16), which is how Q and dO serve both as row operands
+// (for the scores and dP) and as transposed operands (for dK and dV).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fkv_internal.h"
+#include "fkv_mfma_common.h"
+
+namespace fkv {
+namespace {
+
+using namespace dev;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kBwdThreads = 256;  // 4 waves
+constexpr int kKeysPerWg = kBwdKeyTile;  // key-tile kernel: 32 keys per wave
+constexpr int kQRows = 64;        // key-tile kernel: query rows per LDS tile
+constexpr int kKTile = 64;        // query-tile kernel: keys per LDS tile
+
+// Slot of the (batch, KV head, key tile) weight-gradient partial.
+__device__ __forceinline__ int64_t item_index(int b, int g, int kt, int Hkv, int nkt)
+{
+    return ((int64_t)b * Hkv + g) * nkt + kt;
+}
+
+__device__ __forceinline__ f32x16 mma(uint4 a, uint4 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+// Row operand: row r0 + l32 of a row-major LDS tile, channels 16 ks + 8 hi.
+__device__ __forceinline__ uint4 row_frag(const uint16_t* tile, int pitch, int r0, int ks, int l32, int hi)
+{
+    return *reinterpret_cast<const uint4*>(tile + (r0 + l32) * pitch + ks * 16 + hi * 8);
+}
+
+// Transposed operand: column col0 + l32 of a row-major LDS tile, K rows
+// krow0 + 4 hi + (e % 4) + 8 (e / 4) for elements e = 0..7.  Within each
+// 16-lane group a source lane supplies 4 channels of one row and receives
+// one channel of 4 rows.
+__device__ __forceinline__ uint4 tr_frag(const uint16_t* tile, int pitch, int krow0, int col0, int l32, int hi)
+{
+    const uint16_t* p = tile + (krow0 + hi * 4 + ((l32 & 15) >> 2)) * pitch + col0 + (l32 >> 4) * 16 + (l32 & 3) * 4;
+    const v4s x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
+    const v4s x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p + 8 * pitch));
+    return __builtin_bit_cast(uint4, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// 8 channels (16 bytes) of bf16 -> fused (w1 x1 + wn xn) bf16, float32 math.
+__device__ __forceinline__ uint4 fuse8_bf16(uint4 x1, uint4 xn, const float* w1, const float* wn)
+{
+    const uint32_t a[4] = {x1.x, x1.y, x1.z, x1.w};
+    const uint32_t b[4] = {xn.x, xn.y, xn.z, xn.w};
+    uint32_t r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = w1[2 * i] * bf16_lo(a[i]) + wn[2 * i] * bf16_lo(b[i]);
+        const float hi = w1[2 * i + 1] * bf16_hi(a[i]) + wn[2 * i + 1] * bf16_hi(b[i]);
+        r[i] = pack2_bf16(lo, hi);
+    }
+    return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
+__device__ __forceinline__ const uint16_t* row_ptr(const View& v, int b, int t, int h)
+{
+    return static_cast<const uint16_t*>(v.data) + (int64_t)b * v.sb + (int64_t)t * v.ss + (int64_t)h * v.sh;
+}
+
+__device__ __forceinline__ uint16_t* out_row(const OutView& v, int b, int t, int h)
+{
+    return static_cast<uint16_t*>(v.data) + (int64_t)b * v.sb + (int64_t)t * v.ss + (int64_t)h * v.sh;
+}
+
+__device__ __forceinline__ void load8f(const float* p, float* w)
+{
+    const float4 x = *reinterpret_cast<const float4*>(p);
+    const float4 y = *reinterpret_cast<const float4*>(p + 4);
+    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+    w[4] = y.x; w[5] = y.y; w[6] = y.z; w[7] = y.w;
+}
+
+// ---- 1. prep: LSE in log2 units and rowsum(dO * O), [B, Hq, S] ----
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs a)
+{
+    const int64_t n = (int64_t)a.B * a.S * a.Hq;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int h = (int)(i % a.Hq);
+    const int64_t bs = i / a.Hq;
+    const int t = (int)(bs % a.S), b = (int)(bs / a.S);
+    const uint16_t* o = static_cast<const uint16_t*>(a.out) + i * D;
+    const uint16_t* g = static_cast<const uint16_t*>(a.dout) + i * D;
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+        const uint4 x = *reinterpret_cast<const uint4*>(o + c * 8);
+        const uint4 y = *reinterpret_cast<const uint4*>(g + c * 8);
+        const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) s += bf16_lo(xs[k]) * bf16_lo(ys[k]) + bf16_hi(xs[k]) * bf16_hi(ys[k]);
+    }
+    const int64_t r = ((int64_t)b * a.Hq + h) * a.S + t;
+    a.delta[r] = s;
+    a.lse2[r] = a.lse[r] * kLog2e;
+}
+
+// ---- 2. key tiles: dKf, dVf, source gradients, weight partials ----
+template <int D, bool FUSED, int G>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdArgs a)
+{
+    constexpr int DP = (D + 31) / 32 * 32;  // channels padded to whole 32-column blocks
+    constexpr int NDB = DP / 32;
+    constexpr int KS = D / 16;
+    constexpr int P = DP + 8;               // LDS row pitch (elements)
+    constexpr int CPR = D / 8;              // 16-byte chunks per row
+    constexpr int TILE = kQRows * P;
+    constexpr int SP = DP + 4;              // pitch of the float32 transpose buffer
+    static_assert(2 * 2 * TILE * 2 >= kKeysPerWg * SP * 4, "transpose buffer fits in the tile buffers");
+
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];  // [buf][Q, dO][row][P]
+    __shared__ __attribute__((aligned(16))) float Ls[2][kQRows];
+    __shared__ __attribute__((aligned(16))) float Dl[2][kQRows];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    const int nkt = a.nkt;
+    const int items = a.B * a.Hkv * nkt;
+    int item = blockIdx.x;
+    if ((items & 7) == 0) item = (blockIdx.x & 7) * (items >> 3) + (blockIdx.x >> 3);
+    const int unit = item / nkt;
+    const int kt = item - unit * nkt;  // low key tiles see the most query rows: they start first
+    const int b = unit / a.Hkv, g = unit - (unit / a.Hkv) * a.Hkv;
+    const int S = a.S;
+    const int k0 = kt * kKeysPerWg;
+    const int kw = k0 + wave * 32;
+
+    // zero the padded channels [D, DP) of every tile row (never loaded)
+    if constexpr (DP > D) {
+        for (int i = tid; i < 2 * 2 * kQRows * (DP - D); i += kBwdThreads) {
+            const int r = i / (DP - D), c = i - r * (DP - D);
+            smem[r * P + D + c] = 0;
+        }
+    }
+
+    // ---- this wave's 32 fused keys / values as B operands (lane: key l32) ----
+    uint4 kreg[KS], vreg[KS];
+    {
+        const int key = kw + l32;
+        const bool ok = key < S;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int ch = ks * 16 + hi * 8;
+            uint4 k1 = make_uint4(0u, 0u, 0u, 0u), kn = k1, v1 = k1, vn = k1;
+            if (ok) {
+                k1 = *reinterpret_cast<const uint4*>(row_ptr(a.k1, b, key, g) + ch);
+                v1 = *reinterpret_cast<const uint4*>(row_ptr(a.v1, b, key, g) + ch);
+                if constexpr (FUSED) {
+                    kn = *reinterpret_cast<const uint4*>(row_ptr(a.kn, b, key, g) + ch);
+                    vn = *reinterpret_cast<const uint4*>(row_ptr(a.vn, b, key, g) + ch);
+                }
+            }
+            if constexpr (FUSED) {
+                float w1[8], wn[8];
+                load8f(a.kw1 + g * D + ch, w1);
+                load8f(a.kwn + g * D + ch, wn);
+                kreg[ks] = fuse8_bf16(k1, kn, w1, wn);
+                load8f(a.vw1 + g * D + ch, w1);
+                load8f(a.vwn + g * D + ch, wn);
+                vreg[ks] = fuse8_bf16(v1, vn, w1, wn);
+            } else {
+                kreg[ks] = k1;
+                vreg[ks] = v1;
+            }
+        }
+    }
+
+    f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) {
+        dk[i] = f32x16{};
+        dv[i] = f32x16{};
+    }
+
+    // query tiles: rows qb .. qb+63 of head g*G + hh; causal rows below k0
+    // see none of these keys
+    const int q_begin = a.causal ? (k0 / kQRows) * kQRows : 0;
+    const int nqb = S > q_begin ? (S - q_begin + kQRows - 1) / kQRows : 0;
+    const int nit = nqb * G;
+
+    // tile loader: thread -> (row, 16-byte chunk) items of Q and dO
+    constexpr int NITEM = kQRows * CPR;
+    constexpr int NPASS = (NITEM + kBwdThreads - 1) / kBwdThreads;
+    uint4 xq[NPASS], xo[NPASS];
+    float xl = 0.0f, xd = 0.0f;
+    auto load_tile = [&](int it) {
+        const int qb = q_begin + (it / G) * kQRows;
+        const int h = g * G + it % G;
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const int e = tid + p * kBwdThreads;
+            const int r = e / CPR, c = e - (e / CPR) * CPR;
+            const int row = qb + r;
+            xq[p] = make_uint4(0u, 0u, 0u, 0u);
+            xo[p] = xq[p];
+            if (e < NITEM && row < S) {
+                const int64_t off = (((int64_t)b * S + row) * a.Hq + h) * D + c * 8;
+                xq[p] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + off);
+                xo[p] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.dout) + off);
+            }
+        }
+        if (tid < kQRows) {
+            const int row = qb + tid;
+            const int64_t r = ((int64_t)b * a.Hq + h) * S + row;
+            xl = row < S ? a.lse2[r] : 0.0f;
+            xd = row < S ? a.delta[r] : 0.0f;
+        }
+    };
+    auto store_tile = [&](int buf) {
+        uint16_t* qs = smem + (buf * 2 + 0) * TILE;
+        uint16_t* os = smem + (buf * 2 + 1) * TILE;
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const int e = tid + p * kBwdThreads;
+            if (e < NITEM) {
+                const int r = e / CPR, c = e - (e / CPR) * CPR;
+                *reinterpret_cast<uint4*>(qs + r * P + c * 8) = xq[p];
+                *reinterpret_cast<uint4*>(os + r * P + c * 8) = xo[p];
+            }
+        }
+        if (tid < kQRows) {
+            Ls[buf][tid] = xl;
+            Dl[buf][tid] = xd;
+        }
+    };
+
+    const float sl2 = a.scale_log2;
+    if (nit > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    for (int it = 0; it < nit; ++it) {
+        const int buf = it & 1;
+        __syncthreads();  // tile `it` stored; tile it-1's readers are done
+        if (it + 1 < nit) load_tile(it + 1);
+        const int qb = q_begin + (it / G) * kQRows;
+        const uint16_t* qs = smem + (buf * 2 + 0) * TILE;
+        const uint16_t* os = smem + (buf * 2 + 1) * TILE;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const int qs0 = qb + sb * 32;
+            // wave-uniform skips: rows past the end, or (causal) every key
+            // of the wave after every row of the block
+            if (qs0 >= S || (a.causal && qs0 + 31 < kw) || kw >= S) continue;
+            f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                sacc = mma(row_frag(qs, P, sb * 32, ks, l32, hi), kreg[ks], sacc);
+                pacc = mma(row_frag(os, P, sb * 32, ks, l32, hi), vreg[ks], pacc);
+            }
+            // lane: key kw + l32; entries: query rows qs0 + 8j + 4hi + i
+            const int key = kw + l32;
+            float pv[16], dsv[16];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 L4 = *reinterpret_cast<const float4*>(&Ls[buf][sb * 32 + 8 * j + 4 * hi]);
+                const float4 D4 = *reinterpret_cast<const float4*>(&Dl[buf][sb * 32 + 8 * j + 4 * hi]);
+                const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int q = qs0 + 8 * j + 4 * hi + i;
+                    const bool vis = key < S && q < S && (!a.causal || key <= q);
+                    const float p = vis ? exp2_fast(sacc[4 * j + i] * sl2 - Lv[i]) : 0.0f;
+                    pv[4 * j + i] = p;
+                    dsv[4 * j + i] = p * (pacc[4 * j + i] - Dv[i]);
+                }
+            }
+            uint4 pa[2], da[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                pa[c] = make_uint4(pack2_bf16(pv[8 * c + 0], pv[8 * c + 1]), pack2_bf16(pv[8 * c + 2], pv[8 * c + 3]),
+                                   pack2_bf16(pv[8 * c + 4], pv[8 * c + 5]), pack2_bf16(pv[8 * c + 6], pv[8 * c + 7]));
+                da[c] = make_uint4(pack2_bf16(dsv[8 * c + 0], dsv[8 * c + 1]), pack2_bf16(dsv[8 * c + 2], dsv[8 * c + 3]),
+                                   pack2_bf16(dsv[8 * c + 4], dsv[8 * c + 5]), pack2_bf16(dsv[8 * c + 6], dsv[8 * c + 7]));
+            }
+#pragma unroll
+            for (int nb = 0; nb < NDB; ++nb)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    dv[nb] = mma(pa[c], tr_frag(os, P, sb * 32 + 16 * c, nb * 32, l32, hi), dv[nb]);
+                    dk[nb] = mma(da[c], tr_frag(qs, P, sb * 32 + 16 * c, nb * 32, l32, hi), dk[nb]);
+                }
+        }
+        if (it + 1 < nit) store_tile(buf ^ 1);
+    }
+
+    // ---- epilogue: transpose each accumulator through LDS (float32) ----
+    float* st = reinterpret_cast<float*>(smem);
+    float* part = nullptr;
+    if constexpr (FUSED) part = a.wpart + (int64_t)item_index(b, g, kt, a.Hkv, nkt) * 4 * D;
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {  // 0: keys, 1: values
+        __syncthreads();
+#pragma unroll
+        for (int nb = 0; nb < NDB; ++nb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float x = which == 0 ? dk[nb][4 * j + i] * a.scale : dv[nb][4 * j + i];
+                    st[(wave * 32 + 8 * j + 4 * hi + i) * SP + nb * 32 + l32] = x;
+                }
+        __syncthreads();
+        const OutView o1 = which == 0 ? a.dk1 : a.dv1;
+        for (int e = tid; e < kKeysPerWg * CPR; e += kBwdThreads) {
+            const int r = e / CPR, c = e - (e / CPR) * CPR;
+            const int key = k0 + r;
+            if (key >= S) continue;
+            float x[8];
+            load8f(st + r * SP + c * 8, x);
+            if constexpr (FUSED) {
+                const OutView on = which == 0 ? a.dkn : a.dvn;
+                float w1[8], wn[8];
+                load8f((which == 0 ? a.kw1 : a.vw1) + g * D + c * 8, w1);
+                load8f((which == 0 ? a.kwn : a.vwn) + g * D + c * 8, wn);
+                uint32_t r1[4], rn[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    r1[k] = pack2_bf16(w1[2 * k] * x[2 * k], w1[2 * k + 1] * x[2 * k + 1]);
+                    rn[k] = pack2_bf16(wn[2 * k] * x[2 * k], wn[2 * k + 1] * x[2 * k + 1]);
+                }
+                *reinterpret_cast<uint4*>(out_row(o1, b, key, g) + c * 8) = make_uint4(r1[0], r1[1], r1[2], r1[3]);
+                *reinterpret_cast<uint4*>(out_row(on, b, key, g) + c * 8) = make_uint4(rn[0], rn[1], rn[2], rn[3]);
+            } else {
+                uint32_t r1[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) r1[k] = pack2_bf16(x[2 * k], x[2 * k + 1]);
+                *reinterpret_cast<uint4*>(out_row(o1, b, key, g) + c * 8) = make_uint4(r1[0], r1[1], r1[2], r1[3]);
+            }
+        }
+        if constexpr (FUSED) {
+            // column sums over this tile's keys of dKf * K1 and dKf * Kn
+            // (values: dVf * V1, dVf * Vn), one channel per thread
+            const View& s1 = which == 0 ? a.k1 : a.v1;
+            const View& sn = which == 0 ? a.kn : a.vn;
+            for (int d = tid; d < D; d += kBwdThreads) {
+                float acc1 = 0.0f, accn = 0.0f;
+                const int nr = min(kKeysPerWg, S - k0);
+                for (int r = 0; r < nr; ++r) {
+                    const float x = st[r * SP + d];
+                    acc1 += x * bf16_lo(row_ptr(s1, b, k0 + r, g)[d]);
+                    accn += x * bf16_lo(row_ptr(sn, b, k0 + r, g)[d]);
+                }
+                part[(2 * which + 0) * D + d] = acc1;
+                part[(2 * which + 1) * D + d] = accn;
+            }
+        }
+    }
+}
+
+// ---- 3. query tiles: dQ ----
+template <int D, bool FUSED, int G>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdArgs a)
+{
+    constexpr int DP = (D + 31) / 32 * 32;
+    constexpr int NDB = DP / 32;
+    constexpr int KS = D / 16;
+    constexpr int P = DP + 8;
+    constexpr int CPR = D / 8;
+    constexpr int TILE = kKTile * P;
+    constexpr int HPW = G < 4 ? G : 4;       // heads per workgroup
+    constexpr int NHG = G / HPW;             // head groups per KV head
+    constexpr int RB = 4 / HPW;              // 32-row blocks per workgroup
+    constexpr int BM = RB * 32;              // query rows per workgroup
+
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];  // [buf][K~, V~][row][P]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    const int nqt = (a.S + BM - 1) / BM;
+    const int items = a.B * a.Hkv * NHG * nqt;
+    int item = blockIdx.x;
+    if ((items & 7) == 0) item = (blockIdx.x & 7) * (items >> 3) + (blockIdx.x >> 3);
+    const int unit = item / nqt;
+    const int qt = a.causal ? nqt - 1 - (item - unit * nqt) : item - unit * nqt;  // heaviest first
+    const int ug = unit / NHG, hg = unit - (unit / NHG) * NHG;
+    const int b = ug / a.Hkv, g = ug - (ug / a.Hkv) * a.Hkv;
+    const int S = a.S;
+    const int h = g * G + hg * HPW + wave % HPW;
+    const int r0 = qt * BM + (wave / HPW) * 32;  // this wave's 32 query rows
+
+    if constexpr (DP > D) {
+        for (int i = tid; i < 2 * 2 * kKTile * (DP - D); i += kBwdThreads) {
+            const int r = i / (DP - D), c = i - r * (DP - D);
+            smem[r * P + D + c] = 0;
+        }
+    }
+
+    // queries and output gradients as B operands (lane: query row r0 + l32)
+    const int row = r0 + l32;
+    const bool row_ok = row < S;
+    uint4 qreg[KS], oreg[KS];
+    {
+        const int64_t off = (((int64_t)b * S + (row_ok ? row : 0)) * a.Hq + h) * D + hi * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qreg[ks] = make_uint4(0u, 0u, 0u, 0u);
+            oreg[ks] = qreg[ks];
+            if (row_ok) {
+                qreg[ks] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + off + ks * 16);
+                oreg[ks] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.dout) + off + ks * 16);
+            }
+        }
+    }
+    const int64_t lrow = ((int64_t)b * a.Hq + h) * S + (row_ok ? row : 0);
+    const float lse2 = row_ok ? a.lse2[lrow] : 0.0f;
+    const float dlt = row_ok ? a.delta[lrow] : 0.0f;
+
+    f32x16 dq[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) dq[i] = f32x16{};
+
+    const int q_last = min(S, (qt + 1) * BM) - 1;   // last row of the workgroup
+    const int kend = a.causal ? q_last + 1 : S;
+    const int nt = (kend + kKTile - 1) / kKTile;
+
+    constexpr int NITEM = kKTile * CPR;
+    constexpr int NPASS = (NITEM + kBwdThreads - 1) / kBwdThreads;
+    constexpr int NSRC = FUSED ? 4 : 2;
+    uint4 xr[NSRC][NPASS];
+    auto load_tile = [&](int t) {
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const int e = tid + p * kBwdThreads;
+            const int r = e / CPR, c = e - (e / CPR) * CPR;
+            const int key = t * kKTile + r;
+            const bool ok = e < NITEM && key < S;
+#pragma unroll
+            for (int s = 0; s < NSRC; ++s) xr[s][p] = make_uint4(0u, 0u, 0u, 0u);
+            if (ok) {
+                xr[0][p] = *reinterpret_cast<const uint4*>(row_ptr(a.k1, b, key, g) + c * 8);
+                xr[1][p] = *reinterpret_cast<const uint4*>(row_ptr(a.v1, b, key, g) + c * 8);
+                if constexpr (FUSED) {
+                    xr[2][p] = *reinterpret_cast<const uint4*>(row_ptr(a.kn, b, key, g) + c * 8);
+                    xr[3][p] = *reinterpret_cast<const uint4*>(row_ptr(a.vn, b, key, g) + c * 8);
+                }
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+        uint16_t* kt_ = smem + (buf * 2 + 0) * TILE;
+        uint16_t* vt_ = smem + (buf * 2 + 1) * TILE;
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const int e = tid + p * kBwdThreads;
+            if (e >= NITEM) continue;
+            const int r = e / CPR, c = e - (e / CPR) * CPR;
+            uint4 kf = xr[0][p], vf = xr[1][p];
+            if constexpr (FUSED) {
+                float w1[8], wn[8];
+                load8f(a.kw1 + g * D + c * 8, w1);
+                load8f(a.kwn + g * D + c * 8, wn);
+                kf = fuse8_bf16(xr[0][p], xr[2][p], w1, wn);
+                load8f(a.vw1 + g * D + c * 8, w1);
+                load8f(a.vwn + g * D + c * 8, wn);
+                vf = fuse8_bf16(xr[1][p], xr[3][p], w1, wn);
+            }
+            *reinterpret_cast<uint4*>(kt_ + r * P + c * 8) = kf;
+            *reinterpret_cast<uint4*>(vt_ + r * P + c * 8) = vf;
+        }
+    };
+
+    const float sl2 = a.scale_log2;
+    if (nt > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    for (int t = 0; t < nt; ++t) {
+        const int buf = t & 1;
+        __syncthreads();
+        if (t + 1 < nt) load_tile(t + 1);
+        const uint16_t* kt_ = smem + (buf * 2 + 0) * TILE;
+        const uint16_t* vt_ = smem + (buf * 2 + 1) * TILE;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int kk0 = t * kKTile + kb * 32;
+            if (kk0 >= S || r0 >= S || (a.causal && kk0 > r0 + 31)) continue;  // wave-uniform
+            f32x16 st = f32x16{}, dpt = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                st = mma(row_frag(kt_, P, kb * 32, ks, l32, hi), qreg[ks], st);
+                dpt = mma(row_frag(vt_, P, kb * 32, ks, l32, hi), oreg[ks], dpt);
+            }
+            // lane: query row; entries: keys kk0 + 8j + 4hi + i
+            float dsv[16];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = kk0 + 8 * j + 4 * hi + i;
+                    const bool vis = row_ok && key < S && (!a.causal || key <= row);
+                    const float p = vis ? exp2_fast(st[4 * j + i] * sl2 - lse2) : 0.0f;
+                    dsv[4 * j + i] = p * (dpt[4 * j + i] - dlt);
+                }
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const uint4 da = make_uint4(pack2_bf16(dsv[8 * c + 0], dsv[8 * c + 1]),
+                                            pack2_bf16(dsv[8 * c + 2], dsv[8 * c + 3]),
+                                            pack2_bf16(dsv[8 * c + 4], dsv[8 * c + 5]),
+                                            pack2_bf16(dsv[8 * c + 6], dsv[8 * c + 7]));
+#pragma unroll
+                for (int nb = 0; nb < NDB; ++nb)
+                    dq[nb] = mma(da, tr_frag(kt_, P, kb * 32 + 16 * c, nb * 32, l32, hi), dq[nb]);
+            }
+        }
+        if (t + 1 < nt) store_tile(buf ^ 1);
+    }
+
+    // lane: channel nb*32 + l32; entries: rows r0 + 8j + 4hi + i
+    uint16_t* dqp = static_cast<uint16_t*>(a.dq);
+#pragma unroll
+    for (int nb = 0; nb < NDB; ++nb) {
+        const int ch = nb * 32 + l32;
+        if (ch >= D) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = r0 + 8 * j + 4 * hi + i;
+                if (r < S) {
+                    const uint32_t pk = pack2_bf16(dq[nb][4 * j + i] * a.scale, 0.0f);
+                    dqp[(((int64_t)b * S + r) * a.Hq + h) * D + ch] = (uint16_t)(pk & 0xffffu);
+                }
+            }
+    }
+}
+
+// ---- 4. weight gradients: sum of the per-(batch, key tile) partials ----
+__global__ __launch_bounds__(256) void bwd_wreduce_kernel(const BwdArgs a)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;  // (w, g, d)
+    if (i >= 4 * a.Hkv * a.D) return;
+    const int d = i % a.D;
+    const int g = (i / a.D) % a.Hkv;
+    const int w = i / (a.D * a.Hkv);
+    float s = 0.0f;
+    for (int b = 0; b < a.B; ++b)
+        for (int kt = 0; kt < a.nkt; ++kt)
+            s += a.wpart[((int64_t)item_index(b, g, kt, a.Hkv, a.nkt) * 4 + w) * a.D + d];
+    float* out = w == 0 ? a.dkw1 : (w == 1 ? a.dkwn : (w == 2 ? a.dvw1 : a.dvwn));
+    out[g * a.D + d] = s;
+}
+
+template <int D, bool FUSED, int G>
+int launch_bwd3(const BwdArgs& a, hipStream_t st)
+{
+    const int64_t rows = (int64_t)a.B * a.S * a.Hq;
+    hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, a);
+    int rc = (int)hipGetLastError();
+    if (rc) return rc;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, FUSED, G>), dim3((unsigned)(a.B * a.Hkv * a.nkt)), dim3(kBwdThreads), 0, st,
+                       a);
+    if ((rc = (int)hipGetLastError())) return rc;
+    constexpr int HPW = G < 4 ? G : 4;
+    constexpr int BM = (4 / HPW) * 32;
+    const int nqt = (a.S + BM - 1) / BM;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, FUSED, G>), dim3((unsigned)(a.B * a.Hkv * (G / HPW) * nqt)),
+                       dim3(kBwdThreads), 0, st, a);
+    if ((rc = (int)hipGetLastError())) return rc;
+    if constexpr (FUSED) {
+        hipLaunchKernelGGL(bwd_wreduce_kernel, dim3((unsigned)((4 * a.Hkv * a.D + 255) / 256)), dim3(256), 0, st, a);
+        rc = (int)hipGetLastError();
+    }
+    return rc;
+}
+
+template <int D, bool FUSED>
+int launch_bwd2(const BwdArgs& a, hipStream_t st)
+{
+    switch (a.G) {
+    case 1: return launch_bwd3<D, FUSED, 1>(a, st);
+    case 2: return launch_bwd3<D, FUSED, 2>(a, st);
+    case 4: return launch_bwd3<D, FUSED, 4>(a, st);
+    case 8: return launch_bwd3<D, FUSED, 8>(a, st);
+    default: return (int)hipErrorInvalidValue;
+    }
+}
+
+template <bool FUSED>
+int launch_bwd1(const BwdArgs& a, hipStream_t st)
+{
+    switch (a.D) {
+    case 64: return launch_bwd2<64, FUSED>(a, st);
+    case 80: return launch_bwd2<80, FUSED>(a, st);
+    case 96: return launch_bwd2<96, FUSED>(a, st);
+    case 128: return launch_bwd2<128, FUSED>(a, st);
+    default: return (int)hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int launch_backward(const BwdArgs& a, bool fused, void* stream)
+{
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (a.B == 0 || a.S == 0) return 0;
+    return fused ? launch_bwd1<true>(a, st) : launch_bwd1<false>(a, st);
+}
+
+}  // namespace fkv

@@ -108,6 +108,43 @@ struct KiviQuantArgs {
     int32_t is_value;  // 0: per-channel groups of 32 tokens, 1: per-token groups of 32 channels
 };
 
+// A writable [B, S, H, D] view in elements; channel stride 1.
+struct OutView {
+    void* data;
+    int64_t sb, ss, sh;
+};
+
+// Backward pass (S_q == S_k, bfloat16).  Single-source calls (Lite or the
+// plain control) use k1 / v1 as the key / value source, dk1 / dv1 as their
+// gradients, and leave the n-sources, the weights and their gradients unused.
+struct BwdArgs {
+    const void* q;          // [B, S, Hq, D]
+    View k1, kn, v1, vn;
+    const float* kw1;       // [Hkv, D] each
+    const float* kwn;
+    const float* vw1;
+    const float* vwn;
+    const void* out;        // forward output O [B, S, Hq, D]
+    const float* lse;       // forward LSE (natural log) [B, Hq, S]
+    const void* dout;       // dO [B, S, Hq, D]
+    void* dq;               // [B, S, Hq, D]
+    OutView dk1, dkn, dv1, dvn;
+    float* dkw1;            // [Hkv, D] each
+    float* dkwn;
+    float* dvw1;
+    float* dvwn;
+    float* lse2;            // workspace [B, Hq, S]: LSE * log2(e)
+    float* delta;           // workspace [B, Hq, S]: rowsum(dO * O)
+    float* wpart;           // workspace [B, Hkv, nkt, 4, D]: weight-gradient partials
+    int32_t B, S, Hq, Hkv, D, G, causal;
+    int32_t nkt;            // key tiles of 128 per (batch, KV head)
+    float scale;            // softmax scale
+    float scale_log2;       // softmax scale * log2(e)
+};
+
+// Keys per workgroup of the backward key-tile kernel (sizes the workspace).
+constexpr int kBwdKeyTile = 128;
+
 // Launchers (device code units).  They return 0 on success, else the HIP
 // error code of the failed launch.
 int launch_decode(const DecodeArgs& a, bool fused, int dtype, int waves, void* stream);
@@ -119,6 +156,7 @@ int launch_decode_combine_bf16(const DecodeArgs& a, void* stream);
 int launch_kivi_quantize(const KiviQuantArgs& a, void* stream);
 int launch_kivi_decode(const KiviDecodeArgs& a, bool fused, int waves, void* stream);
 int launch_prefill(const PrefillArgs& a, bool fused, void* stream);
+int launch_backward(const BwdArgs& a, bool fused, void* stream);
 // Query rows per prefill workgroup for a GQA ratio (0 when unsupported).
 int prefill_rows_per_tile(int G);
 

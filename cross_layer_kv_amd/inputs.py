@@ -132,6 +132,16 @@ def make_queries(B: int, Sq: int, Hq: int, D: int, dtype: torch.dtype, seed: int
     return out
 
 
+def make_grad_output(B: int, S: int, Hq: int, D: int, dtype: torch.dtype, seed: int, device="cpu",
+                     std: float = 1.0) -> torch.Tensor:
+    """Output gradient dO [B, S, Hq, D] for a backward call: N(0, std^2)
+    draws (on the CPU generator, so that every device gets the same values),
+    rounded to ``dtype``."""
+    gen = _gen(seed, "cpu")
+    x = std * _normal((B, S, Hq, D), gen, "cpu")
+    return x.to(dtype).to(device)
+
+
 def make_weights(Hkv: int, D: int, seed: int, pairing: str = "interleaved", tied: bool = True,
                  mean: float = 0.5, std: float = 0.25, device="cpu"):
     """Per-layer fusion vectors (a, a', b, b') as float32 [Hkv, D] tensors.

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define FKV_ABI_VERSION 2
+#define FKV_ABI_VERSION 3
 
 typedef enum {
     FKV_SUCCESS = 0,
@@ -272,6 +272,84 @@ fkv_status fkv_kivi_lite_decode(const fkv_params* params, const void* q,
                                 const int32_t* seqlens_k, void* out,
                                 float* lse, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * ---- Backward pass (training through the fusion) ----
+ * [Deck] frame "FusedKV learns two-source, channel-wise fusion" (Eqs.
+ * (4)-(5)): the fusion vectors are learned with the model, end to end, so a
+ * training step needs the gradients of a reconstruction layer's attention
+ * with respect to its queries, the four source caches and the four vectors.
+ * For a loss with output gradient dO (the LSE output is not differentiated),
+ * with Kf = a*K1 + a'*Kn, Vf = b*V1 + b'*Vn and P the softmax probabilities:
+ *   dVf = sum_h P^T dO, dS = P * (dO Vf^T - rowsum(dO * O)),
+ *   dQ = scale dS Kf, dKf = scale sum_h dS^T Q,
+ *   dK1 = a*dKf, dKn = a'*dKf, dV1 = b*dVf, dVn = b'*dVf,
+ *   da[g, d] = sum over batch rows and tokens of dKf * K1 (a': Kn; b: dVf *
+ *   V1; b': dVf * Vn) -- per channel; a RoPE-tied parameter's gradient is
+ *   the sum over its channel pair.
+ * The sum over h runs over the G query heads of KV head g.
+ */
+
+/* A writable [B, S, H_kv, D] gradient view: element strides for b, s, h;
+ * channel stride 1; base and rows 16-byte aligned. */
+typedef struct {
+    void* data;
+    int64_t stride_b, stride_s, stride_h;
+} fkv_grad;
+
+/* Gradients of the fusion vectors, device float32 [H_kv, D] each,
+ * overwritten (not accumulated) by each call. */
+typedef struct {
+    float* k_w1;
+    float* k_wn;
+    float* v_w1;
+    float* v_wn;
+} fkv_fusion_grad;
+
+/* Workspace bytes for fkv_prefill_backward / fkv_lite_prefill_backward with
+ * these params (0 when the params are invalid or empty). */
+size_t fkv_backward_workspace_size(const fkv_params* params);
+
+/*
+ * fkv_prefill_backward -- gradients of fkv_prefill for one layer: seqlen_q ==
+ * seqlen_k, bfloat16 data, G in {1, 2, 4, 8}, causal 0 or 1.  Recomputes the
+ * probabilities from the forward LSE; matrix-core operands are bfloat16
+ * (fused tiles, probabilities and dS rounded once from float32), all
+ * accumulation float32.  Outputs are overwritten, not accumulated.  Every
+ * result is run-to-run deterministic (no float atomics).
+ *
+ *   q, out, dout  device [B, S, H_q, D] bfloat16 (out: the forward output)
+ *   lse           device float32 [B, H_q, S] (the forward LSE, natural log)
+ *   dq            device [B, S, H_q, D] bfloat16
+ *   dk1 .. dvn    gradient views of K^1, K^n, V^1, V^n (bfloat16)
+ *   dfusion       device float32 gradients of (a, a', b, b')
+ *   workspace     >= fkv_backward_workspace_size bytes, 256-byte aligned,
+ *                 contents ignored
+ * Errors as fkv_prefill; FKV_ERROR_WORKSPACE for a short workspace.
+ */
+fkv_status fkv_prefill_backward(const fkv_params* params, const void* q,
+                                fkv_cache k1, fkv_cache kn, fkv_cache v1,
+                                fkv_cache vn, const fkv_fusion* fusion,
+                                const void* out, const float* lse,
+                                const void* dout, void* dq, fkv_grad dk1,
+                                fkv_grad dkn, fkv_grad dv1, fkv_grad dvn,
+                                const fkv_fusion_grad* dfusion,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * fkv_lite_prefill_backward -- gradients of fkv_lite_prefill: one key and one
+ * value source (FusedKV-Lite with (K^n, V^1), [Deck] frame "Lite separates
+ * the key source from the value source", Eq. (6); or the plain control), so
+ * dk and dv are the gradients of k_src and v_src.  Otherwise as
+ * fkv_prefill_backward.
+ */
+fkv_status fkv_lite_prefill_backward(const fkv_params* params, const void* q,
+                                     fkv_cache k_src, fkv_cache v_src,
+                                     const void* out, const float* lse,
+                                     const void* dout, void* dq, fkv_grad dk,
+                                     fkv_grad dv, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib, B):
     assert set(names) == set(B.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.fkv_abi_version() == 2
+    assert lib.fkv_abi_version() == 3
     for s in range(5):
         assert lib.fkv_status_string(s)
     assert lib.fkv_status_string(99) == b"unknown status"
@@ -191,6 +191,55 @@ def test_prefill_validation_codes(lib, B):
     p = _params(B, sq=64, sk=64)
     c = _cache(B)
     assert lib.fkv_lite_prefill(ctypes.byref(p), FAKE, c, B.fkv_cache(0, 0, 64, 0), FAKE, None, None) == INV
+
+
+def _grad(B, d=64, hkv=2, sk=64, ptr=FAKE):
+    return B.fkv_grad(ptr, hkv * sk * d, d, sk * d)
+
+
+def _bwd(lib, B, p, q=FAKE, fusion="ok", dfusion="ok", grads=None, ws=FAKE, ws_bytes=1 << 26, lse=FAKE, lite=False):
+    c = _cache(B)
+    g = grads or [_grad(B)] * 4
+    if lite:
+        return lib.fkv_lite_prefill_backward(ctypes.byref(p), q, c, c, FAKE, lse, FAKE, FAKE, g[0], g[1], ws,
+                                             ws_bytes, None)
+    f = _fusion(B) if fusion == "ok" else fusion
+    df = B.fkv_fusion_grad(FAKE, FAKE, FAKE, FAKE) if dfusion == "ok" else dfusion
+    return lib.fkv_prefill_backward(ctypes.byref(p), q, c, c, c, c, ctypes.byref(f) if f is not None else None,
+                                    FAKE, lse, FAKE, FAKE, *g, ctypes.byref(df) if df is not None else None, ws,
+                                    ws_bytes, None)
+
+
+def test_backward_validation_codes(lib, B):
+    INV, UNS, WS = B.FKV_ERROR_INVALID_VALUE, B.FKV_ERROR_UNSUPPORTED, B.FKV_ERROR_WORKSPACE
+    ok = dict(sq=64, sk=64)
+    assert _bwd(lib, B, _params(B, dtype=0, **ok)) == UNS                 # f32
+    assert _bwd(lib, B, _params(B, sq=32, sk=64)) == UNS                  # S_q != S_k
+    assert _bwd(lib, B, _params(B, hq=128, hkv=2, **ok)) == UNS           # G = 64
+    assert _bwd(lib, B, _params(B, causal=2, **ok)) == INV
+    assert _bwd(lib, B, _params(B, d=100, **ok)) == UNS
+    assert _bwd(lib, B, _params(B, **ok), fusion=None) == INV
+    assert _bwd(lib, B, _params(B, **ok), dfusion=None) == INV
+    assert _bwd(lib, B, _params(B, **ok), dfusion=B.fkv_fusion_grad(FAKE, FAKE + 2, FAKE, FAKE)) == INV
+    assert _bwd(lib, B, _params(B, **ok), q=FAKE + 4) == INV
+    assert _bwd(lib, B, _params(B, **ok), lse=None) == INV
+    assert _bwd(lib, B, _params(B, **ok), grads=[_grad(B, ptr=0)] * 4) == INV
+    assert _bwd(lib, B, _params(B, **ok), grads=[B.fkv_grad(FAKE, 2 * 64 * 64, 60, 64 * 64)] * 4) == INV
+    p = _params(B, **ok)
+    need = lib.fkv_backward_workspace_size(ctypes.byref(p))
+    # LSE*log2(e) and rowsum(dO*O) rows (B*Hq*S floats each, 256-byte
+    # rounded) and the weight-gradient partials (B*Hkv key tiles x 4 x D)
+    rows = 2 * 4 * 64 * 4
+    assert need == 2 * (-(-rows // 256) * 256) + 2 * 2 * 1 * 4 * 64 * 4
+    assert _bwd(lib, B, p, ws_bytes=need - 1) == WS
+    assert _bwd(lib, B, p, ws=FAKE + 64) == WS
+    assert _bwd(lib, B, p, ws=None) == WS
+    assert _bwd(lib, B, _params(B, sq=2, sk=64), lite=True) == UNS
+    assert _bwd(lib, B, _params(B, batch=0, **ok)) == B.FKV_SUCCESS
+    assert _bwd(lib, B, _params(B, sq=0, sk=0)) == B.FKV_SUCCESS
+    assert _bwd(lib, B, _params(B, batch=0, **ok), lite=True) == B.FKV_SUCCESS
+    assert lib.fkv_backward_workspace_size(ctypes.byref(_params(B, sq=1, sk=64))) == 0
+    assert lib.fkv_backward_workspace_size(None) == 0
 
 
 def test_workspace_size(lib, B):
