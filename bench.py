@@ -56,6 +56,9 @@ WORKLOADS = {
     "hgqa-decode": dict(kind="decode", name="high-GQA FusedKV decode (128 query heads over 2 KV heads, G=64), 8 layers",
                         B=16, S=32768, Hq=128, Hkv=2, D=128, layers=8, seed=0xF0006),
     "1.5b-prefill": dict(kind="prefill", **PREFILL),
+    "1.5b-prefill-bwd": dict(kind="backward", name="1.5B-shape FusedKV causal prefill backward (dQ, source and "
+                             "fusion-weight gradients), layers 13-24", B=4, S=8192, Hq=16, Hkv=8, D=128, layers=12,
+                             seed=0xF0003),
     "4b-prefill": dict(kind="prefill", name="4B-shape FusedKV causal prefill, layers 19-36 fused from layers 1 and 18",
                        B=1, S=16384, Hq=32, Hkv=16, D=80, layers=18, seed=0xF0004),
     "long-decode-b1": dict(kind="stack", name="1.5B-shape long-context decode, whole 24-layer stack, batch 1",
@@ -239,6 +242,62 @@ def run_prefill(cfg, steps, warmup, stream):
         res[name] = dict(ms_per_step=ms, ms_per_layer=ms / nl,
                          tflops=fl * nl / (ms * 1e-3) / 1e12)
     del qs, out, base
+    torch.cuda.empty_cache()
+    return res
+
+
+def backward_flops(B, S, Hq, D):
+    """Five products (recomputed scores, dP, dV, dQ, dK) over the causal
+    triangle including the diagonal, FMA = 2: 2.5 x the forward's."""
+    return 5 * D * S * (S + 1) * B * Hq
+
+
+def run_backward(cfg, steps, warmup, stream):
+    """One step = `layers` backward calls (distinct queries, output
+    gradients and weights per layer) over the same four sources; the forward
+    outputs and LSEs they consume are computed once, untimed."""
+    import torch
+    from cross_layer_kv_amd import binding, inputs
+    dev = "cuda:0"
+    B, S, Hq, Hkv, D, nl = cfg["B"], cfg["S"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["layers"]
+    base = inputs.make_layer(B, S, S, Hq, Hkv, D, torch.bfloat16, cfg["seed"], dev, decode=False)
+    qs = [base.q] + [inputs.make_queries(B, S, Hq, D, torch.bfloat16, cfg["seed"] * 97 + i, dev)
+                     for i in range(1, nl)]
+    ws_list = [base.weights] + [inputs.make_weights(Hkv, D, cfg["seed"] * 89 + i, device=dev)
+                                for i in range(1, nl)]
+    douts = [inputs.make_grad_output(B, S, Hq, D, torch.bfloat16, cfg["seed"] * 83 + i, dev) for i in range(nl)]
+    fwd = {"fused": [], "lite": []}
+    for i in range(nl):
+        o, l = torch.empty_like(qs[i]), torch.empty(B, Hq, S, dtype=torch.float32, device=dev)
+        binding.fkv_prefill(qs[i], base.k1, base.kn, base.v1, base.vn, ws_list[i], out=o, lse=l, causal=True)
+        fwd["fused"].append((o, l))
+        o, l = torch.empty_like(qs[i]), torch.empty(B, Hq, S, dtype=torch.float32, device=dev)
+        binding.fkv_lite_prefill(qs[i], base.kn, base.v1, out=o, lse=l, causal=True)
+        fwd["lite"].append((o, l))
+    dq = torch.empty_like(base.q)
+    grads = [torch.empty(B, S, Hkv, D, dtype=torch.bfloat16, device=dev) for _ in range(4)]
+    dw = [torch.empty(Hkv, D, dtype=torch.float32, device=dev) for _ in range(4)]
+    ws = binding.backward_workspace(base.q, base.k1)
+
+    def fused_step():
+        for i in range(nl):
+            o, l = fwd["fused"][i]
+            binding.fkv_prefill_backward(qs[i], base.k1, base.kn, base.v1, base.vn, ws_list[i], o, l, douts[i],
+                                         dq=dq, dk1=grads[0], dkn=grads[1], dv1=grads[2], dvn=grads[3], dweights=dw,
+                                         workspace=ws, causal=True, stream=stream)
+
+    def lite_step():
+        for i in range(nl):
+            o, l = fwd["lite"][i]
+            binding.fkv_lite_prefill_backward(qs[i], base.kn, base.v1, o, l, douts[i], dq=dq, dk=grads[0],
+                                              dv=grads[2], workspace=ws, causal=True, stream=stream)
+
+    res = {}
+    fl = backward_flops(B, S, Hq, D)
+    for name, fn in (("fused", fused_step), ("lite", lite_step)):
+        ms = _time_region(fn, max(1, steps // 2), max(1, warmup // 2), stream)
+        res[name] = dict(ms_per_step=ms, ms_per_layer=ms / nl, tflops=fl * nl / (ms * 1e-3) / 1e12)
+    del qs, douts, fwd, base
     torch.cuda.empty_cache()
     return res
 
@@ -494,6 +553,18 @@ def other_workload(args, line, stream):
                                               for k in ("fused", "lite")}
         line["stack"]["bytes_over_vanilla"] = {k: round(res[k]["bytes"] / res["vanilla"]["bytes"], 3)
                                                for k in ("fused", "lite")}
+    elif kind == "backward":
+        res = run_backward(cfg, args.steps, args.warmup, stream)
+        f = res["fused"]
+        line.update(value=round(f["tflops"], 2), unit="TFLOP/s", ms_per_step=round(f["ms_per_step"], 4),
+                    metric="fused-KV causal prefill backward TFLOP/s (% MFMA)",
+                    config=dict(shape, layers_per_step=cfg["layers"]))
+        line["roofline"] = {"bound": "mfma", "achieved": round(f["tflops"], 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(f["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                            "flops_per_launch": backward_flops(cfg["B"], cfg["S"], cfg["Hq"], cfg["D"]),
+                            "avg_call_ms": round(f["ms_per_layer"], 4)}
+        line["backward_variants"] = {k: {"TFLOP/s": round(v["tflops"], 2), "ms_per_layer": round(v["ms_per_layer"], 4),
+                                         "frac": round(v["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)} for k, v in res.items()}
     elif kind == "kivi":
         res = run_kivi(cfg, args.steps, args.warmup, stream)
         f = res["fused"]
