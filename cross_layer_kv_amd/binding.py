@@ -100,7 +100,7 @@ def load_library(path: str = LIB_PATH):
     lib.fkv_check_tied.restype = ctypes.c_int
     lib.fkv_check_tied.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float]
     lib.fkv_kivi_codes_bytes.restype = ctypes.c_size_t
-    lib.fkv_kivi_codes_bytes.argtypes = [P(fkv_params)]
+    lib.fkv_kivi_codes_bytes.argtypes = [P(fkv_params), ctypes.c_int32]
     lib.fkv_kivi_meta_bytes.restype = ctypes.c_size_t
     lib.fkv_kivi_meta_bytes.argtypes = [P(fkv_params), ctypes.c_int32]
     lib.fkv_kivi_quantize.restype = ctypes.c_int
@@ -120,7 +120,7 @@ def load_library(path: str = LIB_PATH):
     lib.fkv_lite_prefill_backward.restype = ctypes.c_int
     lib.fkv_lite_prefill_backward.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, vp, vp, vp, vp, fkv_grad,
                                               fkv_grad, vp, ctypes.c_size_t, vp]
-    if lib.fkv_abi_version() != 3:
+    if lib.fkv_abi_version() != 4:
         raise RuntimeError("libfusedkv ABI version mismatch")
     _lib = lib
     return lib
@@ -248,28 +248,37 @@ def fkv_check_tied(k_w: torch.Tensor, pairing: str = "interleaved", tol: float =
 # ---- KIVI-style 4-bit source caches ----
 
 class Q4Cache:
-    """Device arrays of one 4-bit source (layout in include/fusedkv.h):
-    codes uint8 [B, Hkv, S, D/2], scale and minv float16 (keys
-    [B, Hkv, ceil(S/32), D], values [B, Hkv, S, ceil(D/32)])."""
+    """Device arrays of one 4-bit source (layout in include/fusedkv.h).
+    Keys: codes uint8 [B, Hkv, S, D/2], scale and minv float16
+    [B, Hkv, NB, D]; values: codes uint8 [B, Hkv, NB, D, 16], scale and minv
+    float16 [B, Hkv, NB, ceil(D/32), 32]; NB = ceil(S/32)."""
 
-    def __init__(self, codes, scale, minv, is_value):
+    def __init__(self, codes, scale, minv, is_value, seqlen=None):
         self.codes, self.scale, self.minv, self.is_value = codes, scale, minv, bool(is_value)
+        self._seqlen = seqlen
 
     def view(self) -> fkv_q4_cache:
         return fkv_q4_cache(_dev(self.codes, "codes"), _dev(self.scale, "scale"), _dev(self.minv, "minv"))
 
     @property
     def seqlen(self):
-        return self.codes.shape[2]
+        if not self.is_value:
+            return self.codes.shape[2]
+        return self._seqlen if self._seqlen is not None else self.codes.shape[2] * 32
 
 
 def kivi_empty(B, S, Hkv, D, is_value, device="cuda"):
     """Uninitialised 4-bit cache arrays of the library's layout."""
-    ng = (D + 31) // 32 if is_value else (S + 31) // 32
-    meta = (B, Hkv, S, ng) if is_value else (B, Hkv, ng, D)
-    return Q4Cache(torch.empty((B, Hkv, S, D // 2), dtype=torch.uint8, device=device),
+    nb = (S + 31) // 32
+    if is_value:
+        codes = (B, Hkv, nb, D, 16)
+        meta = (B, Hkv, nb, (D + 31) // 32, 32)
+    else:
+        codes = (B, Hkv, S, D // 2)
+        meta = (B, Hkv, nb, D)
+    return Q4Cache(torch.empty(codes, dtype=torch.uint8, device=device),
                    torch.empty(meta, dtype=torch.float16, device=device),
-                   torch.empty(meta, dtype=torch.float16, device=device), is_value)
+                   torch.empty(meta, dtype=torch.float16, device=device), is_value, S)
 
 
 def fkv_kivi_quantize(src: torch.Tensor, is_value: bool, *, dst: Q4Cache | None = None, num_q_heads=None,
@@ -285,6 +294,7 @@ def fkv_kivi_quantize(src: torch.Tensor, is_value: bool, *, dst: Q4Cache | None 
 
 
 def _kivi_params(q, c: Q4Cache, softmax_scale):
+    """c: the KEY cache (its token count is exact; value codes are padded)."""
     B, Sq, Hq, D = q.shape
     return fkv_params(B, Sq, c.seqlen, Hq, c.codes.shape[1], D, _dtype(q), float(softmax_scale), 0)
 

@@ -111,7 +111,7 @@ fkv::DecodePlan plan_decode(const fkv_params* p, bool fused, bool kivi = false)
     // G = 64 runs the matrix-core kernel: 64-token tiles, and it aims at two
     // workgroups per CU
     const bool wide = G == fkv::kHighGqa;
-    const int64_t iter = wide ? 64 : (int64_t)pl.waves * 16;
+    const int64_t iter = wide ? 64 : (int64_t)pl.waves * (kivi ? 32 : 16);
     const int64_t target = wide ? 512 : 256;
     const int64_t max_splits = S > 0 ? (S + iter - 1) / iter : 1;
     int64_t ns = units > 0 ? (target + units - 1) / units : 1;
@@ -576,12 +576,15 @@ fkv_status fkv_check_tied(const float* host_k_w, int32_t h_kv, int32_t d, int32_
     return ok();
 }
 
-size_t fkv_kivi_codes_bytes(const fkv_params* params)
+size_t fkv_kivi_codes_bytes(const fkv_params* params, int32_t is_value)
 {
     if (!params || params->batch < 0 || params->seqlen_k < 0 || params->num_kv_heads < 1 ||
         !supported_head_dim(params->head_dim))
         return 0;
-    return (size_t)params->batch * params->num_kv_heads * params->seqlen_k * (params->head_dim / 2);
+    const int64_t bh = (int64_t)params->batch * params->num_kv_heads;
+    // values: whole 32-token blocks of D channels x 16 bytes
+    return is_value ? (size_t)(bh * kivi_key_groups(params->seqlen_k) * params->head_dim * 16)
+                    : (size_t)(bh * params->seqlen_k * (params->head_dim / 2));
 }
 
 size_t fkv_kivi_meta_bytes(const fkv_params* params, int32_t is_value)
@@ -590,7 +593,7 @@ size_t fkv_kivi_meta_bytes(const fkv_params* params, int32_t is_value)
         !supported_head_dim(params->head_dim))
         return 0;
     const int64_t bh = (int64_t)params->batch * params->num_kv_heads;
-    const int64_t n = is_value ? bh * params->seqlen_k * kivi_value_groups(params->head_dim)
+    const int64_t n = is_value ? bh * kivi_key_groups(params->seqlen_k) * kivi_value_groups(params->head_dim) * 32
                                : bh * kivi_key_groups(params->seqlen_k) * params->head_dim;
     return (size_t)n * 2;
 }

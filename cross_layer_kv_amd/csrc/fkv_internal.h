@@ -59,12 +59,13 @@ constexpr int decode_waves(int dtype_f32, bool fused, int G)
     return G <= 2 ? 12 : (G == 4 ? 8 : 4);
 }
 
-// Waves per workgroup of the 4-bit decode kernel: its group coefficients
-// need more registers than the bf16 kernel, so fewer waves share a CU.
+// Waves per workgroup of the 4-bit decode kernel (a wave takes 32-token
+// blocks); its block loads and matrix-core operands allow 2 waves per SIMD.
 constexpr int kivi_waves(bool fused, int G)
 {
-    if (fused) return G <= 4 ? 8 : 4;
-    return G <= 2 ? 12 : (G == 4 ? 8 : 4);
+    (void)fused;
+    (void)G;
+    return 8;
 }
 
 // Prefill (S_q == S_k), bf16 only.

@@ -15,15 +15,29 @@
 // (max - min) / 15, and an element's code is rint((x - min) / scale)
 // clamped to 0..15 (0 for a zero scale), decided in float32 with correctly
 // rounded division so that any float32 implementation of the same steps
-// gives the same codes.  Two codes per byte, channel 2i in the low nibble.
+// gives the same codes.  Key codes are token-major, two per byte (channel 2i
+// in the low nibble).  Value codes are channel-major inside 32-token blocks:
+// the 16 bytes of (block, channel) are four words, word w holding tokens
+// 4w + (e%4) + 16(e/4) for e = 0..7 with element e in nibble e/2 (even e)
+// or 4 + e/2 (odd e); value scales and minima list a block's tokens in the
+// same order.  This is the order in which the matrix-core products below
+// consume them, so every operand is one aligned 4- or 16-byte load.
 //
-// Decode reads 4 code bytes (8 channels) per source per token and lane, in
-// place of 16 bf16 bytes, and rebuilds the fused key of a 32-token group's
-// channel as A1 q1 + An qn + C with A1 = a s1, An = a' sn, C = a m1 + a' mn
-// (computed once per group), values as b (m1 + s1 q1) + b' (mn + sn qn).
-// The work layout and the online softmax are those of the bf16 decode
-// kernel (fkv_decode.hip): one workgroup per (batch, KV head, split), a lane
-// owns 8 channels of a token, token groups sum scores with DPP.
+// Decode runs both products of a 32-token block on the matrix cores
+// (v_mfma_f32_16x16x32_f16), the query heads of the KV head padded to 16:
+//   scores^T [16 tokens x 16 heads] = codes [16 x 32 ch] * U [32 ch x 16 heads]
+// with U = scale*log2e * q * a * s (the key weight and the group's key
+// scale folded into the query) and a per-(head, group) constant
+// sum q * a * m added after; and
+//   O [16 heads x 16 ch] += P' [16 heads x 32 tokens] * codes [32 tok x 16 ch]
+// with P' = p * s (the token's value scale folded into the probability) and
+// the value minima accumulated separately as sum p * m per channel group.
+// The scores' accumulator layout (a lane holds one head and 4 tokens) is
+// exactly the P' operand layout, so no data moves between the products.
+// Codes enter the matrix cores as IEEE binary16 subnormals n * 2^-24 --
+// exact, and one mask (and shift) per pair of codes -- and the 2^24 is put
+// back in float32.  The fusion weights a, a' fold into U and b, b' are
+// applied once per output channel.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -37,7 +51,6 @@ namespace {
 using namespace dev;
 
 constexpr int kGroup = 32;       // elements per quantisation group
-constexpr int kWaveTokens = 16;  // tokens per wave per iteration
 constexpr float kLn2 = 0.69314718055994530942f;
 
 __device__ __forceinline__ float h2f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
@@ -103,298 +116,400 @@ __global__ __launch_bounds__(256) void kivi_quant_keys_kernel(const KiviQuantArg
     mn[mo + 1] = p1.mn16;
 }
 
-// Values: one thread per (batch*head, token, 32-channel group).
-__global__ __launch_bounds__(256) void kivi_quant_values_kernel(const KiviQuantArgs a)
+// Value positions inside a 32-token block: element e of word w is token
+// 4w + (e % 4) + 16 (e / 4), stored in nibble e / 2 (even e) or 4 + e / 2.
+__device__ __forceinline__ int vblock_pos(int tt)  // token in block -> 8w + e
 {
-    const int ng = (a.D + kGroup - 1) / kGroup, np = a.D / 2;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (int64_t)a.B * a.H * a.S * ng) return;
-    const int c = (int)(i % ng);
-    const int t = (int)((i / ng) % a.S);
-    const int bh = (int)(i / ((int64_t)ng * a.S));
-    const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
-    const int d0 = c * kGroup, n = min(kGroup, a.D - d0);  // 32, or 16 for the last group of D = 80
-    const uint16_t* src = static_cast<const uint16_t*>(a.src.data) + (int64_t)b * a.src.sb + (int64_t)t * a.src.ss +
-                          (int64_t)h * a.src.sh + d0;
-    uint32_t w[16];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        uint4 u = make_uint4(0u, 0u, 0u, 0u);
-        if (k * 8 < n) u = reinterpret_cast<const uint4*>(src)[k];
-        w[4 * k] = u.x;
-        w[4 * k + 1] = u.y;
-        w[4 * k + 2] = u.z;
-        w[4 * k + 3] = u.w;
-    }
-    float mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        if (2 * k < n) {
-            mn = fminf(mn, fminf(bf16_lo(w[k]), bf16_hi(w[k])));
-            mx = fmaxf(mx, fmaxf(bf16_lo(w[k]), bf16_hi(w[k])));
-        }
-    }
-    const QParams p = qparams(mn, mx);
-    uint8_t* codes = static_cast<uint8_t*>(a.codes) + ((int64_t)bh * a.S + t) * np + d0 / 2;
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-        if (2 * k < n) codes[k] = (uint8_t)(qcode(bf16_lo(w[k]), p) | (qcode(bf16_hi(w[k]), p) << 4));
-    const int64_t mo = ((int64_t)bh * a.S + t) * ng + c;
-    static_cast<uint16_t*>(a.scale)[mo] = p.sc16;
-    static_cast<uint16_t*>(a.minv)[mo] = p.mn16;
+    return tt < 16 ? 8 * (tt >> 2) + (tt & 3) : 8 * ((tt - 16) >> 2) + 4 + ((tt - 16) & 3);
 }
 
-// Codes of 8 channels (one 4-byte word) as floats 0..15, channel order.
-__device__ __forceinline__ void unpack8(uint32_t w, float* f)
+// Values: one workgroup per (batch*head, 32-token block).  The block is
+// staged in LDS as float32; one thread per (token, channel group) takes the
+// group's minimum, maximum and parameters, then one thread per channel packs
+// the block's 32 codes of that channel.
+__global__ __launch_bounds__(256) void kivi_quant_values_kernel(const KiviQuantArgs a)
 {
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    constexpr int kMaxD = 128;
+    __shared__ float xs[kGroup][kMaxD + 1];
+    __shared__ float pm[kGroup][4], pr[kGroup][4];
+    const int nb = (a.S + kGroup - 1) / kGroup, ng = (a.D + kGroup - 1) / kGroup;
+    const int bh = blockIdx.x / nb, j = blockIdx.x - (blockIdx.x / nb) * nb;
+    const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
+    const int tid = threadIdx.x;
+    const int cpr = a.D / 8;
+    for (int e = tid; e < kGroup * cpr; e += 256) {
+        const int tt = e / cpr, c = e - (e / cpr) * cpr;
+        const int t = j * kGroup + tt;
+        uint4 u = make_uint4(0u, 0u, 0u, 0u);
+        if (t < a.S)
+            u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.src.data) + (int64_t)b * a.src.sb +
+                                                (int64_t)t * a.src.ss + (int64_t)h * a.src.sh + c * 8);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[2 * i] = (float)((lo >> (8 * i)) & 0xFFu);
-        f[2 * i + 1] = (float)((hi >> (8 * i)) & 0xFFu);
+        for (int k = 0; k < 4; ++k) {
+            xs[tt][c * 8 + 2 * k] = bf16_lo(w[k]);
+            xs[tt][c * 8 + 2 * k + 1] = bf16_hi(w[k]);
+        }
+    }
+    __syncthreads();
+    if (tid < kGroup * ng) {
+        const int tt = tid / ng, g = tid - (tid / ng) * ng;
+        const int d0 = g * kGroup, n = min(kGroup, a.D - d0);
+        const bool live = j * kGroup + tt < a.S;
+        QParams p{};
+        if (live) {
+            float mn = INFINITY, mx = -INFINITY;
+            for (int c = 0; c < n; ++c) {
+                mn = fminf(mn, xs[tt][d0 + c]);
+                mx = fmaxf(mx, xs[tt][d0 + c]);
+            }
+            p = qparams(mn, mx);
+        }
+        pm[tt][g] = live ? p.m : 0.0f;
+        pr[tt][g] = live ? p.r : 0.0f;
+        const int64_t mo = (((int64_t)bh * nb + j) * ng + g) * kGroup + vblock_pos(tt);
+        static_cast<uint16_t*>(a.scale)[mo] = live ? p.sc16 : (uint16_t)0;
+        static_cast<uint16_t*>(a.minv)[mo] = live ? p.mn16 : (uint16_t)0;
+    }
+    __syncthreads();
+    for (int c = tid; c < a.D; c += 256) {
+        const int g = c / kGroup;
+        uint32_t wd[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            uint32_t acc = 0u;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int tt = 4 * w + (e & 3) + 16 * (e >> 2);
+                QParams p{};
+                p.m = pm[tt][g];
+                p.r = pr[tt][g];
+                const uint32_t q = j * kGroup + tt < a.S ? qcode(xs[tt][c], p) : 0u;
+                const int nib = (e & 1) ? 4 + (e >> 1) : (e >> 1);
+                acc |= q << (4 * nib);
+            }
+            wd[w] = acc;
+        }
+        *reinterpret_cast<uint4*>(static_cast<uint8_t*>(a.codes) + (((int64_t)bh * nb + j) * a.D + c) * 16) =
+            make_uint4(wd[0], wd[1], wd[2], wd[3]);
     }
 }
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+__device__ __forceinline__ f32x4 mma16(uint4 a, uint4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a), as_f16x8(b), c, 0, 0, 0);
+}
+
+// Eight 4-bit codes of one word -> eight binary16 subnormals n * 2^-24, the
+// pair k holding nibbles k and k + 4.
+__device__ __forceinline__ uint4 codes_f16(uint32_t w)
+{
+    return make_uint4(w & 0x000F000Fu, (w >> 4) & 0x000F000Fu, (w >> 8) & 0x000F000Fu, (w >> 12) & 0x000F000Fu);
+}
+
+// fp16 pairs (x_k, x_{k+4}) of eight consecutive fp16 values held as four
+// words (x0 x1)(x2 x3)(x4 x5)(x6 x7): the channel order of codes_f16.
+__device__ __forceinline__ uint4 pair_k4(uint4 u)
+{
+    return make_uint4(__builtin_amdgcn_perm(u.z, u.x, 0x05040100u), __builtin_amdgcn_perm(u.z, u.x, 0x07060302u),
+                      __builtin_amdgcn_perm(u.w, u.y, 0x05040100u), __builtin_amdgcn_perm(u.w, u.y, 0x07060302u));
+}
+
+__device__ __forceinline__ uint32_t pk_mul(uint32_t x, uint32_t y)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, x) * __builtin_bit_cast(f16x2, y));
+}
+__device__ __forceinline__ uint4 pk_mul4(uint4 x, uint4 y)
+{
+    return make_uint4(pk_mul(x.x, y.x), pk_mul(x.y, y.y), pk_mul(x.z, y.z), pk_mul(x.w, y.w));
+}
+__device__ __forceinline__ float dot8(uint4 x, uint4 y, float acc)
+{
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x.x), __builtin_bit_cast(f16x2, y.x), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x.y), __builtin_bit_cast(f16x2, y.y), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x.z), __builtin_bit_cast(f16x2, y.z), acc, false);
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x.w), __builtin_bit_cast(f16x2, y.w), acc, false);
+}
+__device__ __forceinline__ float sum4(float v)  // over the 4 lanes l, l^16, l^32, l^48
+{
+    v += __shfl_xor(v, 16);
+    return v + __shfl_xor(v, 32);
+}
+__device__ __forceinline__ float max4(float v)
+{
+    v = fmaxf(v, __shfl_xor(v, 16));
+    return fmaxf(v, __shfl_xor(v, 32));
+}
+
+constexpr float kTwo24 = 16777216.0f;
 
 template <int D, bool FUSED, int G, int NW>
 __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs a)
 {
     constexpr int NT = 64 * NW;
-    constexpr int NP = D / 8;              // 8-channel pieces per row
-    constexpr int LPT = NP <= 8 ? 8 : 16;  // lanes per token group
-    constexpr int TPW = 64 / LPT;          // tokens per wave step
-    constexpr int U = kWaveTokens / TPW;   // steps per iteration
-    constexpr int NGV = (D + kGroup - 1) / kGroup;
+    constexpr int KS = (D + 31) / 32;  // 32-channel k-steps of the score product (= value groups)
+    constexpr int NVB = D / 16;        // 16-channel column blocks of the output
+    constexpr int NS = FUSED ? 2 : 1;  // key (and value) sources
+    static_assert(G <= 16, "heads of a KV head fit the 16 rows");
 
     __shared__ float s_acc[NW][G][D];
     __shared__ float s_ml[NW][G][2];
+    __shared__ float s_M[NW][NS][G][KS];
 
     const int split = blockIdx.x;
     const int bg = blockIdx.y;  // b * Hkv + g
     const int b = bg / a.Hkv, g = bg - (bg / a.Hkv) * a.Hkv;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int grp = lane / LPT, pc = lane % LPT;
-    const bool active = pc < NP;
-    const int c0 = active ? pc * 8 : 0;
-    const int vgrp = c0 / kGroup;  // this lane's value channel group
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, hb = lane >> 4;
+    const bool hv = l16 < G;  // this lane's head column holds a real head
 
     int len = a.seqlens ? a.seqlens[b] : a.Sk;
     len = len < 0 ? 0 : (len > a.Sk ? a.Sk : len);
     const int t_begin = split * a.chunk;
     const int t_end = min(len, t_begin + a.chunk);
     const int ngk = (a.Sk + kGroup - 1) / kGroup;
+    const int64_t bh = bg;
 
-    // Query of the G heads, pre-scaled into the log2 domain
-    float qs[G][8];
+    // q * a * scale * log2e of this lane's head, as fp16 pairs in the
+    // channel order of codes_f16: k-step ks, channels 32 ks + 8 hb + {k, k+4}
+    uint4 qa[NS][KS];
     {
-        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + (int64_t)g * G) * D + c0;
+        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + (int64_t)g * G + (hv ? l16 : 0)) * D;
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
+        for (int ks = 0; ks < KS; ++ks) {
+            const int c0 = ks * 32 + hb * 8;
+            const bool live = hv && c0 < D;
             uint4 u = make_uint4(0u, 0u, 0u, 0u);
-            if (active) u = *reinterpret_cast<const uint4*>(qp + (int64_t)hh * D);
+            if (live) u = *reinterpret_cast<const uint4*>(qp + c0);
             const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+            float qf[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                qf[2 * k] = bf16_lo(w[k]) * a.scale_log2;
+                qf[2 * k + 1] = bf16_hi(w[k]) * a.scale_log2;
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                float wt[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) wt[k] = 1.0f;
+                if constexpr (FUSED) {
+                    const float* wp = (s == 0 ? a.kw1 : a.kwn) + (int64_t)g * D + c0;
+                    if (live) {
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) wt[k] = wp[k];
+                    }
+                }
+                qa[s][ks] = make_uint4(pack2(qf[0] * wt[0], qf[4] * wt[4]), pack2(qf[1] * wt[1], qf[5] * wt[5]),
+                                       pack2(qf[2] * wt[2], qf[6] * wt[6]), pack2(qf[3] * wt[3], qf[7] * wt[7]));
+                if (!live) qa[s][ks] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+    }
+
+    const Q4View* ksrc[2] = {&a.qk1, &a.qkn};
+    const Q4View* vsrc[2] = {&a.qv1, &a.qvn};
+    const int nbv = (a.Sk + kGroup - 1) / kGroup;
+
+    // Per-block metadata: NC = NS * KS * 2 chunks of 16 bytes per lane
+    // quarter hb (scale or minimum, of one source and one 32-channel slice),
+    // each fetched by one lane (column l16 = chunk) and parked in this
+    // wave's LDS area, where every lane reads the chunks it needs.
+    constexpr int NC = NS * KS * 2;
+    static_assert(NC <= 16, "one metadata chunk per lane column");
+    __shared__ uint4 s_meta[NW][2][NC][4];  // [wave][key, value][chunk][hb]
+
+    // The loads of one 32-token block: key codes (2 tiles x KS k-steps),
+    // value codes (NVB column blocks) and one key and one value metadata
+    // chunk.  The next block's are in flight while this one is computed.
+    struct Blk {
+        uint32_t kc[NS][2][KS];
+        uint32_t vc[NS][NVB];
+        uint4 km, vm;
+    };
+    auto load_block = [&](int t0, Blk& x) {
+        const int j = t0 / kGroup;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const uint8_t* kcp = static_cast<const uint8_t*>(ksrc[s]->codes) + bh * a.Sk * (D / 2);
+            const uint8_t* vcp = static_cast<const uint8_t*>(vsrc[s]->codes) + (bh * nbv + j) * D * 16;
+#pragma unroll
+            for (int tl = 0; tl < 2; ++tl) {
+                const int t = t0 + tl * 16 + l16;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    x.kc[s][tl][ks] = (ks * 32 + hb * 8 < D && t < t_end)
+                                          ? *reinterpret_cast<const uint32_t*>(kcp + (int64_t)t * (D / 2) + ks * 16 + hb * 4)
+                                          : 0u;
+            }
+#pragma unroll
+            for (int n = 0; n < NVB; ++n)
+                x.vc[s][n] = *reinterpret_cast<const uint32_t*>(vcp + (n * 16 + l16) * 16 + hb * 4);
+        }
+        x.km = make_uint4(0u, 0u, 0u, 0u);
+        x.vm = x.km;
+        if (l16 < NC) {
+            const int s = l16 / (2 * KS), ks = (l16 >> 1) - s * KS, sm = l16 & 1;
+            const Q4View& kv = *ksrc[s];
+            const Q4View& vv = *vsrc[s];
+            if (ks * 32 + hb * 8 < D)
+                x.km = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(sm ? kv.minv : kv.scale) +
+                                                       (bh * ngk + j) * D + ks * 32 + hb * 8);
+            x.vm = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(sm ? vv.minv : vv.scale) +
+                                                   ((bh * nbv + j) * KS + ks) * kGroup + hb * 8);
+        }
+    };
+
+    f32x4 oacc[NS][NVB];
+    float Mp[NS][KS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+        for (int n = 0; n < NVB; ++n) oacc[s][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < KS; ++k) Mp[s][k] = 0.0f;
+    }
+    float m_run = -INFINITY, l_part = 0.0f;
+
+    Blk cur;
+    int t0 = t_begin + wave * kGroup;
+    if (t0 < t_end) load_block(t0, cur);
+    for (; t0 < t_end; t0 += NW * kGroup) {
+        // park this block's metadata (a wave-private area: in-order LDS
+        // access within the wave orders it against last block's reads)
+        if (l16 < NC) {
+            s_meta[wave][0][l16][hb] = cur.km;
+            s_meta[wave][1][l16][hb] = cur.vm;
+        }
+        Blk nxt;
+        const int t1 = t0 + NW * kGroup;
+        if (t1 < t_end) load_block(t1, nxt);
+
+        // ---- scores: two 16-token tiles, heads on the columns ----
+        f32x4 sc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+        float cst = 0.0f;  // sum over this lane's channels of q a m (log2 units)
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const uint4 ksc = s_meta[wave][0][(s * KS + ks) * 2 + 0][hb];
+                const uint4 kmn = s_meta[wave][0][(s * KS + ks) * 2 + 1][hb];
+                const uint4 u = pk_mul4(qa[s][ks], pair_k4(ksc));
+                cst = dot8(qa[s][ks], pair_k4(kmn), cst);
+#pragma unroll
+                for (int tl = 0; tl < 2; ++tl) sc[tl] = mma16(codes_f16(cur.kc[s][tl][ks]), u, sc[tl]);
+            }
+        cst = sum4(cst);
+        // lane: head l16; entries: tokens t0 + 16 tl + 4 hb + i
+        float sv[8];
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int tl = 0; tl < 2; ++tl)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                qs[hh][2 * i] = bf16_lo(w[i]) * a.scale_log2;
-                qs[hh][2 * i + 1] = bf16_hi(w[i]) * a.scale_log2;
+                const int t = t0 + tl * 16 + hb * 4 + i;
+                const float x = (hv && t < t_end) ? sc[tl][i] * kTwo24 + cst : -INFINITY;
+                sv[tl * 4 + i] = x;
+                bmax = fmaxf(bmax, x);
             }
-        }
-    }
-    float wk1[8], wkn[8], wv1[8], wvn[8];
-    if constexpr (FUSED) {
-        const int64_t wo = (int64_t)g * D + c0;
+        bmax = max4(bmax);
+        const float m_new = fmaxf(m_run, bmax);
+        if (__any(m_new > m_run)) {
+            const float corr = rel_weight(m_run, m_new);
+            l_part *= corr;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            wk1[c] = active ? a.kw1[wo + c] : 0.0f;
-            wkn[c] = active ? a.kwn[wo + c] : 0.0f;
-            wv1[c] = active ? a.vw1[wo + c] : 0.0f;
-            wvn[c] = active ? a.vwn[wo + c] : 0.0f;
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int k = 0; k < KS; ++k) Mp[s][k] *= corr;
+            // output rows are heads 4 hb + i: fetch those heads' factors
+            // (lane h holds head h's factor: l16 = h, hb = 0)
+            float cr[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) cr[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(corr), h));
+            float rc[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float r = 1.0f;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    if (q4 * 4 + i < G && hb == q4) r = cr[q4 * 4 + i];
+                rc[i] = r;
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int n = 0; n < NVB; ++n)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) oacc[s][n][i] *= rc[i];
+            m_run = m_new;
         }
-    }
+        const float msub = m_run == -INFINITY ? 0.0f : m_run;
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pv[e] = sv[e] == -INFINITY ? 0.0f : exp2_fast(sv[e] - msub);
+            l_part += pv[e];
+        }
+        const uint4 p16 = make_uint4(pack2(pv[0], pv[1]), pack2(pv[2], pv[3]), pack2(pv[4], pv[5]), pack2(pv[6], pv[7]));
 
-    // per-source pointers of this (batch, KV head): codes of channel c0 at
-    // token 0, key group parameters of channel c0 at group 0, value group
-    // parameters of group vgrp at token 0
-    const int64_t bh = bg;
-    auto codes_of = [&](const Q4View& v) { return static_cast<const uint8_t*>(v.codes) + bh * a.Sk * (D / 2) + c0 / 2; };
-    auto kmeta = [&](const void* p) { return static_cast<const uint16_t*>(p) + bh * ngk * D + c0; };
-    auto vmeta = [&](const void* p) { return static_cast<const uint16_t*>(p) + bh * a.Sk * NGV + vgrp; };
-    const uint8_t* ck1 = codes_of(a.qk1);
-    const uint8_t* cv1 = codes_of(a.qv1);
-    const uint16_t* ks1 = kmeta(a.qk1.scale);
-    const uint16_t* km1 = kmeta(a.qk1.minv);
-    const uint16_t* vs1 = vmeta(a.qv1.scale);
-    const uint16_t* vm1 = vmeta(a.qv1.minv);
-    const uint8_t* ckn = ck1;
-    const uint8_t* cvn = cv1;
-    const uint16_t *ksn = ks1, *kmn = km1, *vsn = vs1, *vmn = vm1;
-    if constexpr (FUSED) {
-        ckn = codes_of(a.qkn);
-        cvn = codes_of(a.qvn);
-        ksn = kmeta(a.qkn.scale);
-        kmn = kmeta(a.qkn.minv);
-        vsn = vmeta(a.qvn.scale);
-        vmn = vmeta(a.qvn.minv);
-    }
-
-    float m[G], l[G], acc[G][8];
+        // ---- O += P' * codes, P' = p * (token's value scale), per group ----
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        m[hh] = -INFINITY;
-        l[hh] = 0.0f;
+        for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[hh][c] = 0.0f;
-    }
-
-    for (int t0 = t_begin + wave * kWaveTokens; t0 < t_end; t0 += NW * kWaveTokens) {
-        // key group parameters: the 16 tokens of a slice share one group
-        // (splits start at multiples of 64 and slices at multiples of 16)
-        float A1[8], An[8], C[8];
-        {
-            const int gi = t0 / kGroup;
-            uint4 s1 = make_uint4(0u, 0u, 0u, 0u), m1 = s1, sn = s1, mn = s1;
-            if (active) {
-                s1 = *reinterpret_cast<const uint4*>(ks1 + (int64_t)gi * D);
-                m1 = *reinterpret_cast<const uint4*>(km1 + (int64_t)gi * D);
-                if constexpr (FUSED) {
-                    sn = *reinterpret_cast<const uint4*>(ksn + (int64_t)gi * D);
-                    mn = *reinterpret_cast<const uint4*>(kmn + (int64_t)gi * D);
-                }
+            for (int k = 0; k < KS; ++k) {
+                const uint4 vsc = s_meta[wave][1][(s * KS + k) * 2 + 0][hb];
+                const uint4 vmn = s_meta[wave][1][(s * KS + k) * 2 + 1][hb];
+                const uint4 pa = pk_mul4(p16, vsc);
+                Mp[s][k] = dot8(p16, vmn, Mp[s][k]);
+#pragma unroll
+                for (int n = 2 * k; n < 2 * k + 2 && n < NVB; ++n)
+                    oacc[s][n] = mma16(pa, codes_f16(cur.vc[s][n]), oacc[s][n]);
             }
-            const uint32_t s1w[4] = {s1.x, s1.y, s1.z, s1.w}, m1w[4] = {m1.x, m1.y, m1.z, m1.w};
-            const uint32_t snw[4] = {sn.x, sn.y, sn.z, sn.w}, mnw[4] = {mn.x, mn.y, mn.z, mn.w};
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const float sc1 = h2f((uint16_t)(s1w[c / 2] >> (16 * (c & 1))));
-                const float mi1 = h2f((uint16_t)(m1w[c / 2] >> (16 * (c & 1))));
-                if constexpr (FUSED) {
-                    const float scn = h2f((uint16_t)(snw[c / 2] >> (16 * (c & 1))));
-                    const float min_ = h2f((uint16_t)(mnw[c / 2] >> (16 * (c & 1))));
-                    A1[c] = wk1[c] * sc1;
-                    An[c] = wkn[c] * scn;
-                    C[c] = wk1[c] * mi1 + wkn[c] * min_;
-                } else {
-                    A1[c] = sc1;
-                    An[c] = 0.0f;
-                    C[c] = mi1;
-                }
-            }
-        }
-
-        uint32_t rk1[U], rkn[U], rv1[U], rvn[U];
-        float vs1u[U], vm1u[U], vsnu[U], vmnu[U];
-        bool ok[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int t = t0 + u * TPW + grp;
-            ok[u] = t < t_end;
-            const bool pr = active && ok[u];
-            rk1[u] = pr ? *reinterpret_cast<const uint32_t*>(ck1 + (int64_t)t * (D / 2)) : 0u;
-            rv1[u] = pr ? *reinterpret_cast<const uint32_t*>(cv1 + (int64_t)t * (D / 2)) : 0u;
-            vs1u[u] = pr ? h2f(vs1[(int64_t)t * NGV]) : 0.0f;
-            vm1u[u] = pr ? h2f(vm1[(int64_t)t * NGV]) : 0.0f;
-            if constexpr (FUSED) {
-                rkn[u] = pr ? *reinterpret_cast<const uint32_t*>(ckn + (int64_t)t * (D / 2)) : 0u;
-                rvn[u] = pr ? *reinterpret_cast<const uint32_t*>(cvn + (int64_t)t * (D / 2)) : 0u;
-                vsnu[u] = pr ? h2f(vsn[(int64_t)t * NGV]) : 0.0f;
-                vmnu[u] = pr ? h2f(vmn[(int64_t)t * NGV]) : 0.0f;
-            }
-        }
-
-        // scores of the U tokens of this lane's group, log2 domain
-        float s[U][G];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float q1[8], kf[8];
-            unpack8(rk1[u], q1);
-            if constexpr (FUSED) {
-                float qn[8];
-                unpack8(rkn[u], qn);
-#pragma unroll
-                for (int c = 0; c < 8; ++c) kf[c] = A1[c] * q1[c] + (An[c] * qn[c] + C[c]);
-            } else {
-#pragma unroll
-                for (int c = 0; c < 8; ++c) kf[c] = A1[c] * q1[c] + C[c];
-            }
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
-                float d = 0.0f;
-#pragma unroll
-                for (int c = 0; c < 8; ++c) d += qs[hh][c] * kf[c];
-                d = token_group_sum<LPT>(d);
-                s[u][hh] = ok[u] ? d : -INFINITY;
-            }
-        }
-
-        // online softmax: raise the running max if needed, then accumulate
-        float msub[G];
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            float mx = s[0][hh];
-#pragma unroll
-            for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u][hh]);
-            if (mx > m[hh]) {
-                const float corr = rel_weight(m[hh], mx);
-                l[hh] *= corr;
-#pragma unroll
-                for (int c = 0; c < 8; ++c) acc[hh][c] *= corr;
-                m[hh] = mx;
-            }
-            msub[hh] = m[hh] == -INFINITY ? 0.0f : m[hh];
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float vf[8];
-            unpack8(rv1[u], vf);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) vf[c] = vm1u[u] + vs1u[u] * vf[c];
-            if constexpr (FUSED) {
-                float vn[8];
-                unpack8(rvn[u], vn);
-#pragma unroll
-                for (int c = 0; c < 8; ++c) vf[c] = wv1[c] * vf[c] + wvn[c] * (vmnu[u] + vsnu[u] * vn[c]);
-            }
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
-                const float p = exp2_fast(s[u][hh] - msub[hh]);
-                l[hh] += p;
-#pragma unroll
-                for (int c = 0; c < 8; ++c) acc[hh][c] += p * vf[c];
-            }
-        }
+        cur = nxt;
     }
 
-    // merge the token groups of the wave (lanes with equal pc)
+    // ---- wave results: (m, l) and the minimum terms per head ----
+    const float l_tot = sum4(l_part);
 #pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) {
+    for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            const float mo = __shfl_xor(m[hh], off);
-            const float lo = __shfl_xor(l[hh], off);
-            const float M = fmaxf(m[hh], mo);
-            const float fa = rel_weight(m[hh], M), fb = rel_weight(mo, M);
-            l[hh] = l[hh] * fa + lo * fb;
+        for (int k = 0; k < KS; ++k) Mp[s][k] = sum4(Mp[s][k]);
+    if (hb == 0 && hv) {
+        s_ml[wave][l16][0] = m_run;
+        s_ml[wave][l16][1] = l_tot;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) acc[hh][c] = acc[hh][c] * fa + __shfl_xor(acc[hh][c], off) * fb;
-            m[hh] = M;
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int k = 0; k < KS; ++k) s_M[wave][s][l16][k] = Mp[s][k];
+    }
+    __syncthreads();
+    // lane: output column c = 16 n + l16 of heads 4 hb + i
+#pragma unroll
+    for (int n = 0; n < NVB; ++n) {
+        const int c = n * 16 + l16;
+        const int k = c / kGroup;
+        float w1 = 1.0f, wn = 0.0f;
+        if constexpr (FUSED) {
+            w1 = a.vw1[(int64_t)g * D + c];
+            wn = a.vwn[(int64_t)g * D + c];
         }
-    }
-    if (grp == 0 && active) {
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) s_acc[wave][hh][c0 + c] = acc[hh][c];
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            s_ml[wave][hh][0] = m[hh];
-            s_ml[wave][hh][1] = l[hh];
+        for (int i = 0; i < 4; ++i) {
+            const int h = hb * 4 + i;
+            if (h < G) {
+                float o = w1 * (oacc[0][n][i] * kTwo24 + s_M[wave][0][h][k]);
+                if constexpr (FUSED) o += wn * (oacc[NS - 1][n][i] * kTwo24 + s_M[wave][NS - 1][h][k]);
+                s_acc[wave][h][c] = o;
+            }
         }
     }
     __syncthreads();
 
-    // merge the waves; write O/LSE (one split) or this split's partial row
+    // ---- merge the waves; write O/LSE (one split) or this split's partial row ----
     const bool final_out = a.n_splits == 1;
     const int64_t slot = (int64_t)bg * a.n_splits + split;
     for (int e = tid; e < G * D; e += NT) {
@@ -465,13 +580,12 @@ int launch_kivi_quantize(const KiviQuantArgs& a, void* stream)
 {
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (a.B == 0 || a.S == 0) return 0;
-    int64_t n;
+    int64_t blocks;
     if (a.is_value) {
-        n = (int64_t)a.B * a.H * a.S * ((a.D + kGroup - 1) / kGroup);
+        blocks = (int64_t)a.B * a.H * ((a.S + kGroup - 1) / kGroup);  // one workgroup per 32-token block
     } else {
-        n = (int64_t)a.B * a.H * ((a.S + kGroup - 1) / kGroup) * (a.D / 2);
+        blocks = ((int64_t)a.B * a.H * ((a.S + kGroup - 1) / kGroup) * (a.D / 2) + 255) / 256;
     }
-    const int64_t blocks = (n + 255) / 256;
     if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
     if (a.is_value) hipLaunchKernelGGL(kivi_quant_values_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
     else hipLaunchKernelGGL(kivi_quant_keys_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define FKV_ABI_VERSION 3
+#define FKV_ABI_VERSION 4
 
 typedef enum {
     FKV_SUCCESS = 0,
@@ -223,10 +223,20 @@ fkv_status fkv_check_tied(const float* host_k_w, int32_t h_kv, int32_t d,
  *   a group keeps its minimum and scale = (max - min) / 15 as IEEE binary16;
  *   code = rint((x - min) * (1 / scale)) clamped to 0..15 (0 if scale == 0),
  *   decided in float32 with the rounded min and scale; x ~ min + scale*code.
- * Arrays of one quantised source, contiguous, S = params->seqlen_k:
- *   codes  uint8    [B, H_kv, S, D/2]  channel 2i in the low nibble, 2i+1 high
- *   scale  binary16 keys [B, H_kv, ceil(S/32), D]; values [B, H_kv, S, ceil(D/32)]
- *   minv   binary16 same shape as scale
+ * Arrays of one quantised source, contiguous, S = params->seqlen_k,
+ * NB = ceil(S/32):
+ *   keys    codes uint8    [B, H_kv, S, D/2]   channel 2i low nibble, 2i+1 high
+ *           scale binary16 [B, H_kv, NB, D]     (minv: same shape)
+ *   values  codes uint8    [B, H_kv, NB, D, 16]
+ *           scale binary16 [B, H_kv, NB, ceil(D/32), 32]  (minv: same shape)
+ * Value codes are channel-major inside each 32-token block: the 16 bytes of
+ * (block, channel) are four 4-byte words; word w holds the tokens
+ * 4w + (e%4) + 16(e/4) of the block for e = 0..7, element e in nibble e/2
+ * (even e) or 4 + e/2 (odd e), nibble k meaning bits 4k..4k+3.  A value
+ * scale/minv row lists the block's tokens in the same order (position 8w +
+ * e).  Tokens of the last block past S have code, scale and minv 0.  (This
+ * is the order in which the decode kernel's matrix-core products consume the
+ * codes, so that every operand is one aligned load.)
  * All three device pointers 16-byte aligned; the caller owns them.
  */
 typedef struct {
@@ -235,9 +245,9 @@ typedef struct {
     const void* minv;
 } fkv_q4_cache;
 
-/* Bytes of codes of one quantised source, and of its scale (or minv) array
- * (is_value 0: keys, 1: values).  0 for invalid params. */
-size_t fkv_kivi_codes_bytes(const fkv_params* params);
+/* Bytes of the codes of one quantised source, and of its scale (or minv)
+ * array (is_value 0: keys, 1: values).  0 for invalid params. */
+size_t fkv_kivi_codes_bytes(const fkv_params* params, int32_t is_value);
 size_t fkv_kivi_meta_bytes(const fkv_params* params, int32_t is_value);
 
 /*
@@ -251,9 +261,11 @@ fkv_status fkv_kivi_quantize(const fkv_params* params, fkv_cache src,
                              int32_t is_value, fkv_q4_cache dst, void* stream);
 
 /*
- * fkv_kivi_decode -- fkv_decode over 4-bit sources: each element is
- * dequantised in float32 registers (min + scale * code) and then fused as in
- * fkv_decode.  k1/kn are key caches, v1/vn value caches in the format above.
+ * fkv_kivi_decode -- fkv_decode over 4-bit sources, fused after
+ * dequantisation (min + scale * code).  Both products run on the matrix
+ * cores with the codes as exact binary16 values; the key scale and key
+ * weight fold into the query (rounded to binary16), the value scale into
+ * the probabilities (binary16), all accumulation float32.  k1/kn are key caches, v1/vn value caches in the format above.
  * bfloat16 queries and outputs, G in {1, 2, 4, 8}; other arguments,
  * workspace (fkv_decode_workspace_size covers these calls) and errors as
  * fkv_decode.

@@ -26,10 +26,19 @@ Dequantisation mn16 + sc16 * q is exact in float64, and the attention of a
 layer over quantised sources is the plain oracle attention over the
 dequantised caches (fusion after dequantisation, as the pages compose them).
 
-Array layouts (those of the library's quantised caches):
-  codes      uint8   [B, H, S, D/2]
-  key meta   float16 [B, H, ceil(S/32), D]   (scale and minimum, one each)
-  value meta float16 [B, H, S, ceil(D/32)]
+Array layouts (those of the library's quantised caches; a storage choice,
+the pages fix none):
+  key codes    uint8   [B, H, S, D/2]            channel 2i low nibble, 2i+1 high
+  key meta     float16 [B, H, ceil(S/32), D]     (scale and minimum, one each)
+  value codes  uint8   [B, H, NB, D, 16]         NB = ceil(S/32) blocks of 32 tokens
+  value meta   float16 [B, H, NB, ceil(D/32), 32]
+Value codes are channel-major inside each 32-token block: the 16 bytes of
+(block, channel) are four 4-byte words w = 0..3, and word w holds the eight
+tokens  4w + (e % 4) + 16 (e // 4),  e = 0..7,  element e in nibble e // 2
+(bits 4 (e//2)) when e is even and in nibble 4 + e // 2 when e is odd.  The
+value scale and minimum of (block, channel group) list the block's 32 tokens
+in that same order, position 8w + e.  Tokens past S in the last block have
+code 0, scale 0 and minimum 0.
 """
 from __future__ import annotations
 
@@ -98,9 +107,19 @@ def quantise_keys(k):
     return _pack(q), sc, mn
 
 
+def block_token(w, e):
+    """Token (within its 32-token block) of element e of word w."""
+    return 4 * w + (e % 4) + 16 * (e // 4)
+
+
+def _nibble(e):
+    """Nibble position of element e inside its 4-byte word."""
+    return e // 2 if e % 2 == 0 else 4 + e // 2
+
+
 def quantise_values(v):
     """v: [B, S, H, D] -> (codes, scale, minimum) with per-token groups of 32
-    channels."""
+    channels, in the block layout described above."""
     x = np.ascontiguousarray(np.transpose(_as_f32(v), (0, 2, 1, 3)))  # [B, H, S, D]
     B, H, S, D = x.shape
     ng = (D + GROUP - 1) // GROUP
@@ -110,7 +129,50 @@ def quantise_values(v):
     for c in range(ng):
         d0, d1 = c * GROUP, min(D, (c + 1) * GROUP)
         q[..., d0:d1], sc[..., c], mn[..., c] = _quantise_group(x[..., d0:d1], axis=3)
-    return _pack(q), sc, mn
+    return _to_blocks(q, sc, mn)
+
+
+def _to_blocks(q, sc, mn):
+    """Token-major codes [B, H, S, D] (0..15) and per-token metadata
+    [B, H, S, ng] -> the block layout."""
+    B, H, S, D = q.shape
+    ng = sc.shape[-1]
+    nb = (S + GROUP - 1) // GROUP
+    codes = np.zeros((B, H, nb, D, 16), dtype=np.uint8)
+    bsc = np.zeros((B, H, nb, ng, GROUP), dtype=np.float16)
+    bmn = np.zeros((B, H, nb, ng, GROUP), dtype=np.float16)
+    for j in range(nb):
+        for w in range(4):
+            for e in range(8):
+                t = j * GROUP + block_token(w, e)
+                if t >= S:
+                    continue
+                p = _nibble(e)
+                byte = 4 * w + p // 2
+                shift = 4 * (p % 2)
+                codes[:, :, j, :, byte] |= (q[:, :, t, :] << shift).astype(np.uint8)
+                bsc[:, :, j, :, 8 * w + e] = sc[:, :, t, :]
+                bmn[:, :, j, :, 8 * w + e] = mn[:, :, t, :]
+    return codes, bsc, bmn
+
+
+def value_tokens(codes, sc, mn, S):
+    """Block layout -> token-major codes [B, H, S, D] (0..15) and per-token
+    scale and minimum [B, H, S, ng]."""
+    B, H, nb, D, _ = codes.shape
+    ng = sc.shape[3]
+    q = np.zeros((B, H, nb * GROUP, D), dtype=np.uint8)
+    s = np.zeros((B, H, nb * GROUP, ng), dtype=np.float16)
+    m = np.zeros((B, H, nb * GROUP, ng), dtype=np.float16)
+    for j in range(nb):
+        for w in range(4):
+            for e in range(8):
+                t = j * GROUP + block_token(w, e)
+                p = _nibble(e)
+                q[:, :, t, :] = (codes[:, :, j, :, 4 * w + p // 2] >> (4 * (p % 2))) & 0x0F
+                s[:, :, t, :] = sc[:, :, j, :, 8 * w + e]
+                m[:, :, t, :] = mn[:, :, j, :, 8 * w + e]
+    return q[:, :, :S], s[:, :, :S], m[:, :, :S]
 
 
 def dequantise_keys(codes, sc, mn):
@@ -122,11 +184,13 @@ def dequantise_keys(codes, sc, mn):
     return np.transpose(x, (0, 2, 1, 3))
 
 
-def dequantise_values(codes, sc, mn):
-    q = _unpack(codes).astype(np.float64)  # [B, H, S, D]
+def dequantise_values(codes, sc, mn, S):
+    """Block layout of an S-token value cache -> float64 [B, S, H, D]."""
+    q, s, m = value_tokens(codes, sc, mn, S)
+    q = q.astype(np.float64)
     D = q.shape[3]
     ch_group = np.arange(D) // GROUP
-    x = mn.astype(np.float64)[..., ch_group] + sc.astype(np.float64)[..., ch_group] * q
+    x = m.astype(np.float64)[..., ch_group] + s.astype(np.float64)[..., ch_group] * q
     return np.transpose(x, (0, 2, 1, 3))
 
 
@@ -140,10 +204,11 @@ def attend(q, k1, v1, kn=None, vn=None, **kw):
     ``oracle.attend`` (weights, causal, scale, seqlens_k, rows)."""
     qd = _q_f64(q)
     K1 = dequantise_keys(*k1)
-    V1 = dequantise_values(*v1)
+    S = K1.shape[1]
+    V1 = dequantise_values(*v1, S)
     if kn is None:
         return oracle.attend(qd, K1, V1, **kw)
-    return oracle.attend(qd, K1, V1, dequantise_keys(*kn), dequantise_values(*vn), **kw)
+    return oracle.attend(qd, K1, V1, dequantise_keys(*kn), dequantise_values(*vn, S), **kw)
 
 
 def payload_bytes(L, S, Hkv, D, method, bits):
@@ -154,7 +219,8 @@ def payload_bytes(L, S, Hkv, D, method, bits):
 
 def metadata_bytes(S, Hkv, D, B=1):
     """fp16 scale and minimum of one quantised source: keys and values have
-    the same count when S and D are multiples of 32."""
+    the same count when S and D are multiples of 32 (value metadata is
+    stored per 32-token block, so a partial last block counts whole)."""
     keys = B * Hkv * ((S + GROUP - 1) // GROUP) * D * 2 * 2
-    values = B * Hkv * S * ((D + GROUP - 1) // GROUP) * 2 * 2
+    values = B * Hkv * ((S + GROUP - 1) // GROUP) * GROUP * ((D + GROUP - 1) // GROUP) * 2 * 2
     return keys, values

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib, B):
     assert set(names) == set(B.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.fkv_abi_version() == 3
+    assert lib.fkv_abi_version() == 4
     for s in range(5):
         assert lib.fkv_status_string(s)
     assert lib.fkv_status_string(99) == b"unknown status"
@@ -106,7 +106,7 @@ def test_decode_validation_codes(lib, B):
     p = _params(B, sk=8192)   # 4 (batch, kv head) units: the key axis is split, a workspace is needed
     need = lib.fkv_decode_workspace_size(ctypes.byref(p))
     assert need > 0
-    assert _decode(lib, B, p, ws_bytes=256) == WS
+    assert _decode(lib, B, p, ws_bytes=need - 1) == WS
     assert _decode(lib, B, p, ws=0) == WS
     assert _decode(lib, B, p, ws=FAKE + 16) == WS                  # not 256-byte aligned
     # an empty batch is a valid no-op: nothing is launched
@@ -145,13 +145,16 @@ def test_kivi_validation_codes(lib, B):
     assert _kivi_decode(lib, B, _params(B, sq=2), lite=True) == INV
     assert _kivi_decode(lib, B, _params(B, batch=0)) == B.FKV_SUCCESS
     assert _kivi_decode(lib, B, _params(B, batch=0), lite=True) == B.FKV_SUCCESS
-    # the workspace size covers the 4-bit plans, whose eight-wave fused
-    # workgroups split this shape the finest: 4 units x 64 splits of 128 tokens
+    # the workspace size is the largest of the decode plans; here the bf16
+    # four-source plan (12-wave workgroups, 192-token steps: 43 splits of
+    # 192 tokens) needs more than the 4-bit plan (8 waves x 32-token blocks:
+    # 32 splits of 256 tokens), which is checked exactly
     p = _params(B, sk=8192)
     need = lib.fkv_decode_workspace_size(ctypes.byref(p))
-    units, ns, G, D = 4, 64, 2, 64
-    assert need == math.ceil(units * ns * G * 2 * 4 / 256) * 256 + units * ns * G * D * 4
-    assert _kivi_decode(lib, B, p, ws_bytes=need - 1) == WS
+    ws = lambda units, ns, G, D: math.ceil(units * ns * G * 2 * 4 / 256) * 256 + units * ns * G * D * 4
+    assert need == ws(4, 43, 2, 64)
+    assert _kivi_decode(lib, B, p, ws_bytes=ws(4, 32, 2, 64) - 1) == WS
+    assert _kivi_decode(lib, B, p, ws_bytes=ws(4, 32, 2, 64) - 1, lite=True) == WS
     assert _kivi_decode(lib, B, p, ws=FAKE + 16) == WS
     # quantiser: bfloat16 source only, is_value 0 or 1, an empty cache is a no-op
     c = _cache(B)
@@ -160,12 +163,15 @@ def test_kivi_validation_codes(lib, B):
     assert lib.fkv_kivi_quantize(ctypes.byref(p), c, 2, _q4(B), None) == INV
     assert lib.fkv_kivi_quantize(ctypes.byref(p), c, 0, B.fkv_q4_cache(FAKE, None, FAKE), None) == INV
     assert lib.fkv_kivi_quantize(ctypes.byref(_params(B, sk=0)), c, 1, _q4(B, 0), None) == B.FKV_SUCCESS
-    # array sizes: codes D/2 bytes per token; key metadata per 32-token group
-    # and channel, value metadata per token and 32-channel group (fp16)
+    # array sizes: key codes D/2 bytes per token; key metadata per 32-token
+    # group and channel (fp16)
     p = _params(B, batch=3, sk=100, hkv=2, hq=4, d=80)
-    assert lib.fkv_kivi_codes_bytes(ctypes.byref(p)) == 3 * 2 * 100 * 40
+    assert lib.fkv_kivi_codes_bytes(ctypes.byref(p), 0) == 3 * 2 * 100 * 40
+    # values: 4 blocks of 32 tokens x 80 channels x 16 bytes; metadata per
+    # (block, 32-channel group) lists 32 tokens
+    assert lib.fkv_kivi_codes_bytes(ctypes.byref(p), 1) == 3 * 2 * 4 * 80 * 16
     assert lib.fkv_kivi_meta_bytes(ctypes.byref(p), 0) == 3 * 2 * 4 * 80 * 2
-    assert lib.fkv_kivi_meta_bytes(ctypes.byref(p), 1) == 3 * 2 * 100 * 3 * 2
+    assert lib.fkv_kivi_meta_bytes(ctypes.byref(p), 1) == 3 * 2 * 4 * 3 * 32 * 2
 
 
 def test_lite_decode_validation_codes(lib, B):
