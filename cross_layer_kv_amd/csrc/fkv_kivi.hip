@@ -209,6 +209,15 @@ __device__ __forceinline__ uint4 codes_f16(uint32_t w)
     return make_uint4(w & 0x000F000Fu, (w >> 4) & 0x000F000Fu, (w >> 8) & 0x000F000Fu, (w >> 12) & 0x000F000Fu);
 }
 
+// Key codes: the same pairs with one instruction fewer; pairs 1 and 3 come
+// out 16x larger (nibbles 1, 5 and 3, 7 are masked in place), which the
+// query side divides out exactly.
+__device__ __forceinline__ uint4 codes_f16_k(uint32_t w)
+{
+    const uint32_t h = w >> 8;
+    return make_uint4(w & 0x000F000Fu, w & 0x00F000F0u, h & 0x000F000Fu, h & 0x00F000F0u);
+}
+
 // fp16 pairs (x_k, x_{k+4}) of eight consecutive fp16 values held as four
 // words (x0 x1)(x2 x3)(x4 x5)(x6 x7): the channel order of codes_f16.
 __device__ __forceinline__ uint4 pair_k4(uint4 u)
@@ -304,8 +313,11 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
                         for (int k = 0; k < 8; ++k) wt[k] = wp[k];
                     }
                 }
-                qa[s][ks] = make_uint4(pack2(qf[0] * wt[0], qf[4] * wt[4]), pack2(qf[1] * wt[1], qf[5] * wt[5]),
-                                       pack2(qf[2] * wt[2], qf[6] * wt[6]), pack2(qf[3] * wt[3], qf[7] * wt[7]));
+                // pairs 1 and 3 meet codes held 16x larger (codes_f16_k)
+                qa[s][ks] = make_uint4(pack2(qf[0] * wt[0], qf[4] * wt[4]),
+                                       pack2(qf[1] * wt[1] * 0.0625f, qf[5] * wt[5] * 0.0625f),
+                                       pack2(qf[2] * wt[2], qf[6] * wt[6]),
+                                       pack2(qf[3] * wt[3] * 0.0625f, qf[7] * wt[7] * 0.0625f));
                 if (!live) qa[s][ks] = make_uint4(0u, 0u, 0u, 0u);
             }
         }
@@ -326,42 +338,59 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
     // The loads of one 32-token block: key codes (2 tiles x KS k-steps),
     // value codes (NVB column blocks) and one key and one value metadata
     // chunk.  The next block's are in flight while this one is computed.
-    struct Blk {
+    struct Blk {  // key side, prefetched a block ahead
         uint32_t kc[NS][2][KS];
-        uint32_t vc[NS][NVB];
-        uint4 km, vm;
+        uint4 km;
     };
+    struct VBlk {  // value side, loaded when its block starts
+        uint32_t vc[NS][NVB];
+        uint4 vm;
+    };
+    // Every load is unconditional: out-of-range positions are clamped into
+    // the arrays and their results zeroed, so the loop has no divergent
+    // branches around memory instructions.
     auto load_block = [&](int t0, Blk& x) {
-        const int j = t0 / kGroup;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             const uint8_t* kcp = static_cast<const uint8_t*>(ksrc[s]->codes) + bh * a.Sk * (D / 2);
-            const uint8_t* vcp = static_cast<const uint8_t*>(vsrc[s]->codes) + (bh * nbv + j) * D * 16;
 #pragma unroll
             for (int tl = 0; tl < 2; ++tl) {
                 const int t = t0 + tl * 16 + l16;
+                const int tc = t < a.Sk ? t : a.Sk - 1;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    x.kc[s][tl][ks] = (ks * 32 + hb * 8 < D && t < t_end)
-                                          ? *reinterpret_cast<const uint32_t*>(kcp + (int64_t)t * (D / 2) + ks * 16 + hb * 4)
-                                          : 0u;
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bool chan = ks * 32 + hb * 8 < D;
+                    const uint32_t v = *reinterpret_cast<const uint32_t*>(kcp + (int64_t)tc * (D / 2) +
+                                                                          (chan ? ks * 16 + hb * 4 : 0));
+                    x.kc[s][tl][ks] = (chan && t < t_end) ? v : 0u;
+                }
             }
+        }
+        // metadata chunk of this lane column (columns past NC fetch a copy of
+        // chunk column mod NC and are never read)
+        const int j = t0 / kGroup;
+        const int c = l16 % NC;
+        const int s = c / (2 * KS), ks = (c >> 1) - (c / (2 * KS)) * KS, sm = c & 1;
+        const Q4View& kv = *ksrc[s];
+        const bool chan = ks * 32 + hb * 8 < D;
+        const uint4 km = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(sm ? kv.minv : kv.scale) +
+                                                         (bh * ngk + j) * D + (chan ? ks * 32 + hb * 8 : 0));
+        x.km = chan ? km : make_uint4(0u, 0u, 0u, 0u);
+    };
+    auto load_values = [&](int t0, VBlk& x) {
+        const int j = t0 / kGroup;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const uint8_t* vcp = static_cast<const uint8_t*>(vsrc[s]->codes) + (bh * nbv + j) * D * 16;
 #pragma unroll
             for (int n = 0; n < NVB; ++n)
                 x.vc[s][n] = *reinterpret_cast<const uint32_t*>(vcp + (n * 16 + l16) * 16 + hb * 4);
         }
-        x.km = make_uint4(0u, 0u, 0u, 0u);
-        x.vm = x.km;
-        if (l16 < NC) {
-            const int s = l16 / (2 * KS), ks = (l16 >> 1) - s * KS, sm = l16 & 1;
-            const Q4View& kv = *ksrc[s];
-            const Q4View& vv = *vsrc[s];
-            if (ks * 32 + hb * 8 < D)
-                x.km = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(sm ? kv.minv : kv.scale) +
-                                                       (bh * ngk + j) * D + ks * 32 + hb * 8);
-            x.vm = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(sm ? vv.minv : vv.scale) +
-                                                   ((bh * nbv + j) * KS + ks) * kGroup + hb * 8);
-        }
+        const int c = l16 % NC;
+        const int s = c / (2 * KS), ks = (c >> 1) - (c / (2 * KS)) * KS, sm = c & 1;
+        const Q4View& vv = *vsrc[s];
+        x.vm = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(sm ? vv.minv : vv.scale) +
+                                               ((bh * nbv + j) * KS + ks) * kGroup + hb * 8);
     };
 
     f32x4 oacc[NS][NVB];
@@ -375,100 +404,119 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
     }
     float m_run = -INFINITY, l_part = 0.0f;
 
+    // park a block's metadata chunks in this wave's LDS area (wave-private:
+    // in-order LDS access within the wave orders the writes after the
+    // previous block's reads).  Key chunks are stored re-paired into the
+    // (c, c+4) channel order of the codes, minima of pairs 1 and 3 scaled
+    // by 16 to meet the query side's 1/16.
+    auto park = [&](const Blk& x) {
+        if (l16 < NC) {
+            uint4 k = pair_k4(x.km);
+            if (l16 & 1) {
+                const uint32_t s16 = 0x4C004C00u;  // (16, 16) in binary16
+                k.y = pk_mul(k.y, s16);
+                k.w = pk_mul(k.w, s16);
+            }
+            s_meta[wave][0][l16][hb] = k;
+        }
+    };
+    auto compute = [&](const Blk& x, int t0) {
+        VBlk y;
+        load_values(t0, y);
+            // ---- scores: two 16-token tiles, heads on the columns ----
+            f32x4 sc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+            float cst = 0.0f;  // sum over this lane's channels of q a m (log2 units)
+    #pragma unroll
+            for (int s = 0; s < NS; ++s)
+    #pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const uint4 ksc = s_meta[wave][0][(s * KS + ks) * 2 + 0][hb];
+                    const uint4 kmn = s_meta[wave][0][(s * KS + ks) * 2 + 1][hb];
+                    const uint4 u = pk_mul4(qa[s][ks], ksc);
+                    cst = dot8(qa[s][ks], kmn, cst);
+    #pragma unroll
+                    for (int tl = 0; tl < 2; ++tl) sc[tl] = mma16(codes_f16_k(x.kc[s][tl][ks]), u, sc[tl]);
+                }
+            cst = sum4(cst);
+            // lane: head l16; entries: tokens t0 + 16 tl + 4 hb + i
+            float sv[8];
+            float bmax = -INFINITY;
+    #pragma unroll
+            for (int tl = 0; tl < 2; ++tl)
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = t0 + tl * 16 + hb * 4 + i;
+                    const float x = (hv && t < t_end) ? sc[tl][i] * kTwo24 + cst : -INFINITY;
+                    sv[tl * 4 + i] = x;
+                    bmax = fmaxf(bmax, x);
+                }
+            bmax = max4(bmax);
+            const float m_new = fmaxf(m_run, bmax);
+            if (__any(m_new > m_run)) {
+                const float corr = rel_weight(m_run, m_new);
+                l_part *= corr;
+    #pragma unroll
+                for (int s = 0; s < NS; ++s)
+    #pragma unroll
+                    for (int k = 0; k < KS; ++k) Mp[s][k] *= corr;
+                // output rows are heads 4 hb + i: fetch those heads' factors
+                // (lane h holds head h's factor: l16 = h, hb = 0)
+                float cr[G];
+    #pragma unroll
+                for (int h = 0; h < G; ++h) cr[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(corr), h));
+                float rc[4];
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float r = 1.0f;
+    #pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        if (q4 * 4 + i < G && hb == q4) r = cr[q4 * 4 + i];
+                    rc[i] = r;
+                }
+    #pragma unroll
+                for (int s = 0; s < NS; ++s)
+    #pragma unroll
+                    for (int n = 0; n < NVB; ++n)
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) oacc[s][n][i] *= rc[i];
+                m_run = m_new;
+            }
+            const float msub = m_run == -INFINITY ? 0.0f : m_run;
+            float pv[8];
+    #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pv[e] = sv[e] == -INFINITY ? 0.0f : exp2_fast(sv[e] - msub);
+                l_part += pv[e];
+            }
+            const uint4 p16 = make_uint4(pack2(pv[0], pv[1]), pack2(pv[2], pv[3]), pack2(pv[4], pv[5]), pack2(pv[6], pv[7]));
+
+            // ---- O += P' * codes, P' = p * (token's value scale), per group ----
+        if (l16 < NC) s_meta[wave][1][l16][hb] = y.vm;
+    #pragma unroll
+            for (int s = 0; s < NS; ++s)
+    #pragma unroll
+                for (int k = 0; k < KS; ++k) {
+                    const uint4 vsc = s_meta[wave][1][(s * KS + k) * 2 + 0][hb];
+                    const uint4 vmn = s_meta[wave][1][(s * KS + k) * 2 + 1][hb];
+                    const uint4 pa = pk_mul4(p16, vsc);
+                    Mp[s][k] = dot8(p16, vmn, Mp[s][k]);
+    #pragma unroll
+                    for (int n = 2 * k; n < 2 * k + 2 && n < NVB; ++n)
+                        oacc[s][n] = mma16(pa, codes_f16(y.vc[s][n]), oacc[s][n]);
+                }
+    };
+
+    // the next block's key-side loads are in flight while a block is
+    // computed (its value-side loads are issued when it starts)
+    const int step = NW * kGroup;
     Blk cur;
     int t0 = t_begin + wave * kGroup;
     if (t0 < t_end) load_block(t0, cur);
-    for (; t0 < t_end; t0 += NW * kGroup) {
-        // park this block's metadata (a wave-private area: in-order LDS
-        // access within the wave orders it against last block's reads)
-        if (l16 < NC) {
-            s_meta[wave][0][l16][hb] = cur.km;
-            s_meta[wave][1][l16][hb] = cur.vm;
-        }
+    for (; t0 < t_end; t0 += step) {
+        park(cur);
         Blk nxt;
-        const int t1 = t0 + NW * kGroup;
-        if (t1 < t_end) load_block(t1, nxt);
-
-        // ---- scores: two 16-token tiles, heads on the columns ----
-        f32x4 sc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
-        float cst = 0.0f;  // sum over this lane's channels of q a m (log2 units)
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const uint4 ksc = s_meta[wave][0][(s * KS + ks) * 2 + 0][hb];
-                const uint4 kmn = s_meta[wave][0][(s * KS + ks) * 2 + 1][hb];
-                const uint4 u = pk_mul4(qa[s][ks], pair_k4(ksc));
-                cst = dot8(qa[s][ks], pair_k4(kmn), cst);
-#pragma unroll
-                for (int tl = 0; tl < 2; ++tl) sc[tl] = mma16(codes_f16(cur.kc[s][tl][ks]), u, sc[tl]);
-            }
-        cst = sum4(cst);
-        // lane: head l16; entries: tokens t0 + 16 tl + 4 hb + i
-        float sv[8];
-        float bmax = -INFINITY;
-#pragma unroll
-        for (int tl = 0; tl < 2; ++tl)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = t0 + tl * 16 + hb * 4 + i;
-                const float x = (hv && t < t_end) ? sc[tl][i] * kTwo24 + cst : -INFINITY;
-                sv[tl * 4 + i] = x;
-                bmax = fmaxf(bmax, x);
-            }
-        bmax = max4(bmax);
-        const float m_new = fmaxf(m_run, bmax);
-        if (__any(m_new > m_run)) {
-            const float corr = rel_weight(m_run, m_new);
-            l_part *= corr;
-#pragma unroll
-            for (int s = 0; s < NS; ++s)
-#pragma unroll
-                for (int k = 0; k < KS; ++k) Mp[s][k] *= corr;
-            // output rows are heads 4 hb + i: fetch those heads' factors
-            // (lane h holds head h's factor: l16 = h, hb = 0)
-            float cr[G];
-#pragma unroll
-            for (int h = 0; h < G; ++h) cr[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(corr), h));
-            float rc[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float r = 1.0f;
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    if (q4 * 4 + i < G && hb == q4) r = cr[q4 * 4 + i];
-                rc[i] = r;
-            }
-#pragma unroll
-            for (int s = 0; s < NS; ++s)
-#pragma unroll
-                for (int n = 0; n < NVB; ++n)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) oacc[s][n][i] *= rc[i];
-            m_run = m_new;
-        }
-        const float msub = m_run == -INFINITY ? 0.0f : m_run;
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            pv[e] = sv[e] == -INFINITY ? 0.0f : exp2_fast(sv[e] - msub);
-            l_part += pv[e];
-        }
-        const uint4 p16 = make_uint4(pack2(pv[0], pv[1]), pack2(pv[2], pv[3]), pack2(pv[4], pv[5]), pack2(pv[6], pv[7]));
-
-        // ---- O += P' * codes, P' = p * (token's value scale), per group ----
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-            for (int k = 0; k < KS; ++k) {
-                const uint4 vsc = s_meta[wave][1][(s * KS + k) * 2 + 0][hb];
-                const uint4 vmn = s_meta[wave][1][(s * KS + k) * 2 + 1][hb];
-                const uint4 pa = pk_mul4(p16, vsc);
-                Mp[s][k] = dot8(p16, vmn, Mp[s][k]);
-#pragma unroll
-                for (int n = 2 * k; n < 2 * k + 2 && n < NVB; ++n)
-                    oacc[s][n] = mma16(pa, codes_f16(cur.vc[s][n]), oacc[s][n]);
-            }
+        if (t0 + step < t_end) load_block(t0 + step, nxt);
+        compute(cur, t0);
         cur = nxt;
     }
 

@@ -253,12 +253,17 @@ def test_workspace_size(lib, B):
     p = _params(B, sq=2)
     assert lib.fkv_decode_workspace_size(ctypes.byref(p)) == 0
     # 650M-shape decode: 32 x 8 = 256 (batch, kv head) units fill the chip with
-    # one workgroup each, so no split and no workspace
+    # one workgroup each, so the bf16 plans need no split; the 4-bit
+    # single-source plan aims at two workgroups per CU (2 splits of 4096
+    # tokens) and sets the size
     p = _params(B, batch=32, sk=8192, hq=16, hkv=8, d=96)
-    assert lib.fkv_decode_workspace_size(ctypes.byref(p)) == 0
-    # long context, batch 1: 8 units x 32 splits of 4096 tokens, G = 2, D = 128
+    units, ns, G, D = 256, 2, 2, 96
+    assert lib.fkv_decode_workspace_size(ctypes.byref(p)) == \
+        math.ceil(units * ns * G * 2 * 4 / 256) * 256 + units * ns * G * D * 4
+    # long context, batch 1: 8 units; the bf16 plans take 32 splits of 4096
+    # tokens, the 4-bit single-source plan 64 splits of 2048 (the largest)
     p = _params(B, batch=1, sk=131072, hq=16, hkv=8, d=128)
-    units, ns, G, D = 8, 32, 2, 128
+    units, ns, G, D = 8, 64, 2, 128
     expect = math.ceil(units * ns * G * 2 * 4 / 256) * 256 + units * ns * G * D * 4
     assert lib.fkv_decode_workspace_size(ctypes.byref(p)) == expect
     # G = 64 (matrix-core decode) aims at 512 workgroups of 64-token tiles:
