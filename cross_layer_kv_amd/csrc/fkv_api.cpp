@@ -105,7 +105,7 @@ fkv::DecodePlan plan_decode(const fkv_params* p, bool fused, bool kivi = false)
 {
     fkv::DecodePlan pl{};
     const int64_t G = p->num_q_heads / p->num_kv_heads;
-    pl.waves = kivi ? fkv::kivi_waves(fused, (int)G) : fkv::decode_waves(p->dtype == FKV_F32, fused, (int)G);
+    pl.waves = kivi ? fkv::kivi_waves(fused, (int)G, p->head_dim) : fkv::decode_waves(p->dtype == FKV_F32, fused, (int)G);
     const int64_t units = (int64_t)p->batch * p->num_kv_heads;
     const int64_t S = p->seqlen_k;
     // G = 64 runs the matrix-core kernel: 64-token tiles, and it aims at two

@@ -430,6 +430,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdArgs a)
     constexpr int BM = RB * 32;              // query rows per workgroup
 
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];  // [buf][K~, V~][row][P]
+    __shared__ __attribute__((aligned(16))) float s_w[FUSED ? 4 : 1][D];  // a, a', b, b' of this KV head
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -452,6 +453,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdArgs a)
         for (int i = tid; i < 2 * 2 * kKTile * (DP - D); i += kBwdThreads) {
             const int r = i / (DP - D), c = i - r * (DP - D);
             smem[r * P + D + c] = 0;
+        }
+    }
+    if constexpr (FUSED) {
+        for (int i = tid; i < 4 * D; i += kBwdThreads) {
+            const float* w = i < D ? a.kw1 : (i < 2 * D ? a.kwn : (i < 3 * D ? a.vw1 : a.vwn));
+            s_w[i / D][i - (i / D) * D] = w[(int64_t)g * D + i - (i / D) * D];
         }
     }
 
@@ -517,11 +524,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdArgs a)
             uint4 kf = xr[0][p], vf = xr[1][p];
             if constexpr (FUSED) {
                 float w1[8], wn[8];
-                load8f(a.kw1 + g * D + c * 8, w1);
-                load8f(a.kwn + g * D + c * 8, wn);
+                load8f(&s_w[0][c * 8], w1);
+                load8f(&s_w[1][c * 8], wn);
                 kf = fuse8_bf16(xr[0][p], xr[2][p], w1, wn);
-                load8f(a.vw1 + g * D + c * 8, w1);
-                load8f(a.vwn + g * D + c * 8, wn);
+                load8f(&s_w[2][c * 8], w1);
+                load8f(&s_w[3][c * 8], wn);
                 vf = fuse8_bf16(xr[1][p], xr[3][p], w1, wn);
             }
             *reinterpret_cast<uint4*>(kt_ + r * P + c * 8) = kf;
@@ -595,19 +602,31 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdArgs a)
 }
 
 // ---- 4. weight gradients: sum of the per-(batch, key tile) partials ----
+// One workgroup per (vector w, KV head g); thread (d, part) sums every
+// kRedParts-th partial of channel d in order, then the parts are added in
+// order: a fixed summation order, so the result is deterministic.
+constexpr int kRedParts = 8;
 __global__ __launch_bounds__(256) void bwd_wreduce_kernel(const BwdArgs a)
 {
-    const int i = blockIdx.x * 256 + threadIdx.x;  // (w, g, d)
-    if (i >= 4 * a.Hkv * a.D) return;
-    const int d = i % a.D;
-    const int g = (i / a.D) % a.Hkv;
-    const int w = i / (a.D * a.Hkv);
-    float s = 0.0f;
-    for (int b = 0; b < a.B; ++b)
-        for (int kt = 0; kt < a.nkt; ++kt)
+    __shared__ float red[kRedParts][128];
+    const int w = blockIdx.x / a.Hkv, g = blockIdx.x - (blockIdx.x / a.Hkv) * a.Hkv;
+    const int n = a.B * a.nkt;
+    for (int i = threadIdx.x; i < kRedParts * a.D; i += 256) {
+        const int d = i % a.D, part = i / a.D;
+        float s = 0.0f;
+        for (int k = part; k < n; k += kRedParts) {
+            const int b = k / a.nkt, kt = k - (k / a.nkt) * a.nkt;
             s += a.wpart[((int64_t)item_index(b, g, kt, a.Hkv, a.nkt) * 4 + w) * a.D + d];
-    float* out = w == 0 ? a.dkw1 : (w == 1 ? a.dkwn : (w == 2 ? a.dvw1 : a.dvwn));
-    out[g * a.D + d] = s;
+        }
+        red[part][d] = s;
+    }
+    __syncthreads();
+    for (int d = threadIdx.x; d < a.D; d += 256) {
+        float s = 0.0f;
+        for (int part = 0; part < kRedParts; ++part) s += red[part][d];
+        float* out = w == 0 ? a.dkw1 : (w == 1 ? a.dkwn : (w == 2 ? a.dvw1 : a.dvwn));
+        out[g * a.D + d] = s;
+    }
 }
 
 template <int D, bool FUSED, int G>
@@ -627,7 +646,7 @@ int launch_bwd3(const BwdArgs& a, hipStream_t st)
                        dim3(kBwdThreads), 0, st, a);
     if ((rc = (int)hipGetLastError())) return rc;
     if constexpr (FUSED) {
-        hipLaunchKernelGGL(bwd_wreduce_kernel, dim3((unsigned)((4 * a.Hkv * a.D + 255) / 256)), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(bwd_wreduce_kernel, dim3((unsigned)(4 * a.Hkv)), dim3(256), 0, st, a);
         rc = (int)hipGetLastError();
     }
     return rc;

@@ -60,11 +60,13 @@ constexpr int decode_waves(int dtype_f32, bool fused, int G)
 }
 
 // Waves per workgroup of the 4-bit decode kernel (a wave takes 32-token
-// blocks); its block loads and matrix-core operands allow 2 waves per SIMD.
-constexpr int kivi_waves(bool fused, int G)
+// blocks).  Eight: at twelve the four-source kernel (D = 96) must spill to
+// fit 3 waves per SIMD and measured slower.
+constexpr int kivi_waves(bool fused, int G, int D)
 {
     (void)fused;
     (void)G;
+    (void)D;
     return 8;
 }
 

@@ -285,8 +285,11 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
 
     // q * a * scale * log2e of this lane's head, as fp16 pairs in the
     // channel order of codes_f16: k-step ks, channels 32 ks + 8 hb + {k, k+4}
-    uint4 qa[NS][KS];
-    {
+    // q * a * scale * log2e of each lane's head, fp16 pairs in the channel
+    // order of the codes, kept in LDS (the same for every wave): lane
+    // (head l16, quarter hb), k-step ks, channels 32 ks + 8 hb + {k, k+4}
+    __shared__ uint4 s_qa[NS][KS][64];
+    if (wave == 0) {
         const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + (int64_t)g * G + (hv ? l16 : 0)) * D;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -314,14 +317,16 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
                     }
                 }
                 // pairs 1 and 3 meet codes held 16x larger (codes_f16_k)
-                qa[s][ks] = make_uint4(pack2(qf[0] * wt[0], qf[4] * wt[4]),
-                                       pack2(qf[1] * wt[1] * 0.0625f, qf[5] * wt[5] * 0.0625f),
-                                       pack2(qf[2] * wt[2], qf[6] * wt[6]),
-                                       pack2(qf[3] * wt[3] * 0.0625f, qf[7] * wt[7] * 0.0625f));
-                if (!live) qa[s][ks] = make_uint4(0u, 0u, 0u, 0u);
+                uint4 v = make_uint4(pack2(qf[0] * wt[0], qf[4] * wt[4]),
+                                     pack2(qf[1] * wt[1] * 0.0625f, qf[5] * wt[5] * 0.0625f),
+                                     pack2(qf[2] * wt[2], qf[6] * wt[6]),
+                                     pack2(qf[3] * wt[3] * 0.0625f, qf[7] * wt[7] * 0.0625f));
+                if (!live) v = make_uint4(0u, 0u, 0u, 0u);
+                s_qa[s][ks][lane] = v;
             }
         }
     }
+    __syncthreads();
 
     const Q4View* ksrc[2] = {&a.qk1, &a.qkn};
     const Q4View* vsrc[2] = {&a.qv1, &a.qvn};
@@ -432,8 +437,9 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
                 for (int ks = 0; ks < KS; ++ks) {
                     const uint4 ksc = s_meta[wave][0][(s * KS + ks) * 2 + 0][hb];
                     const uint4 kmn = s_meta[wave][0][(s * KS + ks) * 2 + 1][hb];
-                    const uint4 u = pk_mul4(qa[s][ks], ksc);
-                    cst = dot8(qa[s][ks], kmn, cst);
+                    const uint4 qav = s_qa[s][ks][lane];
+                    const uint4 u = pk_mul4(qav, ksc);
+                    cst = dot8(qav, kmn, cst);
     #pragma unroll
                     for (int tl = 0; tl < 2; ++tl) sc[tl] = mma16(codes_f16_k(x.kc[s][tl][ks]), u, sc[tl]);
                 }
@@ -590,7 +596,7 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
 template <int D, bool FUSED, int G>
 int launch_q4(const KiviDecodeArgs& a, int waves, hipStream_t st)
 {
-    constexpr int NW = kivi_waves(FUSED, G);
+    constexpr int NW = kivi_waves(FUSED, G, D);
     if (waves != NW) return (int)hipErrorInvalidValue;
     hipLaunchKernelGGL((q4_decode_kernel<D, FUSED, G, NW>), dim3(a.n_splits, a.B * a.Hkv), dim3(64 * NW), 0, st, a);
     const int rc = (int)hipGetLastError();
