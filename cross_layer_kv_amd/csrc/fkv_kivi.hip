@@ -343,11 +343,11 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
     // The loads of one 32-token block: key codes (2 tiles x KS k-steps),
     // value codes (NVB column blocks) and one key and one value metadata
     // chunk.  The next block's are in flight while this one is computed.
-    struct Blk {  // key side, prefetched a block ahead
+    struct Blk {  // key side
         uint32_t kc[NS][2][KS];
         uint4 km;
     };
-    struct VBlk {  // value side, loaded when its block starts
+    struct VBlk {  // value side
         uint32_t vc[NS][NVB];
         uint4 vm;
     };
@@ -425,9 +425,7 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
             s_meta[wave][0][l16][hb] = k;
         }
     };
-    auto compute = [&](const Blk& x, int t0) {
-        VBlk y;
-        load_values(t0, y);
+    auto compute = [&](const Blk& x, const VBlk& y, int t0) {
             // ---- scores: two 16-token tiles, heads on the columns ----
             f32x4 sc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
             float cst = 0.0f;  // sum over this lane's channels of q a m (log2 units)
@@ -512,18 +510,30 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
                 }
     };
 
-    // the next block's key-side loads are in flight while a block is
-    // computed (its value-side loads are issued when it starts)
+    // The next block's key-side loads are in flight while a block is
+    // computed.  The four-source kernel prefetches the value side as well;
+    // the single-source one (more waves per SIMD) issues it when a block
+    // starts, which measured faster there.
     const int step = NW * kGroup;
     Blk cur;
+    VBlk vcur;
     int t0 = t_begin + wave * kGroup;
-    if (t0 < t_end) load_block(t0, cur);
+    if (t0 < t_end) {
+        load_block(t0, cur);
+        if constexpr (FUSED) load_values(t0, vcur);
+    }
     for (; t0 < t_end; t0 += step) {
         park(cur);
         Blk nxt;
-        if (t0 + step < t_end) load_block(t0 + step, nxt);
-        compute(cur, t0);
+        VBlk vnxt;
+        if (t0 + step < t_end) {
+            load_block(t0 + step, nxt);
+            if constexpr (FUSED) load_values(t0 + step, vnxt);
+        }
+        if constexpr (!FUSED) load_values(t0, vcur);
+        compute(cur, vcur, t0);
         cur = nxt;
+        if constexpr (FUSED) vcur = vnxt;
     }
 
     // ---- wave results: (m, l) and the minimum terms per head ----
