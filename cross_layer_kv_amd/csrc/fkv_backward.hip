@@ -32,7 +32,7 @@
 //      group in 64-row LDS tiles, accumulating dKf and dVf.  It writes the
 //      four source gradients and its partial column sums for the weight
 //      gradients.
-//   3. query tiles: a workgroup of 4 waves owns 128 (query row, head)
+//   3. query tiles: a workgroup of 8 waves owns 256 (query row, head)
 //      columns and walks the fused key/value tiles (built in LDS once per
 //      workgroup) accumulating dQ.  dQ is thus written once, with no float
 //      atomics, and every result is run-to-run deterministic.
@@ -68,6 +68,8 @@ constexpr int kBwdThreads = 256;  // 4 waves
 constexpr int kKeysPerWg = kBwdKeyTile;  // key-tile kernel: 32 keys per wave
 constexpr int kQRows = 64;        // key-tile kernel: query rows per LDS tile
 constexpr int kKTile = 64;        // query-tile kernel: keys per LDS tile
+constexpr int kDqWaves = 8;       // query-tile kernel: 8 x 32 (query row, head) columns
+constexpr int kDqThreads = 64 * kDqWaves;
 
 // Slot of the (batch, KV head, key tile) weight-gradient partial.
 __device__ __forceinline__ int64_t item_index(int b, int g, int kt, int Hkv, int nkt)
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdArgs a)
 
 // ---- 3. query tiles: dQ ----
 template <int D, bool FUSED, int G>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdArgs a)
+__global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const BwdArgs a)
 {
     constexpr int DP = (D + 31) / 32 * 32;
     constexpr int NDB = DP / 32;
@@ -424,9 +426,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdArgs a)
     constexpr int P = DP + 8;
     constexpr int CPR = D / 8;
     constexpr int TILE = kKTile * P;
-    constexpr int HPW = G < 4 ? G : 4;       // heads per workgroup
-    constexpr int NHG = G / HPW;             // head groups per KV head
-    constexpr int RB = 4 / HPW;              // 32-row blocks per workgroup
+    constexpr int HPW = G < kDqWaves ? G : kDqWaves;  // heads per workgroup
+    constexpr int NHG = G / HPW;                      // head groups per KV head
+    constexpr int RB = kDqWaves / HPW;                // 32-row blocks per workgroup
     constexpr int BM = RB * 32;              // query rows per workgroup
 
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];  // [buf][K~, V~][row][P]
@@ -450,13 +452,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdArgs a)
     const int r0 = qt * BM + (wave / HPW) * 32;  // this wave's 32 query rows
 
     if constexpr (DP > D) {
-        for (int i = tid; i < 2 * 2 * kKTile * (DP - D); i += kBwdThreads) {
+        for (int i = tid; i < 2 * 2 * kKTile * (DP - D); i += kDqThreads) {
             const int r = i / (DP - D), c = i - r * (DP - D);
             smem[r * P + D + c] = 0;
         }
     }
     if constexpr (FUSED) {
-        for (int i = tid; i < 4 * D; i += kBwdThreads) {
+        for (int i = tid; i < 4 * D; i += kDqThreads) {
             const float* w = i < D ? a.kw1 : (i < 2 * D ? a.kwn : (i < 3 * D ? a.vw1 : a.vwn));
             s_w[i / D][i - (i / D) * D] = w[(int64_t)g * D + i - (i / D) * D];
         }
@@ -491,13 +493,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdArgs a)
     const int nt = (kend + kKTile - 1) / kKTile;
 
     constexpr int NITEM = kKTile * CPR;
-    constexpr int NPASS = (NITEM + kBwdThreads - 1) / kBwdThreads;
+    constexpr int NPASS = (NITEM + kDqThreads - 1) / kDqThreads;
     constexpr int NSRC = FUSED ? 4 : 2;
     uint4 xr[NSRC][NPASS];
     auto load_tile = [&](int t) {
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
-            const int e = tid + p * kBwdThreads;
+            const int e = tid + p * kDqThreads;
             const int r = e / CPR, c = e - (e / CPR) * CPR;
             const int key = t * kKTile + r;
             const bool ok = e < NITEM && key < S;
@@ -518,7 +520,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const BwdArgs a)
         uint16_t* vt_ = smem + (buf * 2 + 1) * TILE;
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
-            const int e = tid + p * kBwdThreads;
+            const int e = tid + p * kDqThreads;
             if (e >= NITEM) continue;
             const int r = e / CPR, c = e - (e / CPR) * CPR;
             uint4 kf = xr[0][p], vf = xr[1][p];
@@ -639,11 +641,11 @@ int launch_bwd3(const BwdArgs& a, hipStream_t st)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, FUSED, G>), dim3((unsigned)(a.B * a.Hkv * a.nkt)), dim3(kBwdThreads), 0, st,
                        a);
     if ((rc = (int)hipGetLastError())) return rc;
-    constexpr int HPW = G < 4 ? G : 4;
-    constexpr int BM = (4 / HPW) * 32;
+    constexpr int HPW = G < kDqWaves ? G : kDqWaves;
+    constexpr int BM = (kDqWaves / HPW) * 32;
     const int nqt = (a.S + BM - 1) / BM;
     hipLaunchKernelGGL((bwd_dq_kernel<D, FUSED, G>), dim3((unsigned)(a.B * a.Hkv * (G / HPW) * nqt)),
-                       dim3(kBwdThreads), 0, st, a);
+                       dim3(kDqThreads), 0, st, a);
     if ((rc = (int)hipGetLastError())) return rc;
     if constexpr (FUSED) {
         hipLaunchKernelGGL(bwd_wreduce_kernel, dim3((unsigned)(4 * a.Hkv)), dim3(256), 0, st, a);
