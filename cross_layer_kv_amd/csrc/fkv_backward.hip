@@ -304,18 +304,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdArgs a)
         const int qb = q_begin + (it / G) * kQRows;
         const uint16_t* qs = smem + (buf * 2 + 0) * TILE;
         const uint16_t* os = smem + (buf * 2 + 1) * TILE;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
+        // P, dS and the dV / dK products of sub-block sb (32 query rows)
+        // from its score and dP accumulators
+        auto finish = [&](const f32x16& sacc, const f32x16& pacc, int sb, bool masked) {
             const int qs0 = qb + sb * 32;
-            // wave-uniform skips: rows past the end, or (causal) every key
-            // of the wave after every row of the block
-            if (qs0 >= S || (a.causal && qs0 + 31 < kw) || kw >= S) continue;
-            f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                sacc = mma(row_frag(qs, P, sb * 32, ks, l32, hi), kreg[ks], sacc);
-                pacc = mma(row_frag(os, P, sb * 32, ks, l32, hi), vreg[ks], pacc);
-            }
             // lane: key kw + l32; entries: query rows qs0 + 8j + 4hi + i
             const int key = kw + l32;
             float pv[16], dsv[16];
@@ -327,7 +319,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdArgs a)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int q = qs0 + 8 * j + 4 * hi + i;
-                    const bool vis = key < S && q < S && (!a.causal || key <= q);
+                    const bool vis = !masked || (key < S && q < S && (!a.causal || key <= q));
                     const float p = vis ? exp2_fast(sacc[4 * j + i] * sl2 - Lv[i]) : 0.0f;
                     pv[4 * j + i] = p;
                     dsv[4 * j + i] = p * (pacc[4 * j + i] - Dv[i]);
@@ -348,6 +340,38 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdArgs a)
                     dv[nb] = mma(pa[c], tr_frag(os, P, sb * 32 + 16 * c, nb * 32, l32, hi), dv[nb]);
                     dk[nb] = mma(da[c], tr_frag(qs, P, sb * 32 + 16 * c, nb * 32, l32, hi), dk[nb]);
                 }
+        };
+        // Full tiles (every row and key inside S, and causally every key at
+        // or before every row) take the unmasked path with the four score /
+        // dP chains of both sub-blocks issued together, so that the second
+        // sub-block's products run while the first one's P and dS are formed.
+        const bool full = qb + 63 < S && kw + 31 < S && (!a.causal || qb >= kw + 31);
+        if (full) {
+            f32x16 s0 = f32x16{}, p0 = f32x16{}, s1 = f32x16{}, p1 = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                s0 = mma(row_frag(qs, P, 0, ks, l32, hi), kreg[ks], s0);
+                p0 = mma(row_frag(os, P, 0, ks, l32, hi), vreg[ks], p0);
+                s1 = mma(row_frag(qs, P, 32, ks, l32, hi), kreg[ks], s1);
+                p1 = mma(row_frag(os, P, 32, ks, l32, hi), vreg[ks], p1);
+            }
+            finish(s0, p0, 0, false);
+            finish(s1, p1, 1, false);
+        } else {
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                const int qs0 = qb + sb * 32;
+                // wave-uniform skips: rows past the end, or (causal) every key
+                // of the wave after every row of the block
+                if (qs0 >= S || (a.causal && qs0 + 31 < kw) || kw >= S) continue;
+                f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    sacc = mma(row_frag(qs, P, sb * 32, ks, l32, hi), kreg[ks], sacc);
+                    pacc = mma(row_frag(os, P, sb * 32, ks, l32, hi), vreg[ks], pacc);
+                }
+                finish(sacc, pacc, sb, true);
+            }
         }
         if (it + 1 < nit) store_tile(buf ^ 1);
     }
