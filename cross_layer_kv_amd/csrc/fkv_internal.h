@@ -86,9 +86,12 @@ struct PrefillArgs {
     float scale_log2;
 };
 
-// KIVI-style 4-bit cache of one source, contiguous (see fusedkv.h):
-//   codes [B, Hkv, S, D/2] bytes (channel 2i low nibble, 2i+1 high)
-//   scale / minv fp16: keys [B, Hkv, ceil(S/32), D], values [B, Hkv, S, ceil(D/32)]
+// KIVI-style 4-bit cache of one source, contiguous (layout in fusedkv.h),
+// NB = ceil(S/32):
+//   keys    codes [B, Hkv, S, D/2] bytes (channel 2i low nibble, 2i+1 high);
+//           scale / minv fp16 [B, Hkv, NB, D]
+//   values  codes [B, Hkv, NB, D, 16] bytes, channel-major per 32-token block;
+//           scale / minv fp16 [B, Hkv, NB, ceil(D/32), 32]
 struct Q4View {
     const void* codes;
     const void* scale;

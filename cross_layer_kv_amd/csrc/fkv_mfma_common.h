@@ -1,7 +1,7 @@
 // fkv_mfma_common.h -- device helpers shared by the kernels that are not the
 // plain decode (causal prefill, high-GQA decode, 4-bit decode and its
-// quantiser): fp16 / bf16 packing, the two-source fusion dot products,
-// half-wave and token-group exchanges and buffer-descriptor loads.
+// quantiser, backward pass): fp16 / bf16 packing, the two-source fusion dot
+// products, half-wave and token-group exchanges and buffer-descriptor loads.
 #pragma once
 
 #include <hip/hip_runtime.h>
