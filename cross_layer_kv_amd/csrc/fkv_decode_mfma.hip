@@ -51,7 +51,7 @@ constexpr float kLn2 = 0.69314718055994530942f;
 __device__ __forceinline__ float rel2(float m, float M) { return m == -INFINITY ? 0.0f : exp2_fast(m - M); }
 
 template <int D, bool FUSED>
-__global__ __launch_bounds__(kHThreads) void hgqa_decode_kernel(const DecodeArgs a)
+__global__ __launch_bounds__(kHThreads, 2) void hgqa_decode_kernel(const DecodeArgs a)
 {
     constexpr int DP = (D + 31) / 32 * 32;
     constexpr int KS = D / 16;           // k-steps of the score product
