@@ -26,10 +26,11 @@
 // Kernels
 //   1. prep: per (batch, head, row) the LSE in log2 units and
 //      rowsum(dO * O) (float32).
-//   2. key tiles: a workgroup of 4 waves owns 128 keys of one (batch, KV
-//      head); each wave keeps its 32 fused keys and values as matrix-core
-//      operands in registers and walks the query rows of all G heads of the
-//      group in 64-row LDS tiles, accumulating dKf and dVf.  It writes the
+//   2. key tiles: a workgroup of 8 waves owns 128 keys of one (batch, KV
+//      head): four waves accumulate dVf and four dKf of one 32-key block
+//      each, keeping the block's fused keys (and values) as matrix-core
+//      operands in registers, and walk the query rows of all G heads of the
+//      group in 64-row LDS tiles.  It writes the
 //      four source gradients and its partial column sums for the weight
 //      gradients.
 //   3. query tiles: a workgroup of 8 waves owns 256 (query row, head)
@@ -51,6 +52,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "fkv_internal.h"
 #include "fkv_mfma_common.h"
@@ -64,11 +66,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kBwdThreads = 256;  // 4 waves
-constexpr int kKeysPerWg = kBwdKeyTile;  // key-tile kernel: 32 keys per wave
+constexpr int kKeysPerWg = kBwdKeyTile;  // key-tile kernel: 4 blocks of 32 keys
 constexpr int kQRows = 64;        // key-tile kernel: query rows per LDS tile
 constexpr int kKTile = 64;        // query-tile kernel: keys per LDS tile
 constexpr int kDqWaves = 8;       // query-tile kernel: 8 x 32 (query row, head) columns
+constexpr int kDkvThreads = 512;  // key-tile kernel: 4 value waves + 4 key waves
 constexpr int kDqThreads = 64 * kDqWaves;
 
 // Slot of the (batch, KV head, key tile) weight-gradient partial.
@@ -161,8 +163,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs a)
 }
 
 // ---- 2. key tiles: dKf, dVf, source gradients, weight partials ----
+// Eight waves over 128 keys: wave w < 4 takes key block w for the values
+// (scores, P, dVf += P^T dO), wave w >= 4 key block w - 4 for the keys
+// (scores, dP, dS, dKf += dS^T Q).  Each wave holds one accumulator and the
+// operands it needs, which fits two waves per SIMD (waves w and w + 4
+// share one); the scores are formed by both waves of a block.
 template <int D, bool FUSED, int G>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdArgs a)
+__global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs a)
 {
     constexpr int DP = (D + 31) / 32 * 32;  // channels padded to whole 32-column blocks
     constexpr int NDB = DP / 32;
@@ -174,6 +181,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdArgs a)
     static_assert(2 * 2 * TILE * 2 >= kKeysPerWg * SP * 4, "transpose buffer fits in the tile buffers");
 
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];  // [buf][Q, dO][row][P]
+    __shared__ __attribute__((aligned(16))) uint16_t vsm[kKeysPerWg * P];   // fused values [key][P]
     __shared__ __attribute__((aligned(16))) float Ls[2][kQRows];
     __shared__ __attribute__((aligned(16))) float Dl[2][kQRows];
 
@@ -181,6 +189,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdArgs a)
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hi = lane >> 5;
+    const bool kwave = wave >= 4;  // keys (dK) or values (dV)
+    const int kb = wave & 3;
 
     const int nkt = a.nkt;
     const int items = a.B * a.Hkv * nkt;
@@ -191,31 +201,33 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdArgs a)
     const int b = unit / a.Hkv, g = unit - (unit / a.Hkv) * a.Hkv;
     const int S = a.S;
     const int k0 = kt * kKeysPerWg;
-    const int kw = k0 + wave * 32;
+    const int kw = k0 + kb * 32;
 
     // zero the padded channels [D, DP) of every tile row (never loaded)
     if constexpr (DP > D) {
-        for (int i = tid; i < 2 * 2 * kQRows * (DP - D); i += kBwdThreads) {
+        for (int i = tid; i < 2 * 2 * kQRows * (DP - D); i += kDkvThreads) {
             const int r = i / (DP - D), c = i - r * (DP - D);
             smem[r * P + D + c] = 0;
         }
     }
 
-    // ---- this wave's 32 fused keys / values as B operands (lane: key l32) ----
-    uint4 kreg[KS], vreg[KS];
+    // ---- this block's 32 fused keys as B operands (lane: key l32); key
+    // waves also stage the block's fused values in LDS ----
+    uint4 kreg[KS];
     {
         const int key = kw + l32;
         const bool ok = key < S;
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int ch = ks * 16 + hi * 8;
-            uint4 k1 = make_uint4(0u, 0u, 0u, 0u), kn = k1, v1 = k1, vn = k1;
+            uint4 k1 = z, kn = z, v1 = z, vn = z;
             if (ok) {
                 k1 = *reinterpret_cast<const uint4*>(row_ptr(a.k1, b, key, g) + ch);
-                v1 = *reinterpret_cast<const uint4*>(row_ptr(a.v1, b, key, g) + ch);
-                if constexpr (FUSED) {
-                    kn = *reinterpret_cast<const uint4*>(row_ptr(a.kn, b, key, g) + ch);
-                    vn = *reinterpret_cast<const uint4*>(row_ptr(a.vn, b, key, g) + ch);
+                if constexpr (FUSED) kn = *reinterpret_cast<const uint4*>(row_ptr(a.kn, b, key, g) + ch);
+                if (kwave) {
+                    v1 = *reinterpret_cast<const uint4*>(row_ptr(a.v1, b, key, g) + ch);
+                    if constexpr (FUSED) vn = *reinterpret_cast<const uint4*>(row_ptr(a.vn, b, key, g) + ch);
                 }
             }
             if constexpr (FUSED) {
@@ -223,22 +235,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdArgs a)
                 load8f(a.kw1 + g * D + ch, w1);
                 load8f(a.kwn + g * D + ch, wn);
                 kreg[ks] = fuse8_bf16(k1, kn, w1, wn);
-                load8f(a.vw1 + g * D + ch, w1);
-                load8f(a.vwn + g * D + ch, wn);
-                vreg[ks] = fuse8_bf16(v1, vn, w1, wn);
+                if (kwave) {
+                    load8f(a.vw1 + g * D + ch, w1);
+                    load8f(a.vwn + g * D + ch, wn);
+                    *reinterpret_cast<uint4*>(vsm + (kb * 32 + l32) * P + ch) = fuse8_bf16(v1, vn, w1, wn);
+                }
             } else {
                 kreg[ks] = k1;
-                vreg[ks] = v1;
+                if (kwave) *reinterpret_cast<uint4*>(vsm + (kb * 32 + l32) * P + ch) = v1;
             }
         }
     }
 
-    f32x16 dk[NDB], dv[NDB];
+    f32x16 acc[NDB];  // dKf (key waves) or dVf (value waves)
 #pragma unroll
-    for (int i = 0; i < NDB; ++i) {
-        dk[i] = f32x16{};
-        dv[i] = f32x16{};
-    }
+    for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
 
     // query tiles: rows qb .. qb+63 of head g*G + hh; causal rows below k0
     // see none of these keys
@@ -248,7 +259,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdArgs a)
 
     // tile loader: thread -> (row, 16-byte chunk) items of Q and dO
     constexpr int NITEM = kQRows * CPR;
-    constexpr int NPASS = (NITEM + kBwdThreads - 1) / kBwdThreads;
+    constexpr int NPASS = (NITEM + kDkvThreads - 1) / kDkvThreads;
     uint4 xq[NPASS], xo[NPASS];
     float xl = 0.0f, xd = 0.0f;
     auto load_tile = [&](int it) {
@@ -256,7 +267,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdArgs a)
         const int h = g * G + it % G;
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
-            const int e = tid + p * kBwdThreads;
+            const int e = tid + p * kDkvThreads;
             const int r = e / CPR, c = e - (e / CPR) * CPR;
             const int row = qb + r;
             xq[p] = make_uint4(0u, 0u, 0u, 0u);
@@ -279,7 +290,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdArgs a)
         uint16_t* os = smem + (buf * 2 + 1) * TILE;
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
-            const int e = tid + p * kBwdThreads;
+            const int e = tid + p * kDkvThreads;
             if (e < NITEM) {
                 const int r = e / CPR, c = e - (e / CPR) * CPR;
                 *reinterpret_cast<uint4*>(qs + r * P + c * 8) = xq[p];
@@ -304,75 +315,86 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdArgs a)
         const int qb = q_begin + (it / G) * kQRows;
         const uint16_t* qs = smem + (buf * 2 + 0) * TILE;
         const uint16_t* os = smem + (buf * 2 + 1) * TILE;
-        // P, dS and the dV / dK products of sub-block sb (32 query rows)
-        // from its score and dP accumulators
-        auto finish = [&](const f32x16& sacc, const f32x16& pacc, int sb, bool masked) {
-            const int qs0 = qb + sb * 32;
-            // lane: key kw + l32; entries: query rows qs0 + 8j + 4hi + i
-            const int key = kw + l32;
-            float pv[16], dsv[16];
+        // one tile for one role (KW: key wave), compiled per role so each
+        // keeps only its own operands live
+        auto tile = [&](auto role) {
+            constexpr bool KW = decltype(role)::value;
+            // P (value waves) or dS (key waves) of sub-block sb (32 query
+            // rows) from its score (and dP) accumulators, then the product
+            auto finish = [&](const f32x16& sacc, const f32x16& pacc, int sb, bool masked) {
+                const int qs0 = qb + sb * 32;
+                // lane: key kw + l32; entries: query rows qs0 + 8j + 4hi + i
+                const int key = kw + l32;
+                float xv[16];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float4 L4 = *reinterpret_cast<const float4*>(&Ls[buf][sb * 32 + 8 * j + 4 * hi]);
-                const float4 D4 = *reinterpret_cast<const float4*>(&Dl[buf][sb * 32 + 8 * j + 4 * hi]);
-                const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+                for (int j = 0; j < 4; ++j) {
+                    const float4 L4 = *reinterpret_cast<const float4*>(&Ls[buf][sb * 32 + 8 * j + 4 * hi]);
+                    const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
+                    float Dv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                    if constexpr (KW) {
+                        const float4 D4 = *reinterpret_cast<const float4*>(&Dl[buf][sb * 32 + 8 * j + 4 * hi]);
+                        Dv[0] = D4.x, Dv[1] = D4.y, Dv[2] = D4.z, Dv[3] = D4.w;
+                    }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int q = qs0 + 8 * j + 4 * hi + i;
-                    const bool vis = !masked || (key < S && q < S && (!a.causal || key <= q));
-                    const float p = vis ? exp2_fast(sacc[4 * j + i] * sl2 - Lv[i]) : 0.0f;
-                    pv[4 * j + i] = p;
-                    dsv[4 * j + i] = p * (pacc[4 * j + i] - Dv[i]);
+                    for (int i = 0; i < 4; ++i) {
+                        const int q = qs0 + 8 * j + 4 * hi + i;
+                        const bool vis = !masked || (key < S && q < S && (!a.causal || key <= q));
+                        const float p = vis ? exp2_fast(sacc[4 * j + i] * sl2 - Lv[i]) : 0.0f;
+                        if constexpr (KW)
+                            xv[4 * j + i] = p * (pacc[4 * j + i] - Dv[i]);
+                        else
+                            xv[4 * j + i] = p;
+                    }
                 }
-            }
-            uint4 pa[2], da[2];
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                pa[c] = make_uint4(pack2_bf16(pv[8 * c + 0], pv[8 * c + 1]), pack2_bf16(pv[8 * c + 2], pv[8 * c + 3]),
-                                   pack2_bf16(pv[8 * c + 4], pv[8 * c + 5]), pack2_bf16(pv[8 * c + 6], pv[8 * c + 7]));
-                da[c] = make_uint4(pack2_bf16(dsv[8 * c + 0], dsv[8 * c + 1]), pack2_bf16(dsv[8 * c + 2], dsv[8 * c + 3]),
-                                   pack2_bf16(dsv[8 * c + 4], dsv[8 * c + 5]), pack2_bf16(dsv[8 * c + 6], dsv[8 * c + 7]));
-            }
-#pragma unroll
-            for (int nb = 0; nb < NDB; ++nb)
+                const uint16_t* other = KW ? qs : os;  // dK += dS^T Q, dV += P^T dO
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
-                    dv[nb] = mma(pa[c], tr_frag(os, P, sb * 32 + 16 * c, nb * 32, l32, hi), dv[nb]);
-                    dk[nb] = mma(da[c], tr_frag(qs, P, sb * 32 + 16 * c, nb * 32, l32, hi), dk[nb]);
+                    const uint4 xa = make_uint4(pack2_bf16(xv[8 * c + 0], xv[8 * c + 1]), pack2_bf16(xv[8 * c + 2], xv[8 * c + 3]),
+                                                pack2_bf16(xv[8 * c + 4], xv[8 * c + 5]), pack2_bf16(xv[8 * c + 6], xv[8 * c + 7]));
+#pragma unroll
+                    for (int nb = 0; nb < NDB; ++nb)
+                        acc[nb] = mma(xa, tr_frag(other, P, sb * 32 + 16 * c, nb * 32, l32, hi), acc[nb]);
                 }
-        };
-        // Full tiles (every row and key inside S, and causally every key at
-        // or before every row) take the unmasked path with the four score /
-        // dP chains of both sub-blocks issued together, so that the second
-        // sub-block's products run while the first one's P and dS are formed.
-        const bool full = qb + 63 < S && kw + 31 < S && (!a.causal || qb >= kw + 31);
-        if (full) {
-            f32x16 s0 = f32x16{}, p0 = f32x16{}, s1 = f32x16{}, p1 = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                s0 = mma(row_frag(qs, P, 0, ks, l32, hi), kreg[ks], s0);
-                p0 = mma(row_frag(os, P, 0, ks, l32, hi), vreg[ks], p0);
-                s1 = mma(row_frag(qs, P, 32, ks, l32, hi), kreg[ks], s1);
-                p1 = mma(row_frag(os, P, 32, ks, l32, hi), vreg[ks], p1);
-            }
-            finish(s0, p0, 0, false);
-            finish(s1, p1, 1, false);
-        } else {
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                const int qs0 = qb + sb * 32;
-                // wave-uniform skips: rows past the end, or (causal) every key
-                // of the wave after every row of the block
-                if (qs0 >= S || (a.causal && qs0 + 31 < kw) || kw >= S) continue;
-                f32x16 sacc = f32x16{}, pacc = f32x16{};
+            };
+            auto scores = [&](int sb, f32x16& sacc, f32x16& pacc) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     sacc = mma(row_frag(qs, P, sb * 32, ks, l32, hi), kreg[ks], sacc);
-                    pacc = mma(row_frag(os, P, sb * 32, ks, l32, hi), vreg[ks], pacc);
+                    if constexpr (KW)
+                        pacc = mma(row_frag(os, P, sb * 32, ks, l32, hi), row_frag(vsm, P, kb * 32, ks, l32, hi), pacc);
                 }
-                finish(sacc, pacc, sb, true);
+                // a fence for the scheduler: hoisting the next chain's (or the
+                // product's) fragment loads above this one runs a key wave out
+                // of registers at D = 128
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            // Full tiles (every row and key inside S, and causally every key
+            // at or before every row) take the unmasked path.
+            const bool full = qb + 63 < S && kw + 31 < S && (!a.causal || qb >= kw + 31);
+            if (full) {
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+                    f32x16 sacc = f32x16{}, pacc = f32x16{};
+                    scores(sb, sacc, pacc);
+                    finish(sacc, pacc, sb, false);
+                }
+            } else {
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+                    const int qs0 = qb + sb * 32;
+                    // wave-uniform skips: rows past the end, or (causal) every
+                    // key of the block after every row of the sub-block
+                    if (qs0 >= S || (a.causal && qs0 + 31 < kw) || kw >= S) continue;
+                    f32x16 sacc = f32x16{}, pacc = f32x16{};
+                    scores(sb, sacc, pacc);
+                    finish(sacc, pacc, sb, true);
+                }
             }
-        }
+        };
+        if (kwave)
+            tile(std::true_type{});
+        else
+            tile(std::false_type{});
         if (it + 1 < nit) store_tile(buf ^ 1);
     }
 
@@ -383,18 +405,20 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdArgs a)
 #pragma unroll
     for (int which = 0; which < 2; ++which) {  // 0: keys, 1: values
         __syncthreads();
+        if (kwave == (which == 0)) {
 #pragma unroll
-        for (int nb = 0; nb < NDB; ++nb)
+            for (int nb = 0; nb < NDB; ++nb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float x = which == 0 ? dk[nb][4 * j + i] * a.scale : dv[nb][4 * j + i];
-                    st[(wave * 32 + 8 * j + 4 * hi + i) * SP + nb * 32 + l32] = x;
-                }
+                    for (int i = 0; i < 4; ++i) {
+                        const float x = which == 0 ? acc[nb][4 * j + i] * a.scale : acc[nb][4 * j + i];
+                        st[(kb * 32 + 8 * j + 4 * hi + i) * SP + nb * 32 + l32] = x;
+                    }
+        }
         __syncthreads();
         const OutView o1 = which == 0 ? a.dk1 : a.dv1;
-        for (int e = tid; e < kKeysPerWg * CPR; e += kBwdThreads) {
+        for (int e = tid; e < kKeysPerWg * CPR; e += kDkvThreads) {
             const int r = e / CPR, c = e - (e / CPR) * CPR;
             const int key = k0 + r;
             if (key >= S) continue;
@@ -425,7 +449,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(const BwdArgs a)
             // (values: dVf * V1, dVf * Vn), one channel per thread
             const View& s1 = which == 0 ? a.k1 : a.v1;
             const View& sn = which == 0 ? a.kn : a.vn;
-            for (int d = tid; d < D; d += kBwdThreads) {
+            for (int d = tid; d < D; d += kDkvThreads) {
                 float acc1 = 0.0f, accn = 0.0f;
                 const int nr = min(kKeysPerWg, S - k0);
                 for (int r = 0; r < nr; ++r) {
@@ -662,8 +686,8 @@ int launch_bwd3(const BwdArgs& a, hipStream_t st)
     hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, a);
     int rc = (int)hipGetLastError();
     if (rc) return rc;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, FUSED, G>), dim3((unsigned)(a.B * a.Hkv * a.nkt)), dim3(kBwdThreads), 0, st,
-                       a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, FUSED, G>), dim3((unsigned)(a.B * a.Hkv * a.nkt)), dim3(kDkvThreads), 0,
+                       st, a);
     if ((rc = (int)hipGetLastError())) return rc;
     constexpr int HPW = G < kDqWaves ? G : kDqWaves;
     constexpr int BM = (kDqWaves / HPW) * 32;
