@@ -60,7 +60,8 @@ class fkv_fusion(ctypes.Structure):
 
 
 EXPORTS = ["fkv_abi_version", "fkv_status_string", "fkv_last_error", "fkv_decode_workspace_size",
-           "fkv_decode", "fkv_lite_decode", "fkv_prefill", "fkv_lite_prefill", "fkv_check_tied",
+           "fkv_decode", "fkv_lite_decode", "fkv_prefill_workspace_size", "fkv_prefill", "fkv_lite_prefill",
+           "fkv_check_tied",
            "fkv_kivi_codes_bytes", "fkv_kivi_meta_bytes", "fkv_kivi_quantize", "fkv_kivi_decode",
            "fkv_kivi_lite_decode", "fkv_backward_workspace_size", "fkv_prefill_backward",
            "fkv_lite_prefill_backward"]
@@ -92,11 +93,13 @@ def load_library(path: str = LIB_PATH):
     lib.fkv_lite_decode.restype = ctypes.c_int
     lib.fkv_lite_decode.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, vp, vp, vp, vp,
                                     ctypes.c_size_t, vp]
+    lib.fkv_prefill_workspace_size.restype = ctypes.c_size_t
+    lib.fkv_prefill_workspace_size.argtypes = [P(fkv_params)]
     lib.fkv_prefill.restype = ctypes.c_int
     lib.fkv_prefill.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, fkv_cache, fkv_cache,
-                                P(fkv_fusion), vp, vp, vp]
+                                P(fkv_fusion), vp, vp, vp, ctypes.c_size_t, vp]
     lib.fkv_lite_prefill.restype = ctypes.c_int
-    lib.fkv_lite_prefill.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, vp, vp, vp]
+    lib.fkv_lite_prefill.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, vp, vp, vp, ctypes.c_size_t, vp]
     lib.fkv_check_tied.restype = ctypes.c_int
     lib.fkv_check_tied.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float]
     lib.fkv_kivi_codes_bytes.restype = ctypes.c_size_t
@@ -120,7 +123,7 @@ def load_library(path: str = LIB_PATH):
     lib.fkv_lite_prefill_backward.restype = ctypes.c_int
     lib.fkv_lite_prefill_backward.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, vp, vp, vp, vp, fkv_grad,
                                               fkv_grad, vp, ctypes.c_size_t, vp]
-    if lib.fkv_abi_version() != 4:
+    if lib.fkv_abi_version() != 5:
         raise RuntimeError("libfusedkv ABI version mismatch")
     _lib = lib
     return lib
@@ -213,22 +216,38 @@ def fkv_lite_decode(q, k_src, v_src, *, out, workspace, lse=None, seqlens_k=None
                                _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
 
 
-def fkv_prefill(q, k1, kn, v1, vn, weights, *, out, lse=None, causal=True, softmax_scale=0.0, stream=None):
+def prefill_workspace(q: torch.Tensor, k: torch.Tensor) -> torch.Tensor:
+    """A fuse-once workspace for prefill calls with these shapes."""
+    n = load_library().fkv_prefill_workspace_size(ctypes.byref(make_params(q, k, causal=True)))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+
+
+def _ws(workspace):
+    return (None, 0) if workspace is None else (_dev(workspace, "workspace"), workspace.numel())
+
+
+def fkv_prefill(q, k1, kn, v1, vn, weights, *, out, lse=None, causal=True, softmax_scale=0.0, workspace=None,
+                stream=None):
     """FusedKV prefill of one reconstruction layer (bf16).  q, out:
-    [B, S, Hq, D]; caches [B, S, Hkv, D]."""
+    [B, S, Hq, D]; caches [B, S, Hkv, D].  workspace: a uint8 tensor from
+    prefill_workspace (fuse each tile once) or None (fuse in the kernel)."""
     lib = load_library()
     p = make_params(q, k1, softmax_scale=softmax_scale, causal=causal)
     f = _fusion(weights)
+    ws, nws = _ws(workspace)
     _check(lib.fkv_prefill(ctypes.byref(p), _dev(q, "q"), cache_view(k1), cache_view(kn), cache_view(v1),
-                           cache_view(vn), ctypes.byref(f), _dev(out, "out"), _dev(lse, "lse"), _stream(stream)))
+                           cache_view(vn), ctypes.byref(f), _dev(out, "out"), _dev(lse, "lse"), ws, nws,
+                           _stream(stream)))
 
 
-def fkv_lite_prefill(q, k_src, v_src, *, out, lse=None, causal=True, softmax_scale=0.0, stream=None):
+def fkv_lite_prefill(q, k_src, v_src, *, out, lse=None, causal=True, softmax_scale=0.0, workspace=None,
+                     stream=None):
     """Single-source prefill (FusedKV-Lite or the plain control)."""
     lib = load_library()
     p = make_params(q, k_src, softmax_scale=softmax_scale, causal=causal)
+    ws, nws = _ws(workspace)
     _check(lib.fkv_lite_prefill(ctypes.byref(p), _dev(q, "q"), cache_view(k_src), cache_view(v_src),
-                                _dev(out, "out"), _dev(lse, "lse"), _stream(stream)))
+                                _dev(out, "out"), _dev(lse, "lse"), ws, nws, _stream(stream)))
 
 
 def fkv_check_tied(k_w: torch.Tensor, pairing: str = "interleaved", tol: float = 0.0) -> bool:

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define FKV_ABI_VERSION 4
+#define FKV_ABI_VERSION 5
 
 typedef enum {
     FKV_SUCCESS = 0,
@@ -170,6 +170,14 @@ fkv_status fkv_lite_decode(const fkv_params* params, const void* q,
                            void* stream);
 
 /*
+ * Bytes of the optional fkv_prefill / fkv_lite_prefill workspace for
+ * `params`: the layer's fused keys and values as IEEE binary16,
+ * 4 * B * H_kv * S64 * D bytes plus alignment, S64 = seqlen_k rounded up to a
+ * multiple of 64.  Returns 0 when params is invalid.
+ */
+size_t fkv_prefill_workspace_size(const fkv_params* params);
+
+/*
  * fkv_prefill -- attention of a FusedKV reconstruction layer over a whole
  * prompt (S_q == S_k), bfloat16 data.  With causal = 1, query row p sees keys
  * t <= p.  Key and value tiles are fused in float32 and rounded once to IEEE
@@ -180,23 +188,36 @@ fkv_status fkv_lite_decode(const fkv_params* params, const void* q,
  * (Eqs. (4)-(5)) and "Prefill improves while kernel throughput falls"
  * (the fused kernel's throughput, paper Fig. 4).
  *
- *   q     device [B, S, H_q, D] bfloat16
- *   out   device [B, S, H_q, D] bfloat16
- *   lse   device float32 [B, H_q, S] or NULL
+ * Without a workspace every attention workgroup fuses the key and value
+ * tiles it reads, inside the kernel ([Notes] section 2.3).  With one, a first
+ * kernel fuses each tile once into the workspace (binary16, the same
+ * float32 fusion rounded once) and the attention kernel reads the fused
+ * tiles: the prompt's tiles are otherwise fused once per query tile that
+ * sees them.  The workspace holds only this call's data; calls that may run
+ * concurrently need separate workspaces.
+ *
+ *   q          device [B, S, H_q, D] bfloat16
+ *   out        device [B, S, H_q, D] bfloat16
+ *   lse        device float32 [B, H_q, S] or NULL
+ *   workspace  device, 256-byte aligned, >= fkv_prefill_workspace_size(params)
+ *              bytes; or NULL (workspace_bytes ignored) to fuse in the kernel.
+ *              A shorter workspace returns FKV_ERROR_WORKSPACE.
  */
 fkv_status fkv_prefill(const fkv_params* params, const void* q,
                        fkv_cache k1, fkv_cache kn, fkv_cache v1, fkv_cache vn,
                        const fkv_fusion* fusion, void* out, float* lse,
-                       void* stream);
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * fkv_lite_prefill -- prefill over one key cache and one value cache
  * (FusedKV-Lite with (K^n, V^1), or the plain control with a layer's own
- * caches).  Arguments otherwise as fkv_prefill.
+ * caches).  Arguments otherwise as fkv_prefill; with a workspace the first
+ * kernel converts the tiles to binary16 once.
  */
 fkv_status fkv_lite_prefill(const fkv_params* params, const void* q,
                             fkv_cache k_src, fkv_cache v_src, void* out,
-                            float* lse, void* stream);
+                            float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * fkv_check_tied -- host-side check that key fusion weights are tied on RoPE

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib, B):
     assert set(names) == set(B.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.fkv_abi_version() == 4
+    assert lib.fkv_abi_version() == 5
     for s in range(5):
         assert lib.fkv_status_string(s)
     assert lib.fkv_status_string(99) == b"unknown status"
@@ -71,11 +71,11 @@ def _decode(lib, B, p, q=FAKE, caches=None, fusion="default", ws_bytes=None, ws=
                           ctypes.byref(f) if f is not None else None, seqlens, out, lse, ws, ws_bytes, None)
 
 
-def _prefill(lib, B, p, q=FAKE, caches=None, fusion="default"):
+def _prefill(lib, B, p, q=FAKE, caches=None, fusion="default", ws=None, ws_bytes=0):
     c = caches or [_cache(B, p.head_dim, p.num_kv_heads, p.seqlen_k)] * 4
     f = _fusion(B) if fusion == "default" else fusion
     return lib.fkv_prefill(ctypes.byref(p), q, c[0], c[1], c[2], c[3],
-                           ctypes.byref(f) if f is not None else None, FAKE, None, None)
+                           ctypes.byref(f) if f is not None else None, FAKE, None, ws, ws_bytes, None)
 
 
 def test_decode_validation_codes(lib, B):
@@ -196,7 +196,30 @@ def test_prefill_validation_codes(lib, B):
     assert _prefill(lib, B, _params(B, sq=64, sk=64, hq=128, hkv=2)) == UNS  # G = 64: decode only
     p = _params(B, sq=64, sk=64)
     c = _cache(B)
-    assert lib.fkv_lite_prefill(ctypes.byref(p), FAKE, c, B.fkv_cache(0, 0, 64, 0), FAKE, None, None) == INV
+    assert lib.fkv_lite_prefill(ctypes.byref(p), FAKE, c, B.fkv_cache(0, 0, 64, 0), FAKE, None, None, 0,
+                                None) == INV
+    # fuse-once workspace: too short or misaligned
+    WS = B.FKV_ERROR_WORKSPACE
+    need = lib.fkv_prefill_workspace_size(ctypes.byref(p))
+    assert _prefill(lib, B, p, ws=FAKE, ws_bytes=need - 1) == WS
+    assert _prefill(lib, B, p, ws=FAKE + 16, ws_bytes=need) == WS
+    assert lib.fkv_lite_prefill(ctypes.byref(p), FAKE, c, c, FAKE, None, FAKE, need - 1, None) == WS
+    # an empty prompt needs no workspace and launches nothing
+    assert _prefill(lib, B, _params(B, batch=0, sq=64, sk=64), ws=FAKE, ws_bytes=0) == B.FKV_SUCCESS
+
+
+def test_prefill_workspace_size(lib, B):
+    """Binary16 fused keys [B, Hkv, S64, D], then the value tiles at the next
+    256-byte boundary: 2 * B * Hkv * S64 * D * 2 bytes in all."""
+    assert lib.fkv_prefill_workspace_size(None) == 0
+    assert lib.fkv_prefill_workspace_size(ctypes.byref(_params(B, sq=1, sk=64))) == 0   # not a prefill
+    assert lib.fkv_prefill_workspace_size(ctypes.byref(_params(B, batch=0, sq=64, sk=64))) == 0
+    for batch, s, hkv, d in ((2, 64, 2, 64), (1, 100, 3, 80), (4, 8192, 8, 128), (1, 1, 1, 96)):
+        s64 = (s + 63) // 64 * 64
+        half = batch * hkv * s64 * d * 2
+        want = (half + 255) // 256 * 256 + half
+        p = _params(B, batch=batch, sq=s, sk=s, hq=2 * hkv, hkv=hkv, d=d)
+        assert lib.fkv_prefill_workspace_size(ctypes.byref(p)) == want
 
 
 def _grad(B, d=64, hkv=2, sk=64, ptr=FAKE):

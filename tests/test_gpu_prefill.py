@@ -1,6 +1,7 @@
 """GPU parity of fkv_prefill / fkv_lite_prefill (bf16 MFMA) against the fp64
-oracle, through the C ABI.  Every test prints its case before touching the
-GPU."""
+oracle, through the C ABI, with the tiles fused inside the attention kernel
+(no workspace) and fused once into a workspace first.  Every test prints its
+case before touching the GPU."""
 import numpy as np
 import pytest
 import torch
@@ -13,27 +14,39 @@ DEV = "cuda:0"
 TOL = 1e-2
 
 
-def run_prefill(L, fused=True, causal=True, single=("kn", "v1")):
+def poisoned_workspace(L):
+    """A fuse-once workspace filled with NaN bytes, so that any position the
+    first kernel fails to write (padding rows included) shows up."""
+    ws = binding.prefill_workspace(L.q, L.k1)
+    ws.fill_(0xFF)
+    return ws
+
+
+def run_prefill(L, fused=True, causal=True, single=("kn", "v1"), ws=False):
     B, S, Hq, D = L.q.shape
     out = torch.full_like(L.q, float("nan"))
     lse = torch.full((B, Hq, S), float("nan"), dtype=torch.float32, device=DEV)
+    w = poisoned_workspace(L) if ws is True else (None if ws is False or ws is None else ws)
     if fused:
-        binding.fkv_prefill(L.q, L.k1, L.kn, L.v1, L.vn, L.weights, out=out, lse=lse, causal=causal)
+        binding.fkv_prefill(L.q, L.k1, L.kn, L.v1, L.vn, L.weights, out=out, lse=lse, causal=causal, workspace=w)
     else:
         binding.fkv_lite_prefill(L.q, getattr(L, single[0]), getattr(L, single[1]), out=out, lse=lse,
-                                 causal=causal)
+                                 causal=causal, workspace=w)
     torch.cuda.synchronize()
     return out, lse
 
 
-def check(L, fused=True, causal=True, single=("kn", "v1")):
+def check(L, fused=True, causal=True, single=("kn", "v1"), both=True):
+    """The oracle once; the kernel without a workspace and (both=True) with
+    a fuse-once workspace."""
     B, S, Hq, D = L.q.shape
-    out, lse = run_prefill(L, fused, causal, single)
     ro, rl = oracle_layer(L, fused=fused, causal=causal, single=single)
-    e = rel_err(gpu_rows(out, B, Hq, S, D), ro)
-    el = lse_err(lse.cpu().numpy().reshape(-1), rl)
-    say("  err=%.3e lse_err=%.3e" % (e, el))
-    assert e <= TOL and el <= TOL, (e, el)
+    for ws in ((False, True) if both else (False,)):
+        out, lse = run_prefill(L, fused, causal, single, ws=ws)
+        e = rel_err(gpu_rows(out, B, Hq, S, D), ro)
+        el = lse_err(lse.cpu().numpy().reshape(-1), rl)
+        say("  fuse_once=%s err=%.3e lse_err=%.3e" % (ws, e, el))
+        assert e <= TOL and el <= TOL, (ws, e, el)
     return out, lse
 
 
@@ -69,18 +82,47 @@ def test_layouts(layout):
     check(L, fused=True)
 
 
-def test_selector_weights_equal_lite_bitwise():
+@pytest.mark.parametrize("ws", [False, True])
+def test_selector_weights_equal_lite_bitwise(ws):
     """(0, 1, 1, 0) weights give K~ = K^n and V~ = V^1 exactly (also after the
-    bf16 rounding of the fused tiles), so the fused kernel must equal the Lite
-    kernel bit for bit."""
-    say("prefill selector weights vs lite")
+    binary16 rounding of the fused tiles), so the fused kernel must equal the
+    Lite kernel bit for bit."""
+    say("prefill selector weights vs lite fuse_once=%s" % ws)
     L = inputs.make_layer(1, 333, 333, 8, 4, 80, torch.bfloat16, 600, DEV, decode=False)
     z = torch.zeros_like(L.weights[0])
     o = torch.ones_like(L.weights[0])
     L.weights = (z, o, o, z)
-    of, lf = run_prefill(L, fused=True)
-    ol, ll = run_prefill(L, fused=False)
+    of, lf = run_prefill(L, fused=True, ws=ws)
+    ol, ll = run_prefill(L, fused=False, ws=ws)
     assert torch.equal(of, ol) and torch.equal(lf, ll)
+
+
+@pytest.mark.parametrize("D", [64, 96, 128])
+def test_fuse_once_single_source_equals_in_kernel_bitwise(D):
+    """Single-source tiles convert from bf16 to binary16 exactly, so staging
+    them once in the workspace or in the kernel gives the same operands and
+    the same results bit for bit (S = 300 leaves a ragged last tile)."""
+    say("prefill lite fuse-once vs in-kernel D=%d S=300 G=2" % D)
+    L = inputs.make_layer(2, 300, 300, 8, 4, D, torch.bfloat16, 650 + D, DEV, decode=False)
+    o0, l0 = run_prefill(L, fused=False, ws=False)
+    o1, l1 = run_prefill(L, fused=False, ws=True)
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+
+
+def test_fuse_once_workspace_reused_for_a_smaller_prompt():
+    """One workspace serves a call and then a call with a shorter prompt and
+    fewer heads; the second call's tiles overwrite what it reads."""
+    say("prefill fuse-once workspace reuse: S=520 Hkv=4 then S=130 Hkv=2 (D=96)")
+    big = inputs.make_layer(1, 520, 520, 8, 4, 96, torch.bfloat16, 660, DEV, decode=False)
+    ws = poisoned_workspace(big)
+    for L in (big, inputs.make_layer(1, 130, 130, 4, 2, 96, torch.bfloat16, 661, DEV, decode=False)):
+        B, S, Hq, D = L.q.shape
+        out, lse = run_prefill(L, fused=True, ws=ws)
+        ro, rl = oracle_layer(L, fused=True, causal=True)
+        e = rel_err(gpu_rows(out, B, Hq, S, D), ro)
+        el = lse_err(lse.cpu().numpy().reshape(-1), rl)
+        say("  S=%d err=%.3e lse_err=%.3e" % (S, e, el))
+        assert e <= TOL and el <= TOL
 
 
 def test_vanilla_control_on_own_caches():
@@ -108,15 +150,20 @@ def _full_size(B, S, Hq, Hkv, D, seed):
     L = inputs.make_layer(B, S, S, Hq, Hkv, D, torch.bfloat16, seed, DEV, decode=False)
     rng = np.random.default_rng(seed)
     rows = _sample_rows(B, Hq, S, 256 // (Hq // Hkv), rng)
+    ws = binding.prefill_workspace(L.q, L.k1)
     for fused in (True, False):
-        out, lse = run_prefill(L, fused=fused)
-        assert torch.isfinite(out).all() and torch.isfinite(lse).all()
         ro, rl = oracle_layer(L, fused=fused, causal=True, rows=rows)
-        got = gpu_rows(out, B, Hq, S, D)[rows]
-        e = rel_err(got, ro)
-        el = lse_err(lse.cpu().numpy().reshape(-1)[rows], rl)
-        say("  fused=%s rows=%d err=%.3e lse_err=%.3e" % (fused, rows.size, e, el))
-        assert e <= TOL and el <= TOL
+        for w in (None, ws):
+            if w is not None:
+                w.fill_(0xFF)
+            out, lse = run_prefill(L, fused=fused, ws=w if w is not None else False)
+            assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+            got = gpu_rows(out, B, Hq, S, D)[rows]
+            e = rel_err(got, ro)
+            el = lse_err(lse.cpu().numpy().reshape(-1)[rows], rl)
+            say("  fused=%s fuse_once=%s rows=%d err=%.3e lse_err=%.3e" % (fused, w is not None, rows.size, e, el))
+            assert e <= TOL and el <= TOL
+    del ws
     del L
     torch.cuda.empty_cache()
 
