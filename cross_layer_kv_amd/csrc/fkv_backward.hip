@@ -34,9 +34,12 @@
 //      four source gradients and its partial column sums for the weight
 //      gradients.
 //   3. query tiles: a workgroup of 8 waves owns 256 (query row, head)
-//      columns and walks the fused key/value tiles (built in LDS once per
-//      workgroup) accumulating dQ.  dQ is thus written once, with no float
-//      atomics, and every result is run-to-run deterministic.
+//      columns and walks 64-key tiles staged in LDS, accumulating dQ.  For
+//      four sources a first kernel fuses every key and value row once into
+//      bf16 rows in the workspace, which this kernel reads as one source
+//      (every query tile would otherwise fuse the same tiles again).  dQ is
+//      thus written once, with no float atomics, and every result is
+//      run-to-run deterministic.
 //   4. reduce: the weight-gradient partials summed in a fixed order.
 //
 // Operand layouts (v_mfma_f32_32x32x16_bf16, A 32x16, B 16x32, C 32x32): a
@@ -465,7 +468,9 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
 }
 
 // ---- 3. query tiles: dQ ----
-template <int D, bool FUSED, int G>
+// Reads one bf16 key and one value source through a.k1 / a.v1: the Lite
+// sources, or the rows bwd_prefuse_kernel fused.
+template <int D, int G>
 __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const BwdArgs a)
 {
     constexpr int DP = (D + 31) / 32 * 32;
@@ -480,7 +485,6 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const BwdArgs a)
     constexpr int BM = RB * 32;              // query rows per workgroup
 
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];  // [buf][K~, V~][row][P]
-    __shared__ __attribute__((aligned(16))) float s_w[FUSED ? 4 : 1][D];  // a, a', b, b' of this KV head
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -503,12 +507,6 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const BwdArgs a)
         for (int i = tid; i < 2 * 2 * kKTile * (DP - D); i += kDqThreads) {
             const int r = i / (DP - D), c = i - r * (DP - D);
             smem[r * P + D + c] = 0;
-        }
-    }
-    if constexpr (FUSED) {
-        for (int i = tid; i < 4 * D; i += kDqThreads) {
-            const float* w = i < D ? a.kw1 : (i < 2 * D ? a.kwn : (i < 3 * D ? a.vw1 : a.vwn));
-            s_w[i / D][i - (i / D) * D] = w[(int64_t)g * D + i - (i / D) * D];
         }
     }
 
@@ -542,8 +540,7 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const BwdArgs a)
 
     constexpr int NITEM = kKTile * CPR;
     constexpr int NPASS = (NITEM + kDqThreads - 1) / kDqThreads;
-    constexpr int NSRC = FUSED ? 4 : 2;
-    uint4 xr[NSRC][NPASS];
+    uint4 xr[2][NPASS];
     auto load_tile = [&](int t) {
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
@@ -551,15 +548,11 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const BwdArgs a)
             const int r = e / CPR, c = e - (e / CPR) * CPR;
             const int key = t * kKTile + r;
             const bool ok = e < NITEM && key < S;
-#pragma unroll
-            for (int s = 0; s < NSRC; ++s) xr[s][p] = make_uint4(0u, 0u, 0u, 0u);
+            xr[0][p] = make_uint4(0u, 0u, 0u, 0u);
+            xr[1][p] = xr[0][p];
             if (ok) {
                 xr[0][p] = *reinterpret_cast<const uint4*>(row_ptr(a.k1, b, key, g) + c * 8);
                 xr[1][p] = *reinterpret_cast<const uint4*>(row_ptr(a.v1, b, key, g) + c * 8);
-                if constexpr (FUSED) {
-                    xr[2][p] = *reinterpret_cast<const uint4*>(row_ptr(a.kn, b, key, g) + c * 8);
-                    xr[3][p] = *reinterpret_cast<const uint4*>(row_ptr(a.vn, b, key, g) + c * 8);
-                }
             }
         }
     };
@@ -571,18 +564,8 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const BwdArgs a)
             const int e = tid + p * kDqThreads;
             if (e >= NITEM) continue;
             const int r = e / CPR, c = e - (e / CPR) * CPR;
-            uint4 kf = xr[0][p], vf = xr[1][p];
-            if constexpr (FUSED) {
-                float w1[8], wn[8];
-                load8f(&s_w[0][c * 8], w1);
-                load8f(&s_w[1][c * 8], wn);
-                kf = fuse8_bf16(xr[0][p], xr[2][p], w1, wn);
-                load8f(&s_w[2][c * 8], w1);
-                load8f(&s_w[3][c * 8], wn);
-                vf = fuse8_bf16(xr[1][p], xr[3][p], w1, wn);
-            }
-            *reinterpret_cast<uint4*>(kt_ + r * P + c * 8) = kf;
-            *reinterpret_cast<uint4*>(vt_ + r * P + c * 8) = vf;
+            *reinterpret_cast<uint4*>(kt_ + r * P + c * 8) = xr[0][p];
+            *reinterpret_cast<uint4*>(vt_ + r * P + c * 8) = xr[1][p];
         }
     };
 
@@ -679,6 +662,36 @@ __global__ __launch_bounds__(256) void bwd_wreduce_kernel(const BwdArgs a)
     }
 }
 
+// ---- fused key and value rows for the query-tile kernel ----
+// Every query-tile workgroup walks all the keys it sees, so the four-source
+// tiles are fused once here (the same float32 fusion and bfloat16 rounding
+// as the key-tile kernel's) and the query-tile kernel reads them as a
+// single source.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prefuse_kernel(const BwdArgs a)
+{
+    constexpr int CPR = D / 8;
+    const int64_t items = (int64_t)a.B * a.Hkv * a.S * CPR;
+    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < items; i += (int64_t)gridDim.x * 256) {
+        const int c = (int)(i % CPR);
+        const int64_t row = i / CPR;  // ((b * Hkv + g) * S + t)
+        const int t = (int)(row % a.S);
+        const int64_t unit = row / a.S;
+        const int b = (int)(unit / a.Hkv), g = (int)(unit % a.Hkv);
+        float w1[8], wn[8];
+        load8f(a.kw1 + g * D + c * 8, w1);
+        load8f(a.kwn + g * D + c * 8, wn);
+        const uint4 k1 = *reinterpret_cast<const uint4*>(row_ptr(a.k1, b, t, g) + c * 8);
+        const uint4 kn = *reinterpret_cast<const uint4*>(row_ptr(a.kn, b, t, g) + c * 8);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.kf) + row * D + c * 8) = fuse8_bf16(k1, kn, w1, wn);
+        load8f(a.vw1 + g * D + c * 8, w1);
+        load8f(a.vwn + g * D + c * 8, wn);
+        const uint4 v1 = *reinterpret_cast<const uint4*>(row_ptr(a.v1, b, t, g) + c * 8);
+        const uint4 vn = *reinterpret_cast<const uint4*>(row_ptr(a.vn, b, t, g) + c * 8);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.vf) + row * D + c * 8) = fuse8_bf16(v1, vn, w1, wn);
+    }
+}
+
 template <int D, bool FUSED, int G>
 int launch_bwd3(const BwdArgs& a, hipStream_t st)
 {
@@ -692,8 +705,22 @@ int launch_bwd3(const BwdArgs& a, hipStream_t st)
     constexpr int HPW = G < kDqWaves ? G : kDqWaves;
     constexpr int BM = (kDqWaves / HPW) * 32;
     const int nqt = (a.S + BM - 1) / BM;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, FUSED, G>), dim3((unsigned)(a.B * a.Hkv * (G / HPW) * nqt)),
-                       dim3(kDqThreads), 0, st, a);
+    const dim3 qgrid((unsigned)(a.B * a.Hkv * (G / HPW) * nqt));
+    if constexpr (FUSED) {
+        // fuse once, then the single-source query-tile kernel over the fused rows
+        const int64_t items = (int64_t)a.B * a.Hkv * a.S * (D / 8);
+        const int64_t blocks = (items + 255) / 256;
+        hipLaunchKernelGGL(bwd_prefuse_kernel<D>, dim3((unsigned)(blocks < (1 << 20) ? blocks : (1 << 20))),
+                           dim3(256), 0, st, a);
+        if ((rc = (int)hipGetLastError())) return rc;
+        BwdArgs f = a;
+        const int64_t slab = (int64_t)a.S * D;
+        f.k1 = View{a.kf, a.Hkv * slab, D, slab};
+        f.v1 = View{a.vf, a.Hkv * slab, D, slab};
+        hipLaunchKernelGGL((bwd_dq_kernel<D, G>), qgrid, dim3(kDqThreads), 0, st, f);
+    } else {
+        hipLaunchKernelGGL((bwd_dq_kernel<D, G>), qgrid, dim3(kDqThreads), 0, st, a);
+    }
     if ((rc = (int)hipGetLastError())) return rc;
     if constexpr (FUSED) {
         hipLaunchKernelGGL(bwd_wreduce_kernel, dim3((unsigned)(4 * a.Hkv)), dim3(256), 0, st, a);

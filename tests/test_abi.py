@@ -257,9 +257,10 @@ def test_backward_validation_codes(lib, B):
     p = _params(B, **ok)
     need = lib.fkv_backward_workspace_size(ctypes.byref(p))
     # LSE*log2(e) and rowsum(dO*O) rows (B*Hq*S floats each, 256-byte
-    # rounded) and the weight-gradient partials (B*Hkv key tiles x 4 x D)
+    # rounded), the weight-gradient partials (B*Hkv key tiles x 4 x D) and
+    # the fused key and value rows (B*Hkv*S*D bf16 each)
     rows = 2 * 4 * 64 * 4
-    assert need == 2 * (-(-rows // 256) * 256) + 2 * 2 * 1 * 4 * 64 * 4
+    assert need == 2 * (-(-rows // 256) * 256) + 2 * 2 * 1 * 4 * 64 * 4 + 2 * (2 * 2 * 64 * 64 * 2)
     assert _bwd(lib, B, p, ws_bytes=need - 1) == WS
     assert _bwd(lib, B, p, ws=FAKE + 64) == WS
     assert _bwd(lib, B, p, ws=None) == WS
