@@ -218,35 +218,21 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
     // waves also stage the block's fused values in LDS ----
     uint4 kreg[KS];
     {
+        // four sources: the rows bwd_prefuse_kernel fused, as one source
+        const View ks_ = FUSED ? View{a.kf, (int64_t)a.Hkv * S * D, D, (int64_t)S * D} : a.k1;
+        const View vs_ = FUSED ? View{a.vf, (int64_t)a.Hkv * S * D, D, (int64_t)S * D} : a.v1;
         const int key = kw + l32;
         const bool ok = key < S;
-        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int ch = ks * 16 + hi * 8;
-            uint4 k1 = z, kn = z, v1 = z, vn = z;
+            uint4 k = make_uint4(0u, 0u, 0u, 0u), v = k;
             if (ok) {
-                k1 = *reinterpret_cast<const uint4*>(row_ptr(a.k1, b, key, g) + ch);
-                if constexpr (FUSED) kn = *reinterpret_cast<const uint4*>(row_ptr(a.kn, b, key, g) + ch);
-                if (kwave) {
-                    v1 = *reinterpret_cast<const uint4*>(row_ptr(a.v1, b, key, g) + ch);
-                    if constexpr (FUSED) vn = *reinterpret_cast<const uint4*>(row_ptr(a.vn, b, key, g) + ch);
-                }
+                k = *reinterpret_cast<const uint4*>(row_ptr(ks_, b, key, g) + ch);
+                if (kwave) v = *reinterpret_cast<const uint4*>(row_ptr(vs_, b, key, g) + ch);
             }
-            if constexpr (FUSED) {
-                float w1[8], wn[8];
-                load8f(a.kw1 + g * D + ch, w1);
-                load8f(a.kwn + g * D + ch, wn);
-                kreg[ks] = fuse8_bf16(k1, kn, w1, wn);
-                if (kwave) {
-                    load8f(a.vw1 + g * D + ch, w1);
-                    load8f(a.vwn + g * D + ch, wn);
-                    *reinterpret_cast<uint4*>(vsm + (kb * 32 + l32) * P + ch) = fuse8_bf16(v1, vn, w1, wn);
-                }
-            } else {
-                kreg[ks] = k1;
-                if (kwave) *reinterpret_cast<uint4*>(vsm + (kb * 32 + l32) * P + ch) = v1;
-            }
+            kreg[ks] = k;
+            if (kwave) *reinterpret_cast<uint4*>(vsm + (kb * 32 + l32) * P + ch) = v;
         }
     }
 
@@ -449,19 +435,59 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
         }
         if constexpr (FUSED) {
             // column sums over this tile's keys of dKf * K1 and dKf * Kn
-            // (values: dVf * V1, dVf * Vn), one channel per thread
+            // (values: dVf * V1, dVf * Vn): a thread takes 8 channels of 4
+            // keys (its 8 source loads in flight together), the 32 key
+            // groups' partials meet in the idle value tile, and one thread
+            // per (source, channel) adds them in a fixed order
+            constexpr int NCH = D / 8;
+            constexpr int KPT = 4, NKG = kKeysPerWg / KPT;
+            static_assert(NKG * NCH <= kDkvThreads, "one (key group, chunk) item per thread");
+            static_assert(NKG * 2 * D * 4 <= kKeysPerWg * P * 2, "partials fit in the value tile");
+            float* red = reinterpret_cast<float*>(vsm);  // [NKG][2][D]
             const View& s1 = which == 0 ? a.k1 : a.v1;
             const View& sn = which == 0 ? a.kn : a.vn;
-            for (int d = tid; d < D; d += kDkvThreads) {
-                float acc1 = 0.0f, accn = 0.0f;
-                const int nr = min(kKeysPerWg, S - k0);
-                for (int r = 0; r < nr; ++r) {
-                    const float x = st[r * SP + d];
-                    acc1 += x * bf16_lo(row_ptr(s1, b, k0 + r, g)[d]);
-                    accn += x * bf16_lo(row_ptr(sn, b, k0 + r, g)[d]);
+            if (tid < NKG * NCH) {
+                const int kg = tid / NCH, c8 = tid - (tid / NCH) * NCH;
+                uint4 u1[KPT], un[KPT];
+#pragma unroll
+                for (int r = 0; r < KPT; ++r) {
+                    const int key = k0 + kg * KPT + r;
+                    u1[r] = make_uint4(0u, 0u, 0u, 0u);
+                    un[r] = u1[r];
+                    if (key < S) {
+                        u1[r] = *reinterpret_cast<const uint4*>(row_ptr(s1, b, key, g) + c8 * 8);
+                        un[r] = *reinterpret_cast<const uint4*>(row_ptr(sn, b, key, g) + c8 * 8);
+                    }
                 }
-                part[(2 * which + 0) * D + d] = acc1;
-                part[(2 * which + 1) * D + d] = accn;
+                float acc1[8], accn[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc1[e] = accn[e] = 0.0f;
+#pragma unroll
+                for (int r = 0; r < KPT; ++r) {
+                    float x[8];
+                    load8f(st + (kg * KPT + r) * SP + c8 * 8, x);  // rows past S hold zeros
+                    const uint32_t w1[4] = {u1[r].x, u1[r].y, u1[r].z, u1[r].w};
+                    const uint32_t wn[4] = {un[r].x, un[r].y, un[r].z, un[r].w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        acc1[2 * k] = fmaf(x[2 * k], bf16_lo(w1[k]), acc1[2 * k]);
+                        acc1[2 * k + 1] = fmaf(x[2 * k + 1], bf16_hi(w1[k]), acc1[2 * k + 1]);
+                        accn[2 * k] = fmaf(x[2 * k], bf16_lo(wn[k]), accn[2 * k]);
+                        accn[2 * k + 1] = fmaf(x[2 * k + 1], bf16_hi(wn[k]), accn[2 * k + 1]);
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    red[(kg * 2 + 0) * D + c8 * 8 + e] = acc1[e];
+                    red[(kg * 2 + 1) * D + c8 * 8 + e] = accn[e];
+                }
+            }
+            __syncthreads();
+            for (int i = tid; i < 2 * D; i += kDkvThreads) {
+                const int src = i / D, d = i - (i / D) * D;
+                float sum = 0.0f;
+                for (int kg = 0; kg < NKG; ++kg) sum += red[(kg * 2 + src) * D + d];
+                part[(2 * which + src) * D + d] = sum;
             }
         }
     }
@@ -699,6 +725,14 @@ int launch_bwd3(const BwdArgs& a, hipStream_t st)
     hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, a);
     int rc = (int)hipGetLastError();
     if (rc) return rc;
+    if constexpr (FUSED) {
+        // fuse once; both tile kernels then read the fused rows
+        const int64_t items = (int64_t)a.B * a.Hkv * a.S * (D / 8);
+        const int64_t blocks = (items + 255) / 256;
+        hipLaunchKernelGGL(bwd_prefuse_kernel<D>, dim3((unsigned)(blocks < (1 << 20) ? blocks : (1 << 20))),
+                           dim3(256), 0, st, a);
+        if ((rc = (int)hipGetLastError())) return rc;
+    }
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, FUSED, G>), dim3((unsigned)(a.B * a.Hkv * a.nkt)), dim3(kDkvThreads), 0,
                        st, a);
     if ((rc = (int)hipGetLastError())) return rc;
@@ -707,12 +741,6 @@ int launch_bwd3(const BwdArgs& a, hipStream_t st)
     const int nqt = (a.S + BM - 1) / BM;
     const dim3 qgrid((unsigned)(a.B * a.Hkv * (G / HPW) * nqt));
     if constexpr (FUSED) {
-        // fuse once, then the single-source query-tile kernel over the fused rows
-        const int64_t items = (int64_t)a.B * a.Hkv * a.S * (D / 8);
-        const int64_t blocks = (items + 255) / 256;
-        hipLaunchKernelGGL(bwd_prefuse_kernel<D>, dim3((unsigned)(blocks < (1 << 20) ? blocks : (1 << 20))),
-                           dim3(256), 0, st, a);
-        if ((rc = (int)hipGetLastError())) return rc;
         BwdArgs f = a;
         const int64_t slab = (int64_t)a.S * D;
         f.k1 = View{a.kf, a.Hkv * slab, D, slab};
