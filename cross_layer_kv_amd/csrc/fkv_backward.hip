@@ -707,13 +707,13 @@ __global__ __launch_bounds__(256) void bwd_prefuse_kernel(const BwdArgs a)
         float w1[8], wn[8];
         load8f(a.kw1 + g * D + c * 8, w1);
         load8f(a.kwn + g * D + c * 8, wn);
-        const uint4 k1 = *reinterpret_cast<const uint4*>(row_ptr(a.k1, b, t, g) + c * 8);
-        const uint4 kn = *reinterpret_cast<const uint4*>(row_ptr(a.kn, b, t, g) + c * 8);
+        const uint4 k1 = stream16(row_ptr(a.k1, b, t, g) + c * 8);
+        const uint4 kn = stream16(row_ptr(a.kn, b, t, g) + c * 8);
         *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.kf) + row * D + c * 8) = fuse8_bf16(k1, kn, w1, wn);
         load8f(a.vw1 + g * D + c * 8, w1);
         load8f(a.vwn + g * D + c * 8, wn);
-        const uint4 v1 = *reinterpret_cast<const uint4*>(row_ptr(a.v1, b, t, g) + c * 8);
-        const uint4 vn = *reinterpret_cast<const uint4*>(row_ptr(a.vn, b, t, g) + c * 8);
+        const uint4 v1 = stream16(row_ptr(a.v1, b, t, g) + c * 8);
+        const uint4 vn = stream16(row_ptr(a.vn, b, t, g) + c * 8);
         *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.vf) + row * D + c * 8) = fuse8_bf16(v1, vn, w1, wn);
     }
 }

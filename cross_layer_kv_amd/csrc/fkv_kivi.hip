@@ -365,8 +365,7 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const bool chan = ks * 32 + hb * 8 < D;
-                    const uint32_t v = *reinterpret_cast<const uint32_t*>(kcp + (int64_t)tc * (D / 2) +
-                                                                          (chan ? ks * 16 + hb * 4 : 0));
+                    const uint32_t v = stream4(kcp + (int64_t)tc * (D / 2) + (chan ? ks * 16 + hb * 4 : 0));
                     x.kc[s][tl][ks] = (chan && t < t_end) ? v : 0u;
                 }
             }
@@ -378,8 +377,8 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
         const int s = c / (2 * KS), ks = (c >> 1) - (c / (2 * KS)) * KS, sm = c & 1;
         const Q4View& kv = *ksrc[s];
         const bool chan = ks * 32 + hb * 8 < D;
-        const uint4 km = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(sm ? kv.minv : kv.scale) +
-                                                         (bh * ngk + j) * D + (chan ? ks * 32 + hb * 8 : 0));
+        const uint4 km = stream16(static_cast<const uint16_t*>(sm ? kv.minv : kv.scale) + (bh * ngk + j) * D +
+                                  (chan ? ks * 32 + hb * 8 : 0));
         x.km = chan ? km : make_uint4(0u, 0u, 0u, 0u);
     };
     auto load_values = [&](int t0, VBlk& x) {
@@ -389,13 +388,13 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
             const uint8_t* vcp = static_cast<const uint8_t*>(vsrc[s]->codes) + (bh * nbv + j) * D * 16;
 #pragma unroll
             for (int n = 0; n < NVB; ++n)
-                x.vc[s][n] = *reinterpret_cast<const uint32_t*>(vcp + (n * 16 + l16) * 16 + hb * 4);
+                x.vc[s][n] = stream4(vcp + (n * 16 + l16) * 16 + hb * 4);
         }
         const int c = l16 % NC;
         const int s = c / (2 * KS), ks = (c >> 1) - (c / (2 * KS)) * KS, sm = c & 1;
         const Q4View& vv = *vsrc[s];
-        x.vm = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(sm ? vv.minv : vv.scale) +
-                                               ((bh * nbv + j) * KS + ks) * kGroup + hb * 8);
+        x.vm = stream16(static_cast<const uint16_t*>(sm ? vv.minv : vv.scale) + ((bh * nbv + j) * KS + ks) * kGroup +
+                        hb * 8);
     };
 
     f32x4 oacc[NS][NVB];

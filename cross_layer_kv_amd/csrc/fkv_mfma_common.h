@@ -111,6 +111,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Loads of data a call reads exactly once (source rows, 4-bit codes and
+// their metadata): non-temporal, so they stream through the caches without
+// displacing lines that are reused.
+__device__ __forceinline__ uint32_t stream4(const void* p)
+{
+    return __builtin_nontemporal_load(static_cast<const uint32_t*>(p));
+}
+__device__ __forceinline__ uint4 stream16(const void* p)
+{
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(static_cast<const u32x4*>(p)));
+}
+
 constexpr uint32_t kOffNone = 0x80000000u;  // always past the descriptor's size
 
 __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
@@ -122,10 +135,11 @@ __device__ __forceinline__ uint32_t ld4(__amdgpu_buffer_rsrc_t r, uint32_t off)
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
 // 16 bytes at lane offset + uniform offset; the range check covers the sum
-// (measured on gfx950), so either part may carry the row position.
+// (measured on gfx950), so either part may carry the row position.  For data
+// read once per call: the load is non-temporal (cache policy bit 1, "nt").
 __device__ __forceinline__ uint4 ld16s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff)
 {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, (int)soff, 0));
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, (int)soff, 2));
 }
 
 }  // namespace dev

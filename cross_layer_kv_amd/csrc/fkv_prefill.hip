@@ -103,11 +103,11 @@ __global__ __launch_bounds__(256) void prefuse_kernel(const PrefillArgs a)
         if (t < S) {
             const uint16_t* p1 = static_cast<const uint16_t*>(s1.data) + (int64_t)b * s1.sb + (int64_t)t * s1.ss +
                                  (int64_t)g * s1.sh + c * 8;
-            const uint4 x1 = *reinterpret_cast<const uint4*>(p1);
+            const uint4 x1 = stream16(p1);
             if constexpr (FUSED) {
                 const uint16_t* pn = static_cast<const uint16_t*>(sn.data) + (int64_t)b * sn.sb +
                                      (int64_t)t * sn.ss + (int64_t)g * sn.sh + c * 8;
-                const uint4 xn = *reinterpret_cast<const uint4*>(pn);
+                const uint4 xn = stream16(pn);
                 const float4 wa = *reinterpret_cast<const float4*>(w1 + g * D + c * 8);
                 const float4 wb = *reinterpret_cast<const float4*>(w1 + g * D + c * 8 + 4);
                 const float4 na = *reinterpret_cast<const float4*>(wn + g * D + c * 8);
