@@ -365,7 +365,9 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const bool chan = ks * 32 + hb * 8 < D;
-                    const uint32_t v = stream4(kcp + (int64_t)tc * (D / 2) + (chan ? ks * 16 + hb * 4 : 0));
+                    // plain load: the k-steps of one token row share its cache lines
+                    const uint32_t v = *reinterpret_cast<const uint32_t*>(kcp + (int64_t)tc * (D / 2) +
+                                                                          (chan ? ks * 16 + hb * 4 : 0));
                     x.kc[s][tl][ks] = (chan && t < t_end) ? v : 0u;
                 }
             }
