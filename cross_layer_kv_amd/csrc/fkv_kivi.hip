@@ -81,40 +81,90 @@ __device__ __forceinline__ uint32_t qcode(float x, const QParams& p)
     return (uint32_t)fminf(fmaxf(rintf(t), 0.0f), 15.0f);
 }
 
-// Keys: one thread per (batch*head, 32-token group, channel pair).
+// Keys: one workgroup per (batch*head, 32-token group).  The group's rows
+// are staged in LDS with 16-byte loads; four threads per channel pair take
+// the pair's minimum and maximum over 8 tokens each and combine them across
+// their quad; then one thread per (token, 8-channel chunk) writes that
+// chunk's 4 bytes of codes, so the codes leave as whole words.
 __global__ __launch_bounds__(256) void kivi_quant_keys_kernel(const KiviQuantArgs a)
 {
-    const int np = a.D / 2, ng = (a.S + kGroup - 1) / kGroup;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (int64_t)a.B * a.H * ng * np) return;
-    const int cp = (int)(i % np);
-    const int j = (int)((i / np) % ng);
-    const int bh = (int)(i / ((int64_t)np * ng));
+    constexpr int kMaxD = 128;
+    __shared__ uint32_t xs[kGroup][kMaxD / 2 + 1];  // bf16 channel pairs of each token
+    __shared__ float pm[kMaxD], pr[kMaxD];
+    const int np = a.D / 2, cpr = a.D / 8, ng = (a.S + kGroup - 1) / kGroup;
+    const int bh = blockIdx.x / ng, j = blockIdx.x - (blockIdx.x / ng) * ng;
     const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
-    const int t0 = j * kGroup, t1 = min(a.S, t0 + kGroup);
-    const uint16_t* src = static_cast<const uint16_t*>(a.src.data) + (int64_t)b * a.src.sb + (int64_t)h * a.src.sh + 2 * cp;
-    float lo_mn = INFINITY, lo_mx = -INFINITY, hi_mn = INFINITY, hi_mx = -INFINITY;
-    for (int t = t0; t < t1; ++t) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(src + (int64_t)t * a.src.ss);
-        const float x0 = bf16_lo(w), x1 = bf16_hi(w);
-        lo_mn = fminf(lo_mn, x0);
-        lo_mx = fmaxf(lo_mx, x0);
-        hi_mn = fminf(hi_mn, x1);
-        hi_mx = fmaxf(hi_mx, x1);
+    const int tid = threadIdx.x;
+    const int t0 = j * kGroup, n = min(kGroup, a.S - t0);
+    const uint16_t* src = static_cast<const uint16_t*>(a.src.data) + (int64_t)b * a.src.sb + (int64_t)h * a.src.sh;
+    for (int e = tid; e < n * cpr; e += 256) {
+        const int tt = e / cpr, c = e - (e / cpr) * cpr;
+        const uint4 u = stream16(src + (int64_t)(t0 + tt) * a.src.ss + c * 8);
+        xs[tt][c * 4 + 0] = u.x;
+        xs[tt][c * 4 + 1] = u.y;
+        xs[tt][c * 4 + 2] = u.z;
+        xs[tt][c * 4 + 3] = u.w;
     }
-    const QParams p0 = qparams(lo_mn, lo_mx), p1 = qparams(hi_mn, hi_mx);
-    uint8_t* codes = static_cast<uint8_t*>(a.codes) + (int64_t)bh * a.S * np + cp;
-    for (int t = t0; t < t1; ++t) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(src + (int64_t)t * a.src.ss);
-        codes[(int64_t)t * np] = (uint8_t)(qcode(bf16_lo(w), p0) | (qcode(bf16_hi(w), p1) << 4));
+    __syncthreads();
+    {
+        // (np <= 64: the 256 threads cover every pair; quads are lanes 4p..4p+3)
+        const int cp = tid >> 2, q = tid & 3;
+        float lo_mn = INFINITY, lo_mx = -INFINITY, hi_mn = INFINITY, hi_mx = -INFINITY;
+        if (cp < np) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int tt = q * 8 + k;
+                if (tt < n) {
+                    const uint32_t w = xs[tt][cp];
+                    const float x0 = bf16_lo(w), x1 = bf16_hi(w);
+                    lo_mn = fminf(lo_mn, x0);
+                    lo_mx = fmaxf(lo_mx, x0);
+                    hi_mn = fminf(hi_mn, x1);
+                    hi_mx = fmaxf(hi_mx, x1);
+                }
+            }
+        }
+#pragma unroll
+        for (int o = 1; o < 4; o <<= 1) {
+            lo_mn = fminf(lo_mn, __shfl_xor(lo_mn, o));
+            lo_mx = fmaxf(lo_mx, __shfl_xor(lo_mx, o));
+            hi_mn = fminf(hi_mn, __shfl_xor(hi_mn, o));
+            hi_mx = fmaxf(hi_mx, __shfl_xor(hi_mx, o));
+        }
+        if (cp < np && q == 0) {
+            const QParams p0 = qparams(lo_mn, lo_mx), p1 = qparams(hi_mn, hi_mx);
+            pm[2 * cp] = p0.m;
+            pr[2 * cp] = p0.r;
+            pm[2 * cp + 1] = p1.m;
+            pr[2 * cp + 1] = p1.r;
+            const int64_t mo = ((int64_t)bh * ng + j) * a.D + 2 * cp;
+            uint16_t* sc = static_cast<uint16_t*>(a.scale);
+            uint16_t* mn = static_cast<uint16_t*>(a.minv);
+            sc[mo] = p0.sc16;
+            sc[mo + 1] = p1.sc16;
+            mn[mo] = p0.mn16;
+            mn[mo + 1] = p1.mn16;
+        }
     }
-    const int64_t mo = ((int64_t)bh * ng + j) * a.D + 2 * cp;
-    uint16_t* sc = static_cast<uint16_t*>(a.scale);
-    uint16_t* mn = static_cast<uint16_t*>(a.minv);
-    sc[mo] = p0.sc16;
-    sc[mo + 1] = p1.sc16;
-    mn[mo] = p0.mn16;
-    mn[mo + 1] = p1.mn16;
+    __syncthreads();
+    uint32_t* codes = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.codes) + ((int64_t)bh * a.S + t0) * np);
+    for (int e = tid; e < n * cpr; e += 256) {
+        const int tt = e / cpr, c = e - (e / cpr) * cpr;
+        uint32_t acc = 0u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t w = xs[tt][c * 4 + k];
+            const int ch = c * 8 + 2 * k;
+            QParams p0{}, p1{};
+            p0.m = pm[ch];
+            p0.r = pr[ch];
+            p1.m = pm[ch + 1];
+            p1.r = pr[ch + 1];
+            acc |= (qcode(bf16_lo(w), p0) | (qcode(bf16_hi(w), p1) << 4)) << (8 * k);
+        }
+        // row tt of the group, bytes 4c..4c+3 (D/2 bytes per row: a whole number of words)
+        codes[tt * (np / 4) + c] = acc;
+    }
 }
 
 // Value positions inside a 32-token block: element e of word w is token
@@ -687,7 +737,7 @@ int launch_kivi_quantize(const KiviQuantArgs& a, void* stream)
     if (a.is_value) {
         blocks = (int64_t)a.B * a.H * ((a.S + kGroup - 1) / kGroup);  // one workgroup per 32-token block
     } else {
-        blocks = ((int64_t)a.B * a.H * ((a.S + kGroup - 1) / kGroup) * (a.D / 2) + 255) / 256;
+        blocks = (int64_t)a.B * a.H * ((a.S + kGroup - 1) / kGroup);  // one workgroup per 32-token group
     }
     if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
     if (a.is_value) hipLaunchKernelGGL(kivi_quant_values_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
