@@ -23,7 +23,8 @@ shape), 4b-decode, hgqa-decode (64 query heads per KV head, matrix-core
 kernel), 4b-prefill, 1.5b-prefill, long-decode-b1 / long-decode-b8
 (131072 cached tokens; the whole 24-layer stack: 12 storage layers of plain
 attention plus 12 reconstruction layers, FusedKV vs Lite vs an all-vanilla
-model), and 1.5b-ttft (time to first token over the attention of all 24
+model, each step replayed as one HIP graph, with the eager time beside it),
+and 1.5b-ttft (time to first token over the attention of all 24
 layers: the storage layers run causal prefill, the reconstruction layers only
 the final query row, a decode at S, against 24 layers of causal prefill).
 """
@@ -127,6 +128,23 @@ def _time_region(fn, steps, warmup, stream):
     t1.record(stream)
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps  # ms per call of fn
+
+
+def _capture(fn, stream):
+    """fn(st) (a sequence of library calls on stream st) captured as one HIP
+    graph.  It runs once on the capture stream first, so nothing is set up
+    during capture; the library records only kernel launches."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        fn(cap)
+    cap.synchronize()
+    with torch.cuda.graph(g, stream=cap):
+        fn(cap)
+    torch.cuda.synchronize()
+    return g
 
 
 def run_decode(cfg, steps, warmup, stream):
@@ -327,34 +345,38 @@ def run_stack(cfg, steps, warmup, stream):
     out = torch.empty_like(qs[0])
     ws = binding.decode_workspace(qs[0], base.k1)
 
-    def storage(i):
+    def storage(i, st):
         k, v = pairs[i % 4]
-        binding.fkv_lite_decode(qs[i], k, v, out=out, workspace=ws, stream=stream)
+        binding.fkv_lite_decode(qs[i], k, v, out=out, workspace=ws, stream=st)
 
-    def fused_model():
+    def fused_model(st=stream):
         for i in range(nl):
-            storage(i)
+            storage(i, st)
         for i in range(nl):
             binding.fkv_decode(qs[nl + i], base.k1, base.kn, base.v1, base.vn, ws_list[i], out=out,
-                               workspace=ws, stream=stream)
+                               workspace=ws, stream=st)
 
-    def lite_model():
+    def lite_model(st=stream):
         for i in range(nl):
-            storage(i)
+            storage(i, st)
         for i in range(nl):
-            binding.fkv_lite_decode(qs[nl + i], base.kn, base.v1, out=out, workspace=ws, stream=stream)
+            binding.fkv_lite_decode(qs[nl + i], base.kn, base.v1, out=out, workspace=ws, stream=st)
 
-    def vanilla_model():
+    def vanilla_model(st=stream):
         for i in range(2 * nl):
-            storage(i)
+            storage(i, st)
 
     per_layer = decode_bytes(B, S, Hq, Hkv, D, 2)
     res = {}
     for name, fn, byts in (("fused", fused_model, nl * per_layer + nl * decode_bytes(B, S, Hq, Hkv, D, 4)),
                            ("lite", lite_model, 2 * nl * per_layer),
                            ("vanilla", vanilla_model, 2 * nl * per_layer)):
-        ms = _time_region(fn, steps, warmup, stream)
-        res[name] = dict(ms_per_step=ms, gbs=byts / (ms * 1e-3) / 1e9, bytes=byts)
+        eager = _time_region(fn, steps, warmup, stream)
+        # the whole step as one HIP graph, replayed on the timing stream
+        g = _capture(fn, stream)
+        ms = _time_region(g.replay, steps, warmup, stream)
+        res[name] = dict(ms_per_step=ms, gbs=byts / (ms * 1e-3) / 1e9, bytes=byts, eager_ms_per_step=eager)
+        del g
     return res
 
 
@@ -552,7 +574,8 @@ def other_workload(args, line, stream):
                     config=dict(shape, layers=2 * cfg["layers"]))
         line["roofline"] = {"bound": "hbm", "achieved": round(f["gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(f["gbs"] / HBM_PEAK_GBS, 4), "traffic": None}
-        line["stack"] = {k: {"ms": round(v["ms_per_step"], 4), "GB/s": round(v["gbs"], 2), "bytes": v["bytes"]}
+        line["stack"] = {k: {"ms": round(v["ms_per_step"], 4), "GB/s": round(v["gbs"], 2), "bytes": v["bytes"],
+                             "eager_ms": round(v["eager_ms_per_step"], 4)}
                          for k, v in res.items()}
         line["stack"]["time_over_vanilla"] = {k: round(res[k]["ms_per_step"] / res["vanilla"]["ms_per_step"], 3)
                                               for k in ("fused", "lite")}

@@ -208,3 +208,52 @@ def test_full_size_high_gqa_decode():
     """High-GQA shape: B=16, S=32768, 128/2 heads, D=128 (the benchmarked
     launch); oracle on every head of sampled batch rows."""
     _sampled(16, 32768, 128, 2, 128, 0xF0006, n_batches=2)
+
+
+def test_stack_graph_replay_matches_eager():
+    """A decode stack (two storage-layer calls, a FusedKV call and a Lite call,
+    all with the key axis split, so each call is two kernels over a shared
+    workspace) captured as one HIP graph, as the bench replays whole stacks.
+    Every replay, with eager work and synchronisation between replays, equals
+    the eager result bit for bit, and the FusedKV output matches the oracle."""
+    B, S, Hq, Hkv, D = 1, 700, 8, 4, 96
+    say("decode stack graph replay B=%d S=%d Hq=%d Hkv=%d D=%d bf16" % (B, S, Hq, Hkv, D))
+    L = inputs.make_layer(B, 1, S, Hq, Hkv, D, torch.bfloat16, 0xF00D, DEV)
+    ws = binding.decode_workspace(L.q, L.k1)
+    outs = [torch.empty_like(L.q) for _ in range(4)]
+
+    def stack(st):
+        binding.fkv_lite_decode(L.q, L.k1, L.v1, out=outs[0], workspace=ws, stream=st)
+        binding.fkv_lite_decode(L.q, L.kn, L.vn, out=outs[1], workspace=ws, stream=st)
+        binding.fkv_decode(L.q, L.k1, L.kn, L.v1, L.vn, L.weights, out=outs[2], workspace=ws, stream=st)
+        binding.fkv_lite_decode(L.q, L.kn, L.v1, out=outs[3], workspace=ws, stream=st)
+
+    stack(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    ro, _ = oracle_layer(L, fused=True)
+    e = rel_err(gpu_rows(ref[2], B, Hq, 1, D), ro)
+    say("  eager fused err=%.3e" % e)
+    assert e <= TOL[torch.bfloat16]
+
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        stack(cap)
+    cap.synchronize()
+    with torch.cuda.graph(g, stream=cap):
+        stack(cap)
+    torch.cuda.synchronize()
+    other = torch.empty_like(L.q)
+    for r in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        # eager library work between replays, on the same workspace
+        binding.fkv_decode(L.q, L.kn, L.k1, L.vn, L.v1, L.weights, out=other, workspace=ws)
+        torch.cuda.synchronize()
+        say("  replay %d" % r)
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, x) in enumerate(zip(outs, ref)):
+            assert torch.equal(o, x), (r, i)
