@@ -112,8 +112,8 @@ fkv::DecodePlan plan_decode(const fkv_params* p, bool fused, bool kivi = false)
     // workgroups per CU
     const bool wide = G == fkv::kHighGqa;
     const int64_t iter = wide ? 64 : (int64_t)pl.waves * (kivi ? 32 : 16);
-    // (the 4-bit single-source kernel fits two workgroups per CU)
-    const int64_t target = (wide || (kivi && !fused)) ? 512 : 256;
+    // (the 8-wave 4-bit single-source kernel fits two workgroups per CU)
+    const int64_t target = (wide || (kivi && !fused && pl.waves == 8)) ? 512 : 256;
     const int64_t max_splits = S > 0 ? (S + iter - 1) / iter : 1;
     int64_t ns = units > 0 ? (target + units - 1) / units : 1;
     if (const char* env = std::getenv("FKV_DECODE_SPLITS")) {

@@ -60,14 +60,14 @@ constexpr int decode_waves(int dtype_f32, bool fused, int G)
 }
 
 // Waves per workgroup of the 4-bit decode kernel (a wave takes 32-token
-// blocks).  Eight: at twelve the four-source kernel (D = 96) must spill to
-// fit 3 waves per SIMD and measured slower.
+// blocks).  Four-source: eight; at twelve it (D = 96) must spill to fit 3
+// waves per SIMD and measured slower.  Single-source up to D = 96: sixteen
+// (4 waves per SIMD in one workgroup per unit, so 256 units need no key
+// split and no merge); at D = 128 it would not fit 128 VGPRs.
 constexpr int kivi_waves(bool fused, int G, int D)
 {
-    (void)fused;
     (void)G;
-    (void)D;
-    return 8;
+    return (!fused && D <= 96) ? 16 : 8;
 }
 
 // Prefill (S_q == S_k), bf16 only.
