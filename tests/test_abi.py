@@ -147,14 +147,15 @@ def test_kivi_validation_codes(lib, B):
     assert _kivi_decode(lib, B, _params(B, batch=0), lite=True) == B.FKV_SUCCESS
     # the workspace size is the largest of the decode plans; here the bf16
     # four-source plan (12-wave workgroups, 192-token steps: 43 splits of
-    # 192 tokens) needs more than the 4-bit plan (8 waves x 32-token blocks:
-    # 32 splits of 256 tokens), which is checked exactly
+    # 192 tokens) needs more than the 4-bit plans, which are checked exactly:
+    # four-source 8 waves x 32-token blocks (32 splits of 256 tokens),
+    # single-source 16 waves x 32-token blocks (16 splits of 512 tokens)
     p = _params(B, sk=8192)
     need = lib.fkv_decode_workspace_size(ctypes.byref(p))
     ws = lambda units, ns, G, D: math.ceil(units * ns * G * 2 * 4 / 256) * 256 + units * ns * G * D * 4
     assert need == ws(4, 43, 2, 64)
     assert _kivi_decode(lib, B, p, ws_bytes=ws(4, 32, 2, 64) - 1) == WS
-    assert _kivi_decode(lib, B, p, ws_bytes=ws(4, 32, 2, 64) - 1, lite=True) == WS
+    assert _kivi_decode(lib, B, p, ws_bytes=ws(4, 16, 2, 64) - 1, lite=True) == WS
     assert _kivi_decode(lib, B, p, ws=FAKE + 16) == WS
     # quantiser: bfloat16 source only, is_value 0 or 1, an empty cache is a no-op
     c = _cache(B)
@@ -277,11 +278,14 @@ def test_workspace_size(lib, B):
     p = _params(B, sq=2)
     assert lib.fkv_decode_workspace_size(ctypes.byref(p)) == 0
     # 650M-shape decode: 32 x 8 = 256 (batch, kv head) units fill the chip with
-    # one workgroup each, so the bf16 plans need no split; the 4-bit
-    # single-source plan aims at two workgroups per CU (2 splits of 4096
-    # tokens) and sets the size
+    # one workgroup each (the 4-bit single-source kernel too, with 16-wave
+    # workgroups up to D = 96), so no plan splits the keys
     p = _params(B, batch=32, sk=8192, hq=16, hkv=8, d=96)
-    units, ns, G, D = 256, 2, 2, 96
+    assert lib.fkv_decode_workspace_size(ctypes.byref(p)) == 0
+    # at D = 128 the 4-bit single-source kernel keeps 8-wave workgroups and
+    # aims at two per CU: 2 splits of 4096 tokens
+    p = _params(B, batch=32, sk=8192, hq=16, hkv=8, d=128)
+    units, ns, G, D = 256, 2, 2, 128
     assert lib.fkv_decode_workspace_size(ctypes.byref(p)) == \
         math.ceil(units * ns * G * 2 * 4 / 256) * 256 + units * ns * G * D * 4
     # long context, batch 1: 8 units; the bf16 plans take 32 splits of 4096
