@@ -140,29 +140,35 @@ __device__ __forceinline__ void load8f(const float* p, float* w)
 }
 
 // ---- 1. prep: LSE in log2 units and rowsum(dO * O), [B, Hq, S] ----
+// A group of LPR lanes (D/8 of them active) takes one (b, t, h) row, 16 bytes
+// of O and dO per lane, so each load instruction reads whole rows; the
+// group's partial sums are added over the lanes in a fixed order.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs a)
 {
+    constexpr int LPR = D / 8 <= 8 ? 8 : 16;  // lanes per row
     const int64_t n = (int64_t)a.B * a.S * a.Hq;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;
-    const int h = (int)(i % a.Hq);
-    const int64_t bs = i / a.Hq;
-    const int t = (int)(bs % a.S), b = (int)(bs / a.S);
-    const uint16_t* o = static_cast<const uint16_t*>(a.out) + i * D;
-    const uint16_t* g = static_cast<const uint16_t*>(a.dout) + i * D;
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;
+    const int pc = threadIdx.x % LPR;
+    const bool on = i < n && pc < D / 8;
     float s = 0.0f;
-#pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-        const uint4 x = *reinterpret_cast<const uint4*>(o + c * 8);
-        const uint4 y = *reinterpret_cast<const uint4*>(g + c * 8);
+    if (on) {
+        const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.out) + i * D + pc * 8);
+        const uint4 y = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.dout) + i * D + pc * 8);
         const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) s += bf16_lo(xs[k]) * bf16_lo(ys[k]) + bf16_hi(xs[k]) * bf16_hi(ys[k]);
     }
-    const int64_t r = ((int64_t)b * a.Hq + h) * a.S + t;
-    a.delta[r] = s;
-    a.lse2[r] = a.lse[r] * kLog2e;
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) s += __shfl_xor(s, o);
+    if (i < n && pc == 0) {
+        const int h = (int)(i % a.Hq);
+        const int64_t bs = i / a.Hq;
+        const int t = (int)(bs % a.S), b = (int)(bs / a.S);
+        const int64_t r = ((int64_t)b * a.Hq + h) * a.S + t;
+        a.delta[r] = s;
+        a.lse2[r] = a.lse[r] * kLog2e;
+    }
 }
 
 // ---- 2. key tiles: dKf, dVf, source gradients, weight partials ----
@@ -673,6 +679,8 @@ __global__ __launch_bounds__(256) void bwd_wreduce_kernel(const BwdArgs a)
     for (int i = threadIdx.x; i < kRedParts * a.D; i += 256) {
         const int d = i % a.D, part = i / a.D;
         float s = 0.0f;
+        // (unrolled so that several loads are in flight; the additions keep their order)
+#pragma unroll 8
         for (int k = part; k < n; k += kRedParts) {
             const int b = k / a.nkt, kt = k - (k / a.nkt) * a.nkt;
             s += a.wpart[((int64_t)item_index(b, g, kt, a.Hkv, a.nkt) * 4 + w) * a.D + d];
@@ -722,7 +730,11 @@ template <int D, bool FUSED, int G>
 int launch_bwd3(const BwdArgs& a, hipStream_t st)
 {
     const int64_t rows = (int64_t)a.B * a.S * a.Hq;
-    hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, a);
+    {
+        const int64_t lanes = rows * (D / 8 <= 8 ? 8 : 16);
+        if ((lanes + 255) / 256 > 0x7fffffff) return (int)hipErrorInvalidValue;
+        hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, st, a);
+    }
     int rc = (int)hipGetLastError();
     if (rc) return rc;
     if constexpr (FUSED) {
