@@ -160,27 +160,32 @@ def run_decode(cfg, steps, warmup, stream):
     outs = [torch.empty_like(q) for q in qs]
     ws = binding.decode_workspace(qs[0], base.k1)
 
-    def fused_step():
+    def fused_step(st=stream):
         for i in range(nl):
             binding.fkv_decode(qs[i], base.k1, base.kn, base.v1, base.vn, ws_list[i], out=outs[i],
-                               workspace=ws, stream=stream)
+                               workspace=ws, stream=st)
 
-    def lite_step():
+    def lite_step(st=stream):
         for i in range(nl):
-            binding.fkv_lite_decode(qs[i], base.kn, base.v1, out=outs[i], workspace=ws, stream=stream)
+            binding.fkv_lite_decode(qs[i], base.kn, base.v1, out=outs[i], workspace=ws, stream=st)
 
-    def vanilla_step():  # storage-layer control: attention over a layer's own caches
+    def vanilla_step(st=stream):  # storage-layer control: attention over a layer's own caches
         for i in range(nl):
             k, v = (base.k1, base.v1) if i % 2 == 0 else (base.kn, base.vn)
-            binding.fkv_lite_decode(qs[i], k, v, out=outs[i], workspace=ws, stream=stream)
+            binding.fkv_lite_decode(qs[i], k, v, out=outs[i], workspace=ws, stream=st)
 
     res = {}
     elt = 4 if dt == torch.float32 else 2
     for name, fn, src in (("fused", fused_step, 4), ("lite", lite_step, 2), ("vanilla", vanilla_step, 2)):
         ms = _time_region(fn, steps, warmup, stream)
         byts = decode_bytes(B, S, Hq, Hkv, D, src, elt) * nl
+        # the same step replayed as one HIP graph: no host launch cost between kernels
+        g = _capture(fn, stream)
+        gms = _time_region(g.replay, steps, warmup, stream)
+        del g
         res[name] = dict(ms_per_step=ms, ms_per_layer=ms / nl, gbs=byts / (ms * 1e-3) / 1e9,
-                         bytes_per_layer=byts // nl)
+                         bytes_per_layer=byts // nl, graph_ms_per_layer=gms / nl,
+                         graph_gbs=byts / (gms * 1e-3) / 1e9)
     return res, base
 
 
@@ -493,7 +498,10 @@ def main():
                             "bytes_per_launch": f["bytes_per_layer"],
                             "avg_launch_us": round(f["ms_per_layer"] * 1e3, 2)}
         line["decode_variants"] = {k: {"GB/s": round(v["gbs"], 2), "us_per_layer": round(v["ms_per_layer"] * 1e3, 2),
-                                       "frac": round(v["gbs"] / HBM_PEAK_GBS, 4)} for k, v in dec.items()}
+                                       "frac": round(v["gbs"] / HBM_PEAK_GBS, 4),
+                                       "graph_GB/s": round(v["graph_gbs"], 2),
+                                       "graph_us_per_layer": round(v["graph_ms_per_layer"] * 1e3, 2)}
+                                   for k, v in dec.items()}
         line["decode_variants"]["fused_over_vanilla_time"] = round(dec["fused"]["ms_per_layer"] /
                                                                    dec["vanilla"]["ms_per_layer"], 3)
         if not args.no_cpu_baseline:
@@ -551,7 +559,10 @@ def other_workload(args, line, stream):
                             "frac": round(f["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
                             "bytes_per_launch": f["bytes_per_layer"], "avg_launch_us": round(f["ms_per_layer"] * 1e3, 2)}
         line["decode_variants"] = {k: {"GB/s": round(v["gbs"], 2), "us_per_layer": round(v["ms_per_layer"] * 1e3, 2),
-                                       "frac": round(v["gbs"] / HBM_PEAK_GBS, 4)} for k, v in res.items()}
+                                       "frac": round(v["gbs"] / HBM_PEAK_GBS, 4),
+                                       "graph_GB/s": round(v["graph_gbs"], 2),
+                                       "graph_us_per_layer": round(v["graph_ms_per_layer"] * 1e3, 2)}
+                                   for k, v in res.items()}
         line["decode_variants"]["fused_over_vanilla_time"] = round(res["fused"]["ms_per_layer"] /
                                                                    res["vanilla"]["ms_per_layer"], 3)
     elif kind == "prefill":

@@ -213,28 +213,34 @@ def test_full_size_high_gqa_decode():
 def test_stack_graph_replay_matches_eager():
     """A decode stack (two storage-layer calls, a FusedKV call and a Lite call,
     all with the key axis split, so each call is two kernels over a shared
-    workspace) captured as one HIP graph, as the bench replays whole stacks.
+    workspace, then a FusedKV call on the matrix-core kernel for 64 query
+    heads per KV head) captured as one HIP graph, as the bench replays steps.
     Every replay, with eager work and synchronisation between replays, equals
     the eager result bit for bit, and the FusedKV output matches the oracle."""
     B, S, Hq, Hkv, D = 1, 700, 8, 4, 96
-    say("decode stack graph replay B=%d S=%d Hq=%d Hkv=%d D=%d bf16" % (B, S, Hq, Hkv, D))
+    say("decode stack graph replay B=%d S=%d Hq=%d Hkv=%d D=%d bf16, plus G=64 D=128" % (B, S, Hq, Hkv, D))
     L = inputs.make_layer(B, 1, S, Hq, Hkv, D, torch.bfloat16, 0xF00D, DEV)
+    H = inputs.make_layer(1, 1, 700, 128, 2, 128, torch.bfloat16, 0xF00E, DEV)  # matrix-core decode
     ws = binding.decode_workspace(L.q, L.k1)
-    outs = [torch.empty_like(L.q) for _ in range(4)]
+    wsh = binding.decode_workspace(H.q, H.k1)
+    outs = [torch.empty_like(L.q) for _ in range(4)] + [torch.empty_like(H.q)]
 
     def stack(st):
         binding.fkv_lite_decode(L.q, L.k1, L.v1, out=outs[0], workspace=ws, stream=st)
         binding.fkv_lite_decode(L.q, L.kn, L.vn, out=outs[1], workspace=ws, stream=st)
         binding.fkv_decode(L.q, L.k1, L.kn, L.v1, L.vn, L.weights, out=outs[2], workspace=ws, stream=st)
         binding.fkv_lite_decode(L.q, L.kn, L.v1, out=outs[3], workspace=ws, stream=st)
+        binding.fkv_decode(H.q, H.k1, H.kn, H.v1, H.vn, H.weights, out=outs[4], workspace=wsh, stream=st)
 
     stack(torch.cuda.current_stream())
     torch.cuda.synchronize()
     ref = [o.clone() for o in outs]
     ro, _ = oracle_layer(L, fused=True)
     e = rel_err(gpu_rows(ref[2], B, Hq, 1, D), ro)
-    say("  eager fused err=%.3e" % e)
-    assert e <= TOL[torch.bfloat16]
+    ro, _ = oracle_layer(H, fused=True)
+    eh = rel_err(gpu_rows(ref[4], 1, 128, 1, 128), ro)
+    say("  eager fused err=%.3e, G=64 err=%.3e" % (e, eh))
+    assert e <= TOL[torch.bfloat16] and eh <= TOL[torch.bfloat16]
 
     g = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
