@@ -463,7 +463,7 @@ def main():
                          "used to scale the FETCH_SIZE / WRITE_SIZE counters of a profiler run")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run its own "
+        print("bench.py measures one GPU: the library has no multi-GPU path (each GPU would run its own "
               "share of batch rows or KV heads with no exchange); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
