@@ -523,16 +523,24 @@ def main():
             line.update(value=round(pre["fused"]["tflops"], 2), unit="TFLOP/s",
                         ms_per_step=round(pre["fused"]["ms_per_step"], 4),
                         config={"workload": PREFILL["name"]})
-    if args.copy_calibration:
-        n = args.copy_calibration // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        line["copy_calibration_bytes"] = n * 4
-        del src, dst
+    copy_calibration(args, line)
     finish(line)
+
+
+def copy_calibration(args, line):
+    """A plain float32 copy of args.copy_calibration bytes, for scaling the
+    FETCH_SIZE / WRITE_SIZE counters of a profiler run of the same program."""
+    if not args.copy_calibration:
+        return
+    import torch
+    n = args.copy_calibration // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    line["copy_calibration_bytes"] = n * 4
+    del src, dst
 
 
 def finish(line):
@@ -624,6 +632,7 @@ def other_workload(args, line, stream):
                     ms_per_step=round(res["fused"]["ms"], 4), config=dict(shape, layers=2 * cfg["layers"]))
         line["ttft"] = {"fused_ms": round(res["fused"]["ms"], 4), "vanilla_ms": round(res["vanilla"]["ms"], 4),
                         "fused_over_vanilla": round(res["fused"]["ms"] / res["vanilla"]["ms"], 3)}
+    copy_calibration(args, line)
     finish(line)
 
 
