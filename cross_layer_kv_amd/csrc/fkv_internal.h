@@ -60,14 +60,14 @@ constexpr int decode_waves(int dtype_f32, bool fused, int G)
 }
 
 // Waves per workgroup of the 4-bit decode kernel (a wave takes 32-token
-// blocks).  Four-source: eight; at twelve it (D = 96) must spill to fit 3
-// waves per SIMD and measured slower.  Single-source up to D = 96: sixteen
-// (4 waves per SIMD in one workgroup per unit, so 256 units need no key
-// split and no merge); at D = 128 it would not fit 128 VGPRs.
+// blocks), one workgroup per (batch, KV head) when there are enough of them.
+// Up to D = 96: sixteen single-source waves (4 per SIMD, 128 VGPRs) or
+// twelve four-source waves (3 per SIMD, 168 VGPRs with the value side
+// loaded when a block starts).  At D = 128 neither fits: eight.
 constexpr int kivi_waves(bool fused, int G, int D)
 {
     (void)G;
-    return (!fused && D <= 96) ? 16 : 8;
+    return D <= 96 ? (fused ? 12 : 16) : 8;
 }
 
 // Prefill (S_q == S_k), bf16 only.

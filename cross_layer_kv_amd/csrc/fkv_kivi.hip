@@ -600,16 +600,19 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
     };
 
     // The next block's key-side loads are in flight while a block is
-    // computed.  The four-source kernel prefetches the value side as well;
-    // the single-source one (more waves per SIMD) issues it when a block
-    // starts, which measured faster there.
+    // computed.  The value side is issued when a block starts and lands
+    // during its score product, except in the 8-wave four-source kernel
+    // (D = 128), which prefetches it one block ahead as well: elsewhere the
+    // registers that prefetch would take buy a third wave per SIMD (the
+    // 12-wave four-source kernel) or a fourth (the 16-wave single-source).
     const int step = NW * kGroup;
     Blk cur;
     VBlk vcur;
     int t0 = t_begin + wave * kGroup;
+    constexpr bool VPRE = FUSED && NW == 8;  // prefetch the value side one block ahead
     if (t0 < t_end) {
         load_block(t0, cur);
-        if constexpr (FUSED) load_values(t0, vcur);
+        if constexpr (VPRE) load_values(t0, vcur);
     }
     for (; t0 < t_end; t0 += step) {
         park(cur);
@@ -617,12 +620,12 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
         VBlk vnxt;
         if (t0 + step < t_end) {
             load_block(t0 + step, nxt);
-            if constexpr (FUSED) load_values(t0 + step, vnxt);
+            if constexpr (VPRE) load_values(t0 + step, vnxt);
         }
-        if constexpr (!FUSED) load_values(t0, vcur);
+        if constexpr (!VPRE) load_values(t0, vcur);
         compute(cur, vcur, t0);
         cur = nxt;
-        if constexpr (FUSED) vcur = vnxt;
+        if constexpr (VPRE) vcur = vnxt;
     }
 
     // ---- wave results: (m, l) and the minimum terms per head ----
