@@ -415,9 +415,9 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
     // contiguous range of 16 D bytes.  The wave reads it with contiguous
     // loads of CB bytes (chunk c of the block, source c / NCS, lands at byte
     // CB c of the wave's LDS area) and takes each lane's score-product
-    // operand (4 bytes of one row) from LDS.  Loading the operands straight from the
-    // cache (4 bytes per lane spread over 16 rows) capped the stream at about
-    // 4 TB/s on this part, against 6.2 for contiguous loads of the same bytes.
+    // operand (4 bytes of one row) from LDS.  Loading the operands straight
+    // from memory (4 bytes per lane spread over 16 rows) streams at about
+    // 4 TB/s on gfx950, against 6.2 for contiguous loads of the same bytes.
     struct Blk {  // key side
         KChunk kraw[NKI];
         uint4 km;
