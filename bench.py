@@ -73,16 +73,24 @@ WORKLOADS = {
 }
 
 
+def decode_source_sha():
+    """sha256[:16] over the decode kernel source and the header that sets its
+    launch shape (waves per workgroup, tokens per wave step)."""
+    h = hashlib.sha256()
+    for name in ("fkv_decode.hip", "fkv_internal.h"):
+        h.update(open(os.path.join(ROOT, "cross_layer_kv_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def recorded_traffic():
     """HBM bytes per launch of the four-source decode kernel, from the
     committed counter summary (FETCH_SIZE and WRITE_SIZE runs scaled by a
     copy kernel of known size); None when the kernel source has changed
     since the counters were taken, or when there is no summary."""
     path = os.path.join(ROOT, "profiles", "decode_650m_bf16_hbm_traffic.txt")
-    src = os.path.join(ROOT, "cross_layer_kv_amd", "csrc", "fkv_decode.hip")
     try:
         text = open(path, encoding="utf-8").read()
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        sha = decode_source_sha()
     except OSError:
         return None
     fields = {}

@@ -97,7 +97,7 @@ float scale_log2_of(const fkv_params* p)
 // one compute unit, so the plan aims at one workgroup per CU of a 256-CU
 // part: one split per (batch, KV head) when there are at least 256 of them,
 // otherwise enough splits of the key axis to reach 256 workgroups, each split
-// covering at least one workgroup iteration (waves * 16 tokens).  Splits are
+// covering at least one workgroup iteration (waves * decode_wave_tokens).  Splits are
 // multiples of 64 tokens and at most 256.  The plan depends on the
 // parameters only (no device query), so the workspace size is a pure function
 // of them.  FKV_DECODE_SPLITS overrides the split count (tuning and tests).
@@ -111,7 +111,7 @@ fkv::DecodePlan plan_decode(const fkv_params* p, bool fused, bool kivi = false)
     // G = 64 runs the matrix-core kernel: 64-token tiles, and it aims at two
     // workgroups per CU
     const bool wide = G == fkv::kHighGqa;
-    const int64_t iter = wide ? 64 : (int64_t)pl.waves * (kivi ? 32 : 16);
+    const int64_t iter = wide ? 64 : (int64_t)pl.waves * (kivi ? 32 : fkv::decode_wave_tokens(p->dtype == FKV_F32, fused, (int)G));
     // (the 8-wave 4-bit single-source kernel fits two workgroups per CU)
     const int64_t target = (wide || (kivi && !fused && pl.waves == 8)) ? 512 : 256;
     const int64_t max_splits = S > 0 ? (S + iter - 1) / iter : 1;

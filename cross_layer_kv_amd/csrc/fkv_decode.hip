@@ -43,7 +43,6 @@
 namespace fkv {
 namespace {
 
-constexpr int kWaveTokens = 16;  // tokens per wave per iteration
 constexpr int kCombineThreads = 256;
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -132,7 +131,8 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const DecodeArgs a)
     constexpr int NP = D / 8;              // 8-channel pieces per row
     constexpr int LPT = NP <= 8 ? 8 : 16;  // lanes per token group
     constexpr int TPW = 64 / LPT;          // tokens per wave step
-    constexpr int U = kWaveTokens / TPW;   // steps per iteration
+    constexpr int WT = decode_wave_tokens(sizeof(T) == 4, FUSED, G);  // tokens per wave per iteration
+    constexpr int U = WT / TPW;            // steps per iteration
 
     __shared__ float s_acc[NW][G][D];
     __shared__ float s_ml[NW][G][2];
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const DecodeArgs a)
         for (int c = 0; c < 8; ++c) acc[hh][c] = 0.0f;
     }
 
-    for (int t0 = t_begin + wave * kWaveTokens; t0 < t_end; t0 += NW * kWaveTokens) {
+    for (int t0 = t_begin + wave * WT; t0 < t_end; t0 += NW * WT) {
         Raw8<T> rk1[U], rkn[U], rv1[U], rvn[U];
         bool ok[U];
 #pragma unroll

@@ -42,8 +42,8 @@ struct DecodePlan {
 
 // Waves per decode workgroup.  Chosen so that one workgroup fills a compute
 // unit at the occupancy the kernel's register count allows (4 SIMDs x waves
-// per SIMD): e.g. the bf16 four-source kernel with G <= 2 uses ~155 VGPRs,
-// 3 waves per SIMD, 12 waves.  The kernels are compiled with the matching
+// per SIMD): e.g. the bf16 four-source kernel with G <= 2 uses 123 VGPRs,
+// 4 waves per SIMD, 16 waves.  The kernels are compiled with the matching
 // launch bound, so the register budget is enforced.
 // Query heads per KV head served by the matrix-core decode kernel.
 constexpr int kHighGqa = 64;
@@ -52,11 +52,19 @@ constexpr int decode_waves(int dtype_f32, bool fused, int G)
 {
     if (G == kHighGqa) return 4;  // 2 key halves x 2 blocks of 32 heads
     if (!dtype_f32) {
-        if (fused) return G <= 2 ? 12 : (G == 4 ? 8 : 4);
+        if (fused) return G <= 2 ? 16 : (G == 4 ? 8 : 4);
         return G <= 2 ? 16 : (G == 4 ? 12 : 8);
     }
     if (fused) return G <= 4 ? 8 : 4;
     return G <= 2 ? 12 : (G == 4 ? 8 : 4);
+}
+
+// Tokens a wave takes per iteration of the decode loop.  The bf16
+// four-source kernel with G <= 2 takes 8, which halves its load registers
+// (123 VGPRs) so that 4 waves per SIMD fit; the others take 16.
+constexpr int decode_wave_tokens(int dtype_f32, bool fused, int G)
+{
+    return (!dtype_f32 && fused && G <= 2) ? 8 : 16;
 }
 
 // Waves per workgroup of the 4-bit decode kernel (a wave takes 32-token

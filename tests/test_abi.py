@@ -146,14 +146,15 @@ def test_kivi_validation_codes(lib, B):
     assert _kivi_decode(lib, B, _params(B, batch=0)) == B.FKV_SUCCESS
     assert _kivi_decode(lib, B, _params(B, batch=0), lite=True) == B.FKV_SUCCESS
     # the workspace size is the largest of the decode plans; here the bf16
-    # four-source plan (12-wave workgroups, 192-token steps: 43 splits of
-    # 192 tokens) needs more than the 4-bit plans, which are checked exactly:
+    # four-source plan (16-wave workgroups of 8-token wave steps, 128-token
+    # workgroup steps: 64 splits of 128 tokens) needs more than the 4-bit
+    # plans, which are checked exactly:
     # four-source 12 waves x 32-token blocks (22 splits of 384 tokens),
     # single-source 16 waves x 32-token blocks (16 splits of 512 tokens)
     p = _params(B, sk=8192)
     need = lib.fkv_decode_workspace_size(ctypes.byref(p))
     ws = lambda units, ns, G, D: math.ceil(units * ns * G * 2 * 4 / 256) * 256 + units * ns * G * D * 4
-    assert need == ws(4, 43, 2, 64)
+    assert need == ws(4, 64, 2, 64)
     assert _kivi_decode(lib, B, p, ws_bytes=ws(4, 22, 2, 64) - 1) == WS
     assert _kivi_decode(lib, B, p, ws_bytes=ws(4, 16, 2, 64) - 1, lite=True) == WS
     assert _kivi_decode(lib, B, p, ws=FAKE + 16) == WS
