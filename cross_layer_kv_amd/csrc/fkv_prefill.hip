@@ -200,16 +200,35 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
         }
     }
 
+    // msub: the running reference max, 0 while there is none.  With SPLAT the
+    // queries are pre-multiplied by scale * log2(e) and the score chains start
+    // from -msub, so the accumulators hold exponent arguments directly (the
+    // splat changes only when the reference is raised).  That removes one VALU
+    // instruction per score, which pays where the softmax weighs most against
+    // the matrix-core work of a tile (D = 80, S = 16384: +4.5%).  At D = 128 it
+    // measured 0.5-0.9% slower (and the in-kernel fusion mode would spill), so
+    // there the scores are scaled and shifted by one FMA before each exponential.
+    constexpr bool SPLAT = D <= 96;
+
     // ---- queries: B operand of S^T = K~ Q^T, 8 channels per lane per k-step
     f16x8 qreg[KS];
     {
         const int row = r0 + l32;
         const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (((int64_t)b * S + row) * a.Hq + h) * D + hi * 8;
+        const float qs = a.scale_log2;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             uint4 u = make_uint4(0u, 0u, 0u, 0u);
             if (row < S) u = *reinterpret_cast<const uint4*>(qp + ks * 16);
-            qreg[ks] = as_f16x8(bf16x8_to_f16x8(u));
+            if constexpr (SPLAT) {
+                const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+                uint32_t o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = pack2(bf16_lo(w[i]) * qs, bf16_hi(w[i]) * qs);
+                qreg[ks] = as_f16x8(make_uint4(o[0], o[1], o[2], o[3]));
+            } else {
+                qreg[ks] = as_f16x8(bf16x8_to_f16x8(u));
+            }
         }
     }
 
@@ -409,6 +428,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
 #pragma unroll
     for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
     float m_run = -INFINITY, l_run = 0.0f, l_run2 = 0.0f;  // two row-sum chains
+    float msub = 0.0f;
+    f32x16 msplat = f32x16{};
     const int qrow = r0 + l32;
     const float sl2 = a.scale_log2;
 
@@ -430,7 +451,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
         if (wave_live) {
             // S^T = K~ Q^T over two 32-key blocks; LDS fragments are read two
             // k-steps ahead of the matrix-core instructions that use them
-            f32x16 sacc[2] = {f32x16{}, f32x16{}};
+            f32x16 sacc[2] = {SPLAT ? msplat : f32x16{}, SPLAT ? msplat : f32x16{}};
             const uint16_t* kt = &Kt[buf][0] + l32 * KROW + hi * 8;
             uint4 kf[KS][2];
 #pragma unroll
@@ -474,7 +495,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
                     for (int i = 0; i < 16; ++i)
                         if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) sacc[kb][i] = -INFINITY;
             }
-            // running max (log2 domain)
+            // tile max (log2 domain; relative to msub with SPLAT)
             float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -485,7 +506,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
             // The reference max is raised only when a tile max exceeds it by
             // more than 8 (log2 units): the probabilities then stay <= 2^8,
             // exact in fp16, and the accumulator is rescaled on few tiles.
-            const float m_tile = mx * sl2;
+            const float m_tile = SPLAT ? msub + mx : mx * sl2;
             if (__any(m_tile > m_run + 8.0f)) {
                 const float m_new = fmaxf(m_run, m_tile);
                 const float corr = m_run == -INFINITY ? 0.0f : exp2_fast(m_run - m_new);
@@ -496,8 +517,21 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) oacc[d][i] *= corr;
                 m_run = m_new;
+                // re-base this tile's scores and the splat on the new reference
+                const float msub_new = m_run == -INFINITY ? 0.0f : m_run;
+                if constexpr (SPLAT) {
+                    const float sh = msub_new - msub;
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) sacc[kb][i] -= sh;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) msplat[i] = -msub_new;
+                }
+                msub = msub_new;
             }
-            const float msub = m_run == -INFINITY ? 0.0f : m_run;
+            const float psub = SPLAT ? 0.0f : (m_run == -INFINITY ? 0.0f : m_run);
+            const float pmul = SPLAT ? 1.0f : sl2;
             // per 32-key block: probabilities -> fp16 B operands, then
             // O^T += V~^T P^T; the second block's exponentials overlap the
             // first block's matrix-core work
@@ -509,8 +543,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
                     uint32_t w[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float p0 = exp2_fast(sacc[kb][half * 8 + 2 * i] * sl2 - msub);
-                        const float p1 = exp2_fast(sacc[kb][half * 8 + 2 * i + 1] * sl2 - msub);
+                        const float p0 = exp2_fast(sacc[kb][half * 8 + 2 * i] * pmul - psub);
+                        const float p1 = exp2_fast(sacc[kb][half * 8 + 2 * i + 1] * pmul - psub);
                         w[i] = pack2(p0, p1);
                         // row sum of the rounded probabilities the products use
                         if (i & 1)
