@@ -68,6 +68,26 @@ def test_ragged_lengths(S):
 
 
 @pytest.mark.parametrize("D", [80, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_reference_max_raised_mid_row(D, causal):
+    """Keys of the first 64-key tile scaled by 0.05 and all later keys by 3:
+    in about half of the rows the second tile's max exceeds the running max
+    by more than 8 log2 units, so the accumulator rescale (and, at D <= 96,
+    the re-base of the score chains on a non-zero reference) runs in the
+    middle of a row.  Scores stay within ~30 log2 units: larger ones lose
+    more than the tolerance to binary16 operand rounding in any form of the
+    kernel (a CPU emulation of its roundings puts this case at 0.006-0.007)."""
+    say("prefill mid-row max raises D=%d causal=%s S=320" % (D, causal))
+    S = 320
+    L = inputs.make_layer(1, S, S, 4, 2, D, torch.bfloat16, 500 + D, DEV, decode=False)
+    ramp = torch.where(torch.arange(S, device=DEV) < 64, 0.05, 3.0).to(torch.bfloat16).view(1, S, 1, 1)
+    for t in (L.k1, L.kn):
+        t.mul_(ramp)
+    check(L, fused=True, causal=causal)
+    check(L, fused=False, causal=causal)
+
+
+@pytest.mark.parametrize("D", [80, 128])
 def test_non_causal(D):
     say("prefill non-causal D=%d S=190" % D)
     L = inputs.make_layer(1, 190, 190, 4, 2, D, torch.bfloat16, 400 + D, DEV, decode=False)
