@@ -191,6 +191,23 @@ def test_high_gqa_splits_and_ragged(splits, monkeypatch):
     check(L, fused=False)
 
 
+@pytest.mark.parametrize("D", [80, 128])
+def test_high_gqa_reference_max_raised_mid_sequence(D, monkeypatch):
+    """One split over the whole cache; keys of the first 64-token tile
+    scaled by 0.05 and later keys by 3, so for many heads the second tile's
+    max exceeds the running max by more than 8 log2 units and the lazy
+    rescale runs after a non-empty first tile."""
+    monkeypatch.setenv("FKV_DECODE_SPLITS", "1")
+    say("decode high-GQA mid-sequence max raises D=%d S=333" % D)
+    S = 333
+    L = inputs.make_layer(2, 1, S, 128, 2, D, torch.bfloat16, 970 + D, DEV)
+    ramp = torch.where(torch.arange(S, device=DEV) < 64, 0.05, 3.0).to(torch.bfloat16).view(1, S, 1, 1)
+    for t in (L.k1, L.kn):
+        t.mul_(ramp)
+    check(L, fused=True)
+    check(L, fused=False)
+
+
 def test_high_gqa_selector_weights_match_lite():
     """(a, a', b, b') = (0, 1, 1, 0): the fused kernel reads exactly K^n and
     V^1 and its fp16 tiles equal the Lite kernel's, bit for bit."""
