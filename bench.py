@@ -256,27 +256,25 @@ def run_prefill(cfg, steps, warmup, stream):
     ws_list = [base.weights] + [inputs.make_weights(Hkv, D, cfg["seed"] * 89 + i, device=dev)
                                 for i in range(1, nl)]
     out = torch.empty_like(base.q)
-    pre = binding.prefill_workspace(base.q, base.k1)
 
-    # "fused"/"lite": each tile fused (converted) once into the workspace, then
-    # attended; "*_in_kernel": every workgroup fuses the tiles it reads
-    def fused_step(ws=pre):
+    # every attention workgroup fuses (or, single-source, converts) the
+    # tiles it reads inside the kernel; nothing is staged in memory
+    def fused_step():
         for i in range(nl):
             binding.fkv_prefill(qs[i], base.k1, base.kn, base.v1, base.vn, ws_list[i], out=out, causal=True,
-                                workspace=ws, stream=stream)
+                                stream=stream)
 
-    def lite_step(ws=pre):
+    def lite_step():
         for i in range(nl):
-            binding.fkv_lite_prefill(qs[i], base.kn, base.v1, out=out, causal=True, workspace=ws, stream=stream)
+            binding.fkv_lite_prefill(qs[i], base.kn, base.v1, out=out, causal=True, stream=stream)
 
     res = {}
     fl = prefill_flops(B, S, Hq, D)
-    for name, fn in (("fused", fused_step), ("lite", lite_step), ("fused_in_kernel", lambda: fused_step(None)),
-                     ("lite_in_kernel", lambda: lite_step(None))):
+    for name, fn in (("fused", fused_step), ("lite", lite_step)):
         ms = _time_region(fn, max(1, steps // 2), max(1, warmup // 2), stream)
         res[name] = dict(ms_per_step=ms, ms_per_layer=ms / nl,
                          tflops=fl * nl / (ms * 1e-3) / 1e12)
-    del qs, out, base, pre
+    del qs, out, base
     torch.cuda.empty_cache()
     return res
 

@@ -59,8 +59,10 @@ class fkv_fusion(ctypes.Structure):
                 ("v_w1", ctypes.c_void_p), ("v_wn", ctypes.c_void_p)]
 
 
+ABI_VERSION = 6
+
 EXPORTS = ["fkv_abi_version", "fkv_status_string", "fkv_last_error", "fkv_decode_workspace_size",
-           "fkv_decode", "fkv_lite_decode", "fkv_prefill_workspace_size", "fkv_prefill", "fkv_lite_prefill",
+           "fkv_decode", "fkv_lite_decode", "fkv_prefill", "fkv_lite_prefill",
            "fkv_check_tied",
            "fkv_kivi_codes_bytes", "fkv_kivi_meta_bytes", "fkv_kivi_quantize", "fkv_kivi_decode",
            "fkv_kivi_lite_decode", "fkv_backward_workspace_size", "fkv_prefill_backward",
@@ -93,13 +95,11 @@ def load_library(path: str = LIB_PATH):
     lib.fkv_lite_decode.restype = ctypes.c_int
     lib.fkv_lite_decode.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, vp, vp, vp, vp,
                                     ctypes.c_size_t, vp]
-    lib.fkv_prefill_workspace_size.restype = ctypes.c_size_t
-    lib.fkv_prefill_workspace_size.argtypes = [P(fkv_params)]
     lib.fkv_prefill.restype = ctypes.c_int
     lib.fkv_prefill.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, fkv_cache, fkv_cache,
-                                P(fkv_fusion), vp, vp, vp, ctypes.c_size_t, vp]
+                                P(fkv_fusion), vp, vp, vp]
     lib.fkv_lite_prefill.restype = ctypes.c_int
-    lib.fkv_lite_prefill.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fkv_lite_prefill.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, vp, vp, vp]
     lib.fkv_check_tied.restype = ctypes.c_int
     lib.fkv_check_tied.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float]
     lib.fkv_kivi_codes_bytes.restype = ctypes.c_size_t
@@ -123,7 +123,7 @@ def load_library(path: str = LIB_PATH):
     lib.fkv_lite_prefill_backward.restype = ctypes.c_int
     lib.fkv_lite_prefill_backward.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, vp, vp, vp, vp, fkv_grad,
                                               fkv_grad, vp, ctypes.c_size_t, vp]
-    if lib.fkv_abi_version() != 5:
+    if lib.fkv_abi_version() != ABI_VERSION:
         raise RuntimeError("libfusedkv ABI version mismatch")
     _lib = lib
     return lib
@@ -151,6 +151,89 @@ def _dev(t, name):
     return t.data_ptr()
 
 
+# ---- argument checks ----
+# The C ABI sees only pointers, strides and the shape block, so a tensor whose
+# shape, dtype or extent disagrees with the others would make the kernels read
+# or write outside it.  These checks compare the tensors with each other
+# before any pointer is handed over; they raise ValueError / TypeError.  They
+# look at shapes, dtypes and strides only (the device check comes when the
+# pointers are taken), so they run the same way on host tensors.
+
+def _contig(t, name):
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _same_dtype(ref, t, name):
+    if t.dtype != ref.dtype:
+        raise TypeError("%s is %s, expected %s like q" % (name, t.dtype, ref.dtype))
+
+
+def _check_qo(q, out, name_q="q", name_o="out"):
+    """q, out: contiguous [B, S_q, H_q, D] tensors of one dtype and shape."""
+    if q.dim() != 4:
+        raise ValueError("%s must be [B, S_q, H_q, D]" % name_q)
+    _contig(q, name_q)
+    _contig(out, name_o)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("%s shape %s differs from %s shape %s" % (name_o, tuple(out.shape), name_q, tuple(q.shape)))
+    _same_dtype(q, out, name_o)
+
+
+def _check_caches(q, caches, names):
+    """Every cache a [B, S_k, H_kv, D] view of q's dtype with B and D of q,
+    H_q a multiple of H_kv, and all caches of one shape."""
+    B, _, Hq, D = q.shape
+    ref = None
+    for c, n in zip(caches, names):
+        if c.dim() != 4 or c.stride(3) != 1:
+            raise ValueError("%s must be a [B, S, H_kv, D] view with a contiguous channel axis" % n)
+        _same_dtype(q, c, n)
+        if c.shape[0] != B or c.shape[3] != D:
+            raise ValueError("%s shape %s does not match q (B=%d, D=%d)" % (n, tuple(c.shape), B, D))
+        if c.shape[2] < 1 or Hq % c.shape[2]:
+            raise ValueError("%s has %d KV heads; q has %d heads" % (n, c.shape[2], Hq))
+        if ref is None:
+            ref = (tuple(c.shape), n)
+        elif tuple(c.shape) != ref[0]:
+            raise ValueError("%s shape %s differs from %s shape %s" % (n, tuple(c.shape), ref[1], ref[0]))
+
+
+def _check_weights(weights, Hkv, D, name="weights"):
+    if weights is None or len(weights) != 4:
+        raise ValueError("%s are the four [H_kv, D] float32 vectors (a, a', b, b')" % name)
+    for w in weights:
+        if w.dtype != torch.float32 or not w.is_contiguous():
+            raise TypeError("%s must be contiguous float32" % name)
+        if tuple(w.shape) != (Hkv, D):
+            raise ValueError("%s must be [H_kv, D] = [%d, %d], got %s" % (name, Hkv, D, tuple(w.shape)))
+
+
+def _check_lse(lse, q):
+    """lse: contiguous float32 [B, H_q, S_q] (or [B, H_q] when S_q = 1)."""
+    if lse is None:
+        return
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TypeError("lse must be contiguous float32")
+    B, Sq, Hq, _ = q.shape
+    if lse.numel() != B * Hq * Sq:
+        raise ValueError("lse holds %d elements, the call writes B*H_q*S_q = %d" % (lse.numel(), B * Hq * Sq))
+
+
+def _check_seqlens(seqlens_k, B):
+    if seqlens_k is None:
+        return
+    if seqlens_k.dtype != torch.int32 or not seqlens_k.is_contiguous() or seqlens_k.numel() != B:
+        raise ValueError("seqlens_k must be a contiguous int32 tensor of B = %d elements" % B)
+
+
+def _check_workspace(workspace):
+    if workspace is None:
+        return
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 tensor")
+
+
 def cache_view(t: torch.Tensor) -> fkv_cache:
     """fkv_cache of a logical [B, S, H, D] tensor (any strides, channel axis
     contiguous)."""
@@ -174,13 +257,28 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
-def _fusion(weights) -> fkv_fusion:
-    if weights is None or len(weights) != 4:
-        raise ValueError("weights are the four [Hkv, D] float32 vectors (a, a', b, b')")
-    for w in weights:
-        if w.dtype != torch.float32 or not w.is_contiguous():
-            raise TypeError("fusion weights must be contiguous float32")
+def _fusion(weights, Hkv, D) -> fkv_fusion:
+    _check_weights(weights, Hkv, D)
     return fkv_fusion(*[_dev(w, "weight") for w in weights])
+
+
+def _decode_checks(q, caches, names, out, lse, seqlens_k, workspace):
+    _check_qo(q, out)
+    if q.shape[1] != 1:
+        raise ValueError("decode takes one query row per batch row (q is [B, 1, H_q, D])")
+    _check_caches(q, caches, names)
+    _check_lse(lse, q)
+    _check_seqlens(seqlens_k, q.shape[0])
+    _check_workspace(workspace)
+
+
+def _prefill_checks(q, caches, names, out, lse):
+    _check_qo(q, out)
+    _check_caches(q, caches, names)
+    if caches[0].shape[1] != q.shape[1]:
+        raise ValueError("prefill needs S_q == S_k (q has %d rows, the caches %d tokens)"
+                         % (q.shape[1], caches[0].shape[1]))
+    _check_lse(lse, q)
 
 
 def fkv_decode_workspace_size(params: fkv_params) -> int:
@@ -198,8 +296,9 @@ def fkv_decode(q, k1, kn, v1, vn, weights, *, out, workspace, lse=None, seqlens_
     """FusedKV decode step of one reconstruction layer (see fkv_decode in
     include/fusedkv.h).  q, out: [B, 1, Hq, D]; caches [B, Sk, Hkv, D]."""
     lib = load_library()
+    _decode_checks(q, (k1, kn, v1, vn), ("k1", "kn", "v1", "vn"), out, lse, seqlens_k, workspace)
     p = make_params(q, k1, softmax_scale=softmax_scale)
-    f = _fusion(weights)
+    f = _fusion(weights, k1.shape[2], q.shape[3])
     _check(lib.fkv_decode(ctypes.byref(p), _dev(q, "q"), cache_view(k1), cache_view(kn), cache_view(v1),
                           cache_view(vn), ctypes.byref(f), _dev(seqlens_k, "seqlens_k"), _dev(out, "out"),
                           _dev(lse, "lse"), _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
@@ -210,44 +309,31 @@ def fkv_lite_decode(q, k_src, v_src, *, out, workspace, lse=None, seqlens_k=None
     """Single-source decode step: FusedKV-Lite with (K^n, V^1), or plain
     attention of a storage layer over its own caches."""
     lib = load_library()
+    _decode_checks(q, (k_src, v_src), ("k_src", "v_src"), out, lse, seqlens_k, workspace)
     p = make_params(q, k_src, softmax_scale=softmax_scale)
     _check(lib.fkv_lite_decode(ctypes.byref(p), _dev(q, "q"), cache_view(k_src), cache_view(v_src),
                                _dev(seqlens_k, "seqlens_k"), _dev(out, "out"), _dev(lse, "lse"),
                                _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
 
 
-def prefill_workspace(q: torch.Tensor, k: torch.Tensor) -> torch.Tensor:
-    """A fuse-once workspace for prefill calls with these shapes."""
-    n = load_library().fkv_prefill_workspace_size(ctypes.byref(make_params(q, k, causal=True)))
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
-
-
-def _ws(workspace):
-    return (None, 0) if workspace is None else (_dev(workspace, "workspace"), workspace.numel())
-
-
-def fkv_prefill(q, k1, kn, v1, vn, weights, *, out, lse=None, causal=True, softmax_scale=0.0, workspace=None,
-                stream=None):
-    """FusedKV prefill of one reconstruction layer (bf16).  q, out:
-    [B, S, Hq, D]; caches [B, S, Hkv, D].  workspace: a uint8 tensor from
-    prefill_workspace (fuse each tile once) or None (fuse in the kernel)."""
+def fkv_prefill(q, k1, kn, v1, vn, weights, *, out, lse=None, causal=True, softmax_scale=0.0, stream=None):
+    """FusedKV prefill of one reconstruction layer (bf16), tiles fused inside
+    the attention kernel.  q, out: [B, S, Hq, D]; caches [B, S, Hkv, D]."""
     lib = load_library()
+    _prefill_checks(q, (k1, kn, v1, vn), ("k1", "kn", "v1", "vn"), out, lse)
     p = make_params(q, k1, softmax_scale=softmax_scale, causal=causal)
-    f = _fusion(weights)
-    ws, nws = _ws(workspace)
+    f = _fusion(weights, k1.shape[2], q.shape[3])
     _check(lib.fkv_prefill(ctypes.byref(p), _dev(q, "q"), cache_view(k1), cache_view(kn), cache_view(v1),
-                           cache_view(vn), ctypes.byref(f), _dev(out, "out"), _dev(lse, "lse"), ws, nws,
-                           _stream(stream)))
+                           cache_view(vn), ctypes.byref(f), _dev(out, "out"), _dev(lse, "lse"), _stream(stream)))
 
 
-def fkv_lite_prefill(q, k_src, v_src, *, out, lse=None, causal=True, softmax_scale=0.0, workspace=None,
-                     stream=None):
+def fkv_lite_prefill(q, k_src, v_src, *, out, lse=None, causal=True, softmax_scale=0.0, stream=None):
     """Single-source prefill (FusedKV-Lite or the plain control)."""
     lib = load_library()
+    _prefill_checks(q, (k_src, v_src), ("k_src", "v_src"), out, lse)
     p = make_params(q, k_src, softmax_scale=softmax_scale, causal=causal)
-    ws, nws = _ws(workspace)
     _check(lib.fkv_lite_prefill(ctypes.byref(p), _dev(q, "q"), cache_view(k_src), cache_view(v_src),
-                                _dev(out, "out"), _dev(lse, "lse"), ws, nws, _stream(stream)))
+                                _dev(out, "out"), _dev(lse, "lse"), _stream(stream)))
 
 
 def fkv_check_tied(k_w: torch.Tensor, pairing: str = "interleaved", tol: float = 0.0) -> bool:
@@ -300,13 +386,40 @@ def kivi_empty(B, S, Hkv, D, is_value, device="cuda"):
                    torch.empty(meta, dtype=torch.float16, device=device), is_value, S)
 
 
+def _q4_shapes(B, S, Hkv, D, is_value):
+    nb = (S + 31) // 32
+    if is_value:
+        return (B, Hkv, nb, D, 16), (B, Hkv, nb, (D + 31) // 32, 32)
+    return (B, Hkv, S, D // 2), (B, Hkv, nb, D)
+
+
+def _check_q4(c: Q4Cache, B, S, Hkv, D, is_value, name):
+    """A 4-bit cache of the layout above for B batch rows, S tokens, Hkv heads
+    and head dim D (values: S rounded up to whole 32-token blocks)."""
+    if not isinstance(c, Q4Cache):
+        raise TypeError("%s must be a Q4Cache" % name)
+    if c.is_value != bool(is_value):
+        raise ValueError("%s must be a %s cache" % (name, "value" if is_value else "key"))
+    codes, meta = _q4_shapes(B, S, Hkv, D, is_value)
+    if c.codes.dtype != torch.uint8 or tuple(c.codes.shape) != codes or not c.codes.is_contiguous():
+        raise ValueError("%s codes must be contiguous uint8 %s, got %s %s"
+                         % (name, codes, c.codes.dtype, tuple(c.codes.shape)))
+    for t, n in ((c.scale, "scale"), (c.minv, "minv")):
+        if t.dtype != torch.float16 or tuple(t.shape) != meta or not t.is_contiguous():
+            raise ValueError("%s %s must be contiguous float16 %s, got %s %s"
+                             % (name, n, meta, t.dtype, tuple(t.shape)))
+
+
 def fkv_kivi_quantize(src: torch.Tensor, is_value: bool, *, dst: Q4Cache | None = None, num_q_heads=None,
                       stream=None) -> Q4Cache:
     """4-bit cache of a bf16 source [B, S, Hkv, D] (keys: is_value False)."""
     lib = load_library()
+    if src.dim() != 4 or src.stride(3) != 1:
+        raise ValueError("src must be a [B, S, H_kv, D] view with a contiguous channel axis")
     B, S, Hkv, D = src.shape
     if dst is None:
         dst = kivi_empty(B, S, Hkv, D, is_value, src.device)
+    _check_q4(dst, B, S, Hkv, D, is_value, "dst")
     p = fkv_params(B, 1, S, num_q_heads or Hkv, Hkv, D, _dtype(src), 0.0, 0)
     _check(lib.fkv_kivi_quantize(ctypes.byref(p), cache_view(src), 1 if is_value else 0, dst.view(), _stream(stream)))
     return dst
@@ -318,12 +431,35 @@ def _kivi_params(q, c: Q4Cache, softmax_scale):
     return fkv_params(B, Sq, c.seqlen, Hq, c.codes.shape[1], D, _dtype(q), float(softmax_scale), 0)
 
 
+def _kivi_checks(q, keys, values, out, lse, seqlens_k, workspace):
+    """keys / values: (Q4Cache, name) pairs; all share the first key cache's
+    batch, token count, KV heads and q's head dim."""
+    _check_qo(q, out)
+    if q.shape[1] != 1:
+        raise ValueError("decode takes one query row per batch row (q is [B, 1, H_q, D])")
+    B, _, Hq, D = q.shape
+    k0 = keys[0][0]
+    if not isinstance(k0, Q4Cache) or k0.codes.dim() != 4:
+        raise TypeError("%s must be a key Q4Cache" % keys[0][1])
+    S, Hkv = k0.seqlen, k0.codes.shape[1]
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError("%s has %d KV heads; q has %d heads" % (keys[0][1], Hkv, Hq))
+    for c, n in keys:
+        _check_q4(c, B, S, Hkv, D, False, n)
+    for c, n in values:
+        _check_q4(c, B, S, Hkv, D, True, n)
+    _check_lse(lse, q)
+    _check_seqlens(seqlens_k, B)
+    _check_workspace(workspace)
+
+
 def fkv_kivi_decode(q, k1: Q4Cache, kn: Q4Cache, v1: Q4Cache, vn: Q4Cache, weights, *, out, workspace, lse=None,
                     seqlens_k=None, softmax_scale=0.0, stream=None):
     """FusedKV decode over 4-bit sources (fkv_kivi_decode in fusedkv.h)."""
     lib = load_library()
+    _kivi_checks(q, ((k1, "k1"), (kn, "kn")), ((v1, "v1"), (vn, "vn")), out, lse, seqlens_k, workspace)
     p = _kivi_params(q, k1, softmax_scale)
-    f = _fusion(weights)
+    f = _fusion(weights, k1.codes.shape[1], q.shape[3])
     _check(lib.fkv_kivi_decode(ctypes.byref(p), _dev(q, "q"), k1.view(), kn.view(), v1.view(), vn.view(),
                                ctypes.byref(f), _dev(seqlens_k, "seqlens_k"), _dev(out, "out"), _dev(lse, "lse"),
                                _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
@@ -333,6 +469,7 @@ def fkv_kivi_lite_decode(q, k_src: Q4Cache, v_src: Q4Cache, *, out, workspace, l
                          softmax_scale=0.0, stream=None):
     """Single-source decode over 4-bit sources (FusedKV-Lite: K^n, V^1)."""
     lib = load_library()
+    _kivi_checks(q, ((k_src, "k_src"),), ((v_src, "v_src"),), out, lse, seqlens_k, workspace)
     p = _kivi_params(q, k_src, softmax_scale)
     _check(lib.fkv_kivi_lite_decode(ctypes.byref(p), _dev(q, "q"), k_src.view(), v_src.view(),
                                     _dev(seqlens_k, "seqlens_k"), _dev(out, "out"), _dev(lse, "lse"),
@@ -350,6 +487,24 @@ def grad_view(t: torch.Tensor) -> fkv_grad:
     return fkv_grad(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
 
 
+def _backward_checks(q, caches, names, out, lse, dout, dq, grads, gnames, workspace):
+    """Forward tensors as fkv_prefill; out, dout, dq like q; each gradient
+    view shaped and typed like its cache; lse the forward's [B, H_q, S]."""
+    _prefill_checks(q, caches, names, out, None)
+    _check_qo(q, dout, name_o="dout")
+    _check_qo(q, dq, name_o="dq")
+    if lse is None:
+        raise ValueError("the backward pass needs the forward LSE")
+    _check_lse(lse, q)
+    for g, n, c in zip(grads, gnames, caches):
+        if g.dim() != 4 or g.stride(3) != 1:
+            raise ValueError("%s must be a [B, S, H_kv, D] view with a contiguous channel axis" % n)
+        _same_dtype(q, g, n)
+        if tuple(g.shape) != tuple(c.shape):
+            raise ValueError("%s shape %s differs from its cache's %s" % (n, tuple(g.shape), tuple(c.shape)))
+    _check_workspace(workspace)
+
+
 def backward_workspace(q: torch.Tensor, k: torch.Tensor) -> torch.Tensor:
     """A workspace for backward calls with these shapes (contents ignored)."""
     n = load_library().fkv_backward_workspace_size(ctypes.byref(make_params(q, k, causal=True)))
@@ -362,11 +517,11 @@ def fkv_prefill_backward(q, k1, kn, v1, vn, weights, out, lse, dout, *, dq, dk1,
     fusedkv.h).  dweights: four contiguous float32 [Hkv, D] tensors written
     with the gradients of (a, a', b, b')."""
     lib = load_library()
+    _backward_checks(q, (k1, kn, v1, vn), ("k1", "kn", "v1", "vn"), out, lse, dout, dq, (dk1, dkn, dv1, dvn),
+                     ("dk1", "dkn", "dv1", "dvn"), workspace)
+    _check_weights(dweights, k1.shape[2], q.shape[3], "weight gradients")
     p = make_params(q, k1, softmax_scale=softmax_scale, causal=causal)
-    f = _fusion(weights)
-    for w in dweights:
-        if w.dtype != torch.float32 or not w.is_contiguous():
-            raise TypeError("weight gradients must be contiguous float32")
+    f = _fusion(weights, k1.shape[2], q.shape[3])
     df = fkv_fusion_grad(*[_dev(w, "weight gradient") for w in dweights])
     _check(lib.fkv_prefill_backward(ctypes.byref(p), _dev(q, "q"), cache_view(k1), cache_view(kn), cache_view(v1),
                                     cache_view(vn), ctypes.byref(f), _dev(out, "out"), _dev(lse, "lse"),
@@ -380,6 +535,7 @@ def fkv_lite_prefill_backward(q, k_src, v_src, out, lse, dout, *, dq, dk, dv, wo
     """Gradients of a single-source prefill layer (FusedKV-Lite with (K^n,
     V^1), or the plain control): dk, dv are the gradients of k_src, v_src."""
     lib = load_library()
+    _backward_checks(q, (k_src, v_src), ("k_src", "v_src"), out, lse, dout, dq, (dk, dv), ("dk", "dv"), workspace)
     p = make_params(q, k_src, softmax_scale=softmax_scale, causal=causal)
     _check(lib.fkv_lite_prefill_backward(ctypes.byref(p), _dev(q, "q"), cache_view(k_src), cache_view(v_src),
                                          _dev(out, "out"), _dev(lse, "lse"), _dev(dout, "dout"), _dev(dq, "dq"),

@@ -212,7 +212,7 @@ fkv_status decode_common(const fkv_params* p, const void* q, const fkv_cache* ca
 
 fkv_status prefill_common(const fkv_params* p, const void* q, const fkv_cache* caches,
                           const char* const* names, int ncaches, const fkv_fusion* fusion,
-                          void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream)
+                          void* out, float* lse, void* stream)
 {
     fkv_status s = check_shape(p);
     if (s) return s;
@@ -250,24 +250,8 @@ fkv_status prefill_common(const fkv_params* p, const void* q, const fkv_cache* c
     const int bm = fkv::prefill_rows_per_tile(G);
     if (bm <= 0) return fail(FKV_ERROR_UNSUPPORTED, "GQA ratio %d not supported by prefill", G);
 
-    if (workspace) {
-        int64_t voff = 0;
-        const int64_t need = fkv::prefill_pre_bytes(p->batch, p->num_kv_heads, p->seqlen_k, p->head_dim, &voff);
-        if (workspace_bytes < (size_t)need)
-            return fail(FKV_ERROR_WORKSPACE, "workspace needs %lld bytes (got %zu)", (long long)need, workspace_bytes);
-        if (reinterpret_cast<uintptr_t>(workspace) & 255u)
-            return fail(FKV_ERROR_WORKSPACE, "workspace is not 256-byte aligned");
-        // the fused key rows of one (batch, KV head) are read through a 32-bit buffer range
-        if (((int64_t)p->seqlen_k + 63) / 64 * 64 * p->head_dim * 2 >= ((int64_t)1 << 31))
-            return fail(FKV_ERROR_UNSUPPORTED, "fused key rows of one head exceed 2^31 bytes");
-    }
-
     fkv::PrefillArgs a{};
     a.q = q;
-    if (workspace) {
-        a.pre = workspace;
-        fkv::prefill_pre_bytes(p->batch, p->num_kv_heads, p->seqlen_k, p->head_dim, &a.pre_v_offset);
-    }
     a.k1 = view_of(caches[0]);
     a.v1 = view_of(caches[fused ? 2 : 1]);
     if (fused) {
@@ -290,9 +274,8 @@ fkv_status prefill_common(const fkv_params* p, const void* q, const fkv_cache* c
     a.n_qtiles = (p->seqlen_q + bm - 1) / bm;
     a.scale_log2 = scale_log2_of(p);
     if (std::getenv("FKV_TRACE"))
-        std::fprintf(stderr, "libfusedkv: prefill %s%s B=%d S=%d Hq=%d Hkv=%d D=%d qtiles=%d causal=%d\n",
-                     fused ? "fused" : "single", a.pre ? " (fuse once)" : "", a.B, a.S, a.Hq, a.Hkv, a.D,
-                     a.n_qtiles, a.causal);
+        std::fprintf(stderr, "libfusedkv: prefill %s B=%d S=%d Hq=%d Hkv=%d D=%d qtiles=%d causal=%d\n",
+                     fused ? "fused" : "single", a.B, a.S, a.Hq, a.Hkv, a.D, a.n_qtiles, a.causal);
     const int rc = fkv::launch_prefill(a, fused, stream);
     if (rc) return fail(FKV_ERROR_LAUNCH, "prefill launch failed (HIP error %d)", rc);
     return ok();
@@ -565,30 +548,21 @@ fkv_status fkv_lite_decode(const fkv_params* params, const void* q, fkv_cache k_
                          workspace_bytes, stream);
 }
 
-size_t fkv_prefill_workspace_size(const fkv_params* params)
-{
-    if (check_shape(params) != FKV_SUCCESS || params->seqlen_q != params->seqlen_k) return 0;
-    if (params->batch == 0 || params->seqlen_q == 0) return 0;
-    return (size_t)fkv::prefill_pre_bytes(params->batch, params->num_kv_heads, params->seqlen_k,
-                                          params->head_dim, nullptr);
-}
-
 fkv_status fkv_prefill(const fkv_params* params, const void* q, fkv_cache k1, fkv_cache kn,
                        fkv_cache v1, fkv_cache vn, const fkv_fusion* fusion, void* out,
-                       float* lse, void* workspace, size_t workspace_bytes, void* stream)
+                       float* lse, void* stream)
 {
     const fkv_cache c[4] = {k1, kn, v1, vn};
     static const char* const n[4] = {"k1", "kn", "v1", "vn"};
-    return prefill_common(params, q, c, n, 4, fusion, out, lse, workspace, workspace_bytes, stream);
+    return prefill_common(params, q, c, n, 4, fusion, out, lse, stream);
 }
 
 fkv_status fkv_lite_prefill(const fkv_params* params, const void* q, fkv_cache k_src,
-                            fkv_cache v_src, void* out, float* lse, void* workspace,
-                            size_t workspace_bytes, void* stream)
+                            fkv_cache v_src, void* out, float* lse, void* stream)
 {
     const fkv_cache c[2] = {k_src, v_src};
     static const char* const n[2] = {"k_src", "v_src"};
-    return prefill_common(params, q, c, n, 2, nullptr, out, lse, workspace, workspace_bytes, stream);
+    return prefill_common(params, q, c, n, 2, nullptr, out, lse, stream);
 }
 
 fkv_status fkv_check_tied(const float* host_k_w, int32_t h_kv, int32_t d, int32_t pairing, float tol)

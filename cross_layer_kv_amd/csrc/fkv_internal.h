@@ -92,16 +92,7 @@ struct PrefillArgs {
     int32_t causal;
     int32_t n_qtiles;       // ceil(S / rows per tile)
     float scale_log2;
-    // Fuse-once mode (pre != nullptr): the tiles are fused (or converted) once
-    // into binary16 buffers, keys [B, Hkv, S64, D] row-major and values as
-    // transposed tiles [B, Hkv, S64/64, D, 64] (keys permuted within a tile as
-    // the score accumulator holds them); S64 = S rounded up to 64, padding 0.
-    void* pre;
-    int64_t pre_v_offset;   // bytes from pre to the value tiles
 };
-
-// Bytes of the fuse-once prefill buffers (keys, then 256-aligned value tiles).
-int64_t prefill_pre_bytes(int64_t B, int64_t Hkv, int64_t S, int64_t D, int64_t* v_offset);
 
 // KIVI-style 4-bit cache of one source, contiguous (layout in fusedkv.h),
 // NB = ceil(S/32):
@@ -180,7 +171,7 @@ int launch_decode_combine_bf16(const DecodeArgs& a, void* stream);
 // 4-bit KIVI-style sources: quantiser and decode (bfloat16 queries/outputs).
 int launch_kivi_quantize(const KiviQuantArgs& a, void* stream);
 int launch_kivi_decode(const KiviDecodeArgs& a, bool fused, int waves, void* stream);
-int launch_prefill(const PrefillArgs& a, bool fused, void* stream);  // fuse-once when a.pre is set
+int launch_prefill(const PrefillArgs& a, bool fused, void* stream);
 int launch_backward(const BwdArgs& a, bool fused, void* stream);
 // Query rows per prefill workgroup for a GQA ratio (0 when unsupported).
 int prefill_rows_per_tile(int G);

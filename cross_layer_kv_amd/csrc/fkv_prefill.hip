@@ -61,88 +61,10 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int BN = 64;  // keys per tile
 constexpr float kLn2 = 0.69314718055994530942f;
 
-// Operand modes of the attention kernel: one bf16 key and value source, two
-// bf16 sources fused per tile in the kernel, or tiles already fused into
-// binary16 by prefuse_kernel (fuse once, attend many times).
+// Operand modes of the attention kernel: one bf16 key and value source, or
+// two bf16 sources fused per tile in the kernel.
 constexpr int kModeSingle = 0;
 constexpr int kModeFused = 1;
-constexpr int kModePre = 2;
-
-// Position c of a transposed value tile holds key vkey(c / 8) + koff(c % 8)
-// of the tile: the key order in which the score accumulator holds P.
-__device__ __forceinline__ int vtile_key(int c)
-{
-    const int vo = c >> 3, e = c & 7;
-    return (vo >> 1) * 16 + (vo & 1) * 4 + (e & 3) + (e >> 2) * 8;
-}
-
-// Fuse (or convert) one 64-key tile of one (batch, KV head) into binary16:
-// keys row-major, values transposed with keys in vtile_key order.  Rows past
-// S are written as zeros.  Fusion is float32 with the exact weights, rounded
-// once to binary16 (round to nearest even), as the attention kernel's
-// in-kernel fusion rounds its tiles.
-template <int D, bool FUSED>
-__global__ __launch_bounds__(256) void prefuse_kernel(const PrefillArgs a)
-{
-    constexpr int CPR = D / 8;          // 16-byte chunks per row
-    constexpr int VP = D + 8;           // LDS pitch of the fused value tile (elements)
-    __shared__ __attribute__((aligned(16))) uint16_t sv[BN * VP];
-
-    const int nt = (a.S + BN - 1) / BN;
-    const int j = blockIdx.x % nt;
-    const int unit = blockIdx.x / nt;
-    const int b = unit / a.Hkv, g = unit - (unit / a.Hkv) * a.Hkv;
-    const int S = a.S;
-    const int64_t S64 = (int64_t)nt * BN;
-    uint16_t* kout = static_cast<uint16_t*>(a.pre) + ((int64_t)unit * S64 + (int64_t)j * BN) * D;
-    uint16_t* vout = reinterpret_cast<uint16_t*>(static_cast<char*>(a.pre) + a.pre_v_offset) +
-                     ((int64_t)unit * nt + j) * D * BN;
-
-    auto fuse8 = [&](const View& s1, const View& sn, const float* w1, const float* wn, int t, int c) {
-        uint4 o = make_uint4(0u, 0u, 0u, 0u);
-        if (t < S) {
-            const uint16_t* p1 = static_cast<const uint16_t*>(s1.data) + (int64_t)b * s1.sb + (int64_t)t * s1.ss +
-                                 (int64_t)g * s1.sh + c * 8;
-            const uint4 x1 = stream16(p1);
-            if constexpr (FUSED) {
-                const uint16_t* pn = static_cast<const uint16_t*>(sn.data) + (int64_t)b * sn.sb +
-                                     (int64_t)t * sn.ss + (int64_t)g * sn.sh + c * 8;
-                const uint4 xn = stream16(pn);
-                const float4 wa = *reinterpret_cast<const float4*>(w1 + g * D + c * 8);
-                const float4 wb = *reinterpret_cast<const float4*>(w1 + g * D + c * 8 + 4);
-                const float4 na = *reinterpret_cast<const float4*>(wn + g * D + c * 8);
-                const float4 nb = *reinterpret_cast<const float4*>(wn + g * D + c * 8 + 4);
-                const float W1[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
-                const float WN[8] = {na.x, na.y, na.z, na.w, nb.x, nb.y, nb.z, nb.w};
-                const uint32_t u1[4] = {x1.x, x1.y, x1.z, x1.w}, un[4] = {xn.x, xn.y, xn.z, xn.w};
-                uint32_t r[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    r[i] = pack2(fmaf(W1[2 * i], bf16_lo(u1[i]), WN[2 * i] * bf16_lo(un[i])),
-                                 fmaf(W1[2 * i + 1], bf16_hi(u1[i]), WN[2 * i + 1] * bf16_hi(un[i])));
-                o = make_uint4(r[0], r[1], r[2], r[3]);
-            } else {
-                o = bf16x8_to_f16x8(x1);
-            }
-        }
-        return o;
-    };
-    for (int i = threadIdx.x; i < BN * CPR; i += 256) {
-        const int r = i / CPR, c = i - (i / CPR) * CPR;
-        const int t = j * BN + r;
-        *reinterpret_cast<uint4*>(kout + (int64_t)r * D + c * 8) = fuse8(a.k1, a.kn, a.kw1, a.kwn, t, c);
-        *reinterpret_cast<uint4*>(&sv[r * VP + c * 8]) = fuse8(a.v1, a.vn, a.vw1, a.vwn, t, c);
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < D * (BN / 8); i += 256) {
-        const int ch = i >> 3, c0 = (i & 7) * 8;
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            w[e] = (uint32_t)sv[vtile_key(c0 + 2 * e) * VP + ch] | ((uint32_t)sv[vtile_key(c0 + 2 * e + 1) * VP + ch] << 16);
-        *reinterpret_cast<uint4*>(vout + (int64_t)ch * BN + c0) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-}
 
 int rows_per_tile(int G) { return (G == 1 || G == 2 || G == 4 || G == 8) ? 256 / G : 0; }
 
@@ -150,7 +72,6 @@ template <int D, int MODE, int G>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
 {
     constexpr bool FUSED = MODE == kModeFused;
-    constexpr bool PRE = MODE == kModePre;
     constexpr int BM = 256 / G;          // query rows per workgroup
     constexpr int WPH = kWaves / G;      // waves per query head
     constexpr int DP = (D + 31) / 32 * 32;
@@ -163,8 +84,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
     constexpr int KPASS = (BN + RPP - 1) / RPP;
     constexpr int NVITEM = (D / 2) * (BN / 8);  // (channel pair, key octet) items
     static_assert(NVITEM <= kThreads, "one V item per thread");
-    constexpr int NVPRE = D * (BN / 8);         // 16-byte (channel, key octet) items of a binary16 tile
-    constexpr int VPASS = (NVPRE + kThreads - 1) / kThreads;
 
     __shared__ __attribute__((aligned(16))) uint16_t Kt[2][BN * KROW];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[2][DP * VROW];
@@ -262,7 +181,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
     // Per-tile buffer descriptors: the base advances by one tile of rows per
     // tile (scalar work) and the size shrinks with it, so the lanes keep
     // fixed offsets and rows past S-1 read as zero.
-    // (in fuse-once mode a.k1 describes the binary16 key buffer)
     const uint16_t* b_k1 = static_cast<const uint16_t*>(a.k1.data) + (int64_t)b * a.k1.sb + (int64_t)g * a.k1.sh;
     const uint16_t* b_v1 = static_cast<const uint16_t*>(a.v1.data) + (int64_t)b * a.v1.sb + (int64_t)g * a.v1.sh;
     const uint16_t* b_kn = b_k1;
@@ -295,35 +213,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
 
     uint4 xk1[KPASS], xkn[KPASS];
     uint32_t xv1[8], xvn[8];
-    // fuse-once mode: this thread's 16-byte items of the transposed value tile
-    uint4 xvp[VPASS];
-    uint32_t vpoff[VPASS];
-    const int nt_all = (a.S + BN - 1) / BN;
-    const uint16_t* b_vp = nullptr;
-    if constexpr (PRE) {
-        b_vp = reinterpret_cast<const uint16_t*>(static_cast<const char*>(a.pre) + a.pre_v_offset) +
-               ((int64_t)b * a.Hkv + g) * nt_all * D * BN;
-#pragma unroll
-        for (int p = 0; p < VPASS; ++p) {
-            const int i = tid + p * kThreads;
-            vpoff[p] = i < NVPRE ? (uint32_t)i * 16u : kOffNone;
-        }
-    }
 
     // The loads of the next tile, one at a time (index i < NKL: key loads).
     // They are spread over the k-steps of the score product instead of being
     // issued together at the start of a tile, where all waves of the
     // workgroup would stall on the vector-memory queue at once.
     constexpr int NSRCK = FUSED ? 2 : 1;
-    constexpr int NKL = KPASS * NSRCK, NL = NKL + (PRE ? VPASS : 8 * NSRCK);
+    constexpr int NKL = KPASS * NSRCK, NL = NKL + 8 * NSRCK;
     __amdgpu_buffer_rsrc_t nk1, nkn, nv1, nvn;
-    auto vpre_rsrc = [&](int j) { return slab_rsrc(b_vp + (int64_t)j * D * BN, (uint32_t)(D * BN * 2)); };
     auto next_rsrc = [&](int j) {
         nk1 = tile_rsrc(b_k1, a.k1.ss, j);
-        if constexpr (PRE)
-            nv1 = vpre_rsrc(j);
-        else
-            nv1 = tile_rsrc(b_v1, a.v1.ss, j);
+        nv1 = tile_rsrc(b_v1, a.v1.ss, j);
         nkn = nk1; nvn = nv1;
         if constexpr (FUSED) {
             nkn = tile_rsrc(b_kn, a.kn.ss, j);
@@ -335,8 +235,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
             const int p = i / NSRCK, s = i % NSRCK;
             if (s == 0) xk1[p] = ld16(nk1, koff1[p]);
             else xkn[p] = ld16(nkn, koffn[p]);
-        } else if constexpr (PRE) {
-            xvp[i - NKL] = ld16(nv1, vpoff[i - NKL]);
         } else {
             const int s8 = (i - NKL) / NSRCK, s = (i - NKL) % NSRCK;
             if (s == 0) xv1[s8] = ld4(nv1, voff1[s8]);
@@ -345,14 +243,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
     };
     auto issue_loads = [&](int j) {
         const __amdgpu_buffer_rsrc_t rk1 = tile_rsrc(b_k1, a.k1.ss, j);
-        if constexpr (PRE) {
-#pragma unroll
-            for (int p = 0; p < KPASS; ++p) xk1[p] = ld16(rk1, koff1[p]);
-            const __amdgpu_buffer_rsrc_t rv = vpre_rsrc(j);
-#pragma unroll
-            for (int p = 0; p < VPASS; ++p) xvp[p] = ld16(rv, vpoff[p]);
-            return;
-        }
         const __amdgpu_buffer_rsrc_t rv1 = tile_rsrc(b_v1, a.v1.ss, j);
         __amdgpu_buffer_rsrc_t rkn = rk1, rvn = rv1;
         if constexpr (FUSED) {
@@ -387,21 +277,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
                         r[i] = pack2(fuse_pair(pair_lo(x1[i], xn[i]), wk_hi[2 * i], wk_lo[2 * i]),
                                      fuse_pair(pair_hi(x1[i], xn[i]), wk_hi[2 * i + 1], wk_lo[2 * i + 1]));
                     o = make_uint4(r[0], r[1], r[2], r[3]);
-                } else if constexpr (PRE) {
-                    o = xk1[p];
                 } else {
                     o = bf16x8_to_f16x8(xk1[p]);
                 }
                 *reinterpret_cast<uint4*>(&Kt[nb][row * KROW + kc * 8]) = o;
             }
         }
-        if constexpr (PRE) {
-#pragma unroll
-            for (int p = 0; p < VPASS; ++p) {
-                const int i = tid + p * kThreads;
-                if (i < NVPRE) *reinterpret_cast<uint4*>(&Vt[nb][(i >> 3) * VROW + (i & 7) * 8]) = xvp[p];
-            }
-        } else if (v_active) {
+        if (v_active) {
             uint32_t lo[4], hv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -609,23 +491,9 @@ int launch_g(const PrefillArgs& a, hipStream_t st)
     return (int)hipGetLastError();
 }
 
-// fuse once, then attend over the binary16 tiles
-template <int D, bool FUSED>
-int launch_pre(PrefillArgs a, hipStream_t st)
-{
-    const int64_t nt = (a.S + BN - 1) / BN;
-    hipLaunchKernelGGL((prefuse_kernel<D, FUSED>), dim3((unsigned)(a.B * a.Hkv * nt)), dim3(256), 0, st, a);
-    const int rc = (int)hipGetLastError();
-    if (rc) return rc;
-    // the attention kernel reads the key buffer through the key view
-    a.k1 = View{a.pre, a.Hkv * nt * BN * D, D, nt * BN * D};
-    return launch_g<D, kModePre>(a, st);
-}
-
 template <int D>
 int launch_mode(const PrefillArgs& a, bool fused, hipStream_t st)
 {
-    if (a.pre) return fused ? launch_pre<D, true>(a, st) : launch_pre<D, false>(a, st);
     return fused ? launch_g<D, kModeFused>(a, st) : launch_g<D, kModeSingle>(a, st);
 }
 
@@ -633,21 +501,11 @@ int launch_mode(const PrefillArgs& a, bool fused, hipStream_t st)
 
 int prefill_rows_per_tile(int G) { return rows_per_tile(G); }
 
-int64_t prefill_pre_bytes(int64_t B, int64_t Hkv, int64_t S, int64_t D, int64_t* v_offset)
-{
-    const int64_t s64 = (S + BN - 1) / BN * BN;
-    const int64_t half = B * Hkv * s64 * D * 2;
-    const int64_t voff = (half + 255) / 256 * 256;
-    if (v_offset) *v_offset = voff;
-    return voff + half;
-}
-
 int launch_prefill(const PrefillArgs& a, bool fused, void* stream)
 {
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (a.B == 0 || a.S == 0) return 0;
     if ((int64_t)a.B * a.Hkv * a.n_qtiles > 0x7fffffff) return (int)hipErrorInvalidValue;
-    if (a.pre && (int64_t)a.B * a.Hkv * ((a.S + BN - 1) / BN) > 0x7fffffff) return (int)hipErrorInvalidValue;
     switch (a.D) {
     case 64: return launch_mode<64>(a, fused, st);
     case 80: return launch_mode<80>(a, fused, st);

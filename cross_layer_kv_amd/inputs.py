@@ -86,13 +86,14 @@ def _normal(shape, gen, device) -> torch.Tensor:
 
 def make_cache(B: int, S: int, H: int, D: int, dtype: torch.dtype, seed: int, device="cpu",
                layout: str = "bhsd", rotate: bool = True, pairing: str = "interleaved",
-               base: float = ROPE_BASE, chunk_elems: int = 1 << 27) -> torch.Tensor:
+               base: float = ROPE_BASE, chunk_elems: int = 1 << 27, pos0: int = 0) -> torch.Tensor:
     """One cache as a logical [B, S, H, D] tensor.
 
     layout 'bhsd' stores it head-major ([B, H, S, D] buffer, a permuted view is
     returned); 'bshd' stores it token-major.  Keys are rotated at positions
-    0..S-1 when ``rotate``.  Generation runs in slices of the batch/head axes
-    so the float64 temporary stays small.
+    pos0..pos0+S-1 when ``rotate`` (the raw draws do not depend on pos0).
+    Generation runs in slices of the batch/head axes so the float64 temporary
+    stays small.
     """
     gen = _gen(seed, device)
     if layout == "bhsd":
@@ -101,7 +102,7 @@ def make_cache(B: int, S: int, H: int, D: int, dtype: torch.dtype, seed: int, de
         buf = torch.empty(B, S, H, D, dtype=dtype, device=device)
     else:
         raise ValueError("layout is 'bhsd' or 'bshd'")
-    pos = torch.arange(S, dtype=torch.int64, device=device)
+    pos = torch.arange(S, dtype=torch.int64, device=device) + int(pos0)
     per_slice = max(1, chunk_elems // max(1, S * D))
     for b in range(B):
         for h0 in range(0, H, per_slice):
@@ -181,16 +182,18 @@ class LayerInputs:
 
 
 def make_layer(B, Sq, Sk, Hq, Hkv, D, dtype, seed, device="cpu", layout="bhsd",
-               pairing="interleaved", decode=True, seqlens_k=None) -> LayerInputs:
+               pairing="interleaved", decode=True, seqlens_k=None, pos0=0, tied=True) -> LayerInputs:
     """A full set of inputs.  Seeds of the parts are derived from ``seed`` so
-    that each part can also be regenerated on its own."""
-    k1 = make_cache(B, Sk, Hkv, D, dtype, seed * 16 + 1, device, layout, True, pairing)
-    kn = make_cache(B, Sk, Hkv, D, dtype, seed * 16 + 2, device, layout, True, pairing)
+    that each part can also be regenerated on its own.  ``pos0`` shifts every
+    position (keys at pos0..pos0+Sk-1, the decode query at pos0+Sk-1) while
+    keeping the raw draws; ``tied`` False draws untied key weights."""
+    k1 = make_cache(B, Sk, Hkv, D, dtype, seed * 16 + 1, device, layout, True, pairing, pos0=pos0)
+    kn = make_cache(B, Sk, Hkv, D, dtype, seed * 16 + 2, device, layout, True, pairing, pos0=pos0)
     v1 = make_cache(B, Sk, Hkv, D, dtype, seed * 16 + 3, device, layout, False, pairing)
     vn = make_cache(B, Sk, Hkv, D, dtype, seed * 16 + 4, device, layout, False, pairing)
     qpos = torch.full((Sq,), Sk - 1, dtype=torch.int64) if decode else torch.arange(Sq)
-    q = make_queries(B, Sq, Hq, D, dtype, seed * 16 + 5, device, qpos, pairing)
-    w = make_weights(Hkv, D, seed * 16 + 6, pairing, device=device)
+    q = make_queries(B, Sq, Hq, D, dtype, seed * 16 + 5, device, qpos + int(pos0), pairing)
+    w = make_weights(Hkv, D, seed * 16 + 6, pairing, tied=tied, device=device)
     sl = None
     if seqlens_k is not None:
         sl = torch.as_tensor(seqlens_k, dtype=torch.int32).to(device)

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define FKV_ABI_VERSION 5
+#define FKV_ABI_VERSION 6
 
 typedef enum {
     FKV_SUCCESS = 0,
@@ -170,54 +170,51 @@ fkv_status fkv_lite_decode(const fkv_params* params, const void* q,
                            void* stream);
 
 /*
- * Bytes of the optional fkv_prefill / fkv_lite_prefill workspace for
- * `params`: the layer's fused keys and values as IEEE binary16,
- * 4 * B * H_kv * S64 * D bytes plus alignment, S64 = seqlen_k rounded up to a
- * multiple of 64.  Returns 0 when params is invalid.
- */
-size_t fkv_prefill_workspace_size(const fkv_params* params);
-
-/*
  * fkv_prefill -- attention of a FusedKV reconstruction layer over a whole
  * prompt (S_q == S_k), bfloat16 data.  With causal = 1, query row p sees keys
- * t <= p.  Key and value tiles are fused in float32 and rounded once to IEEE
- * binary16 for the matrix-core products (bf16 queries convert exactly), and
- * the softmax probabilities are rounded to binary16 as well; softmax and
- * accumulation are float32.  Queries, fused keys and fused values must
- * therefore stay below 65504 in magnitude.  [Deck] frames "FusedKV learns two-source, channel-wise fusion"
+ * t <= p.  [Deck] frames "FusedKV learns two-source, channel-wise fusion"
  * (Eqs. (4)-(5)) and "Prefill improves while kernel throughput falls"
- * (the fused kernel's throughput, paper Fig. 4).
+ * (the fused kernel's throughput, paper Fig. 4); [Notes] section 2.3 (the
+ * reconstruction is built block by block inside the attention kernel).
  *
- * Without a workspace every attention workgroup fuses the key and value
- * tiles it reads, inside the kernel ([Notes] section 2.3).  With one, a first
- * kernel fuses each tile once into the workspace (binary16, the same
- * float32 fusion rounded once) and the attention kernel reads the fused
- * tiles: the prompt's tiles are otherwise fused once per query tile that
- * sees them.  The workspace holds only this call's data; calls that may run
- * concurrently need separate workspaces.
+ * Every attention workgroup fuses the 64-token key and value tiles it reads
+ * in float32 registers and keeps them in LDS only; nothing of the
+ * reconstruction is written to memory.  The matrix-core operands are IEEE
+ * binary16 (11 significant bits):
+ *   - fused key and value tiles are rounded once from float32;
+ *   - at D <= 96 the queries are multiplied by scale * log2(e) in float32 and
+ *     then rounded to binary16 (one rounding per element); at D = 128 the
+ *     bf16 queries convert to binary16 exactly and the scale is applied to
+ *     the float32 scores;
+ *   - softmax probabilities are rounded to binary16 after the exponential.
+ * Softmax, row sums and accumulation are float32.
+ * Limits that follow from binary16 operands:
+ *   - |scale*log2(e)*q| (D <= 96) or |q| (D = 128), |fused key| and |fused
+ *     value| must stay below 65504, else the call yields inf/NaN;
+ *   - each operand rounding carries a relative error of up to 2^-11, so a
+ *     score s (in log2 units) carries an absolute error that grows with |s|;
+ *     with softmax inputs spanning up to ~30 log2 units within a row the
+ *     output stays inside a 1e-2 relative error, while scores near 100 log2
+ *     units (a near one-hot softmax) exceed it (measured 2.6e-2).
  *
  *   q          device [B, S, H_q, D] bfloat16
  *   out        device [B, S, H_q, D] bfloat16
  *   lse        device float32 [B, H_q, S] or NULL
- *   workspace  device, 256-byte aligned, >= fkv_prefill_workspace_size(params)
- *              bytes; or NULL (workspace_bytes ignored) to fuse in the kernel.
- *              A shorter workspace returns FKV_ERROR_WORKSPACE.
  */
 fkv_status fkv_prefill(const fkv_params* params, const void* q,
                        fkv_cache k1, fkv_cache kn, fkv_cache v1, fkv_cache vn,
                        const fkv_fusion* fusion, void* out, float* lse,
-                       void* workspace, size_t workspace_bytes, void* stream);
+                       void* stream);
 
 /*
  * fkv_lite_prefill -- prefill over one key cache and one value cache
  * (FusedKV-Lite with (K^n, V^1), or the plain control with a layer's own
- * caches).  Arguments otherwise as fkv_prefill; with a workspace the first
- * kernel converts the tiles to binary16 once.
+ * caches).  The bf16 tiles convert to binary16 exactly (inside its range);
+ * arguments, arithmetic and limits otherwise as fkv_prefill.
  */
 fkv_status fkv_lite_prefill(const fkv_params* params, const void* q,
                             fkv_cache k_src, fkv_cache v_src, void* out,
-                            float* lse, void* workspace,
-                            size_t workspace_bytes, void* stream);
+                            float* lse, void* stream);
 
 /*
  * fkv_check_tied -- host-side check that key fusion weights are tied on RoPE

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib, B):
     assert set(names) == set(B.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.fkv_abi_version() == 5
+    assert lib.fkv_abi_version() == B.ABI_VERSION == 6
     for s in range(5):
         assert lib.fkv_status_string(s)
     assert lib.fkv_status_string(99) == b"unknown status"
@@ -71,11 +71,11 @@ def _decode(lib, B, p, q=FAKE, caches=None, fusion="default", ws_bytes=None, ws=
                           ctypes.byref(f) if f is not None else None, seqlens, out, lse, ws, ws_bytes, None)
 
 
-def _prefill(lib, B, p, q=FAKE, caches=None, fusion="default", ws=None, ws_bytes=0):
+def _prefill(lib, B, p, q=FAKE, caches=None, fusion="default"):
     c = caches or [_cache(B, p.head_dim, p.num_kv_heads, p.seqlen_k)] * 4
     f = _fusion(B) if fusion == "default" else fusion
     return lib.fkv_prefill(ctypes.byref(p), q, c[0], c[1], c[2], c[3],
-                           ctypes.byref(f) if f is not None else None, FAKE, None, ws, ws_bytes, None)
+                           ctypes.byref(f) if f is not None else None, FAKE, None, None)
 
 
 def test_decode_validation_codes(lib, B):
@@ -198,30 +198,11 @@ def test_prefill_validation_codes(lib, B):
     assert _prefill(lib, B, _params(B, sq=64, sk=64, hq=128, hkv=2)) == UNS  # G = 64: decode only
     p = _params(B, sq=64, sk=64)
     c = _cache(B)
-    assert lib.fkv_lite_prefill(ctypes.byref(p), FAKE, c, B.fkv_cache(0, 0, 64, 0), FAKE, None, None, 0,
-                                None) == INV
-    # fuse-once workspace: too short or misaligned
-    WS = B.FKV_ERROR_WORKSPACE
-    need = lib.fkv_prefill_workspace_size(ctypes.byref(p))
-    assert _prefill(lib, B, p, ws=FAKE, ws_bytes=need - 1) == WS
-    assert _prefill(lib, B, p, ws=FAKE + 16, ws_bytes=need) == WS
-    assert lib.fkv_lite_prefill(ctypes.byref(p), FAKE, c, c, FAKE, None, FAKE, need - 1, None) == WS
-    # an empty prompt needs no workspace and launches nothing
-    assert _prefill(lib, B, _params(B, batch=0, sq=64, sk=64), ws=FAKE, ws_bytes=0) == B.FKV_SUCCESS
-
-
-def test_prefill_workspace_size(lib, B):
-    """Binary16 fused keys [B, Hkv, S64, D], then the value tiles at the next
-    256-byte boundary: 2 * B * Hkv * S64 * D * 2 bytes in all."""
-    assert lib.fkv_prefill_workspace_size(None) == 0
-    assert lib.fkv_prefill_workspace_size(ctypes.byref(_params(B, sq=1, sk=64))) == 0   # not a prefill
-    assert lib.fkv_prefill_workspace_size(ctypes.byref(_params(B, batch=0, sq=64, sk=64))) == 0
-    for batch, s, hkv, d in ((2, 64, 2, 64), (1, 100, 3, 80), (4, 8192, 8, 128), (1, 1, 1, 96)):
-        s64 = (s + 63) // 64 * 64
-        half = batch * hkv * s64 * d * 2
-        want = (half + 255) // 256 * 256 + half
-        p = _params(B, batch=batch, sq=s, sk=s, hq=2 * hkv, hkv=hkv, d=d)
-        assert lib.fkv_prefill_workspace_size(ctypes.byref(p)) == want
+    assert lib.fkv_lite_prefill(ctypes.byref(p), FAKE, c, B.fkv_cache(0, 0, 64, 0), FAKE, None, None) == INV
+    assert lib.fkv_lite_prefill(ctypes.byref(p), FAKE + 8, c, c, FAKE, None, None) == INV
+    # an empty prompt launches nothing
+    assert lib.fkv_lite_prefill(ctypes.byref(_params(B, batch=0, sq=64, sk=64)), FAKE, c, c, FAKE, None,
+                                None) == B.FKV_SUCCESS
 
 
 def _grad(B, d=64, hkv=2, sk=64, ptr=FAKE):
@@ -329,3 +310,123 @@ def test_binding_refuses_host_tensors(B):
     w = [torch.zeros(2, 64)] * 4
     with pytest.raises(TypeError):
         B.fkv_decode(q, k, k, k, k, w, out=q, workspace=torch.zeros(4096, dtype=torch.uint8))
+
+
+# ---- the binding compares tensors with each other before any pointer is
+# handed to the library (shape, dtype, contiguity, extent); these run on host
+# tensors and must fail with ValueError / TypeError before the device check ----
+
+def _host_decode_args(Hq=4, Hkv=2, D=64, Sk=16, Bt=2, dtype=torch.bfloat16):
+    q = torch.zeros(Bt, 1, Hq, D, dtype=dtype)
+    caches = [torch.zeros(Bt, Sk, Hkv, D, dtype=dtype) for _ in range(4)]
+    w = [torch.zeros(Hkv, D) for _ in range(4)]
+    return q, caches, w
+
+
+def test_binding_refuses_mismatched_decode_tensors(B):
+    q, c, w = _host_decode_args()
+    ws = torch.zeros(4096, dtype=torch.uint8)
+
+    def call(**kw):
+        args = dict(q=q, k1=c[0], kn=c[1], v1=c[2], vn=c[3], weights=w, out=torch.zeros_like(q), workspace=ws)
+        args.update(kw)
+        B.fkv_decode(args.pop("q"), args.pop("k1"), args.pop("kn"), args.pop("v1"), args.pop("vn"),
+                     args.pop("weights"), **args)
+
+    bad = [
+        dict(kn=torch.zeros(2, 8, 2, 64, dtype=torch.bfloat16)),            # kn shorter than k1
+        dict(vn=torch.zeros(2, 16, 1, 64, dtype=torch.bfloat16)),           # other head count
+        dict(v1=torch.zeros(3, 16, 2, 64, dtype=torch.bfloat16)),           # other batch
+        dict(k1=torch.zeros(2, 16, 2, 64, dtype=torch.float32)),            # f32 cache, bf16 q
+        dict(k1=torch.zeros(2, 16, 64, 2, dtype=torch.bfloat16).transpose(2, 3)),  # strided channels
+        dict(weights=[torch.zeros(2, 32)] * 4),                             # weights not [Hkv, D]
+        dict(weights=[torch.zeros(2, 64, dtype=torch.float64)] * 4),        # weights not float32
+        dict(weights=[torch.zeros(2, 64)] * 3),                             # three weights
+        dict(out=torch.zeros(2, 1, 2, 64, dtype=torch.bfloat16)),           # out smaller than q
+        dict(out=torch.zeros(2, 1, 4, 64, dtype=torch.float32)),            # out dtype
+        dict(q=torch.zeros(2, 1, 64, 4, dtype=torch.bfloat16).transpose(2, 3)),    # non-contiguous q
+        dict(q=torch.zeros(2, 2, 4, 64, dtype=torch.bfloat16)),             # two query rows
+        dict(q=torch.zeros(2, 1, 5, 64, dtype=torch.bfloat16), out=torch.zeros(2, 1, 5, 64, dtype=torch.bfloat16)),
+        dict(lse=torch.zeros(2, 3)),                                        # lse smaller than B*Hq
+        dict(lse=torch.zeros(2, 4, dtype=torch.float64)),                   # lse dtype
+        dict(seqlens_k=torch.zeros(3, dtype=torch.int32)),                  # one length per batch row
+        dict(seqlens_k=torch.zeros(2, dtype=torch.int64)),
+        dict(workspace=torch.zeros(1024, dtype=torch.float32)),
+    ]
+    for kw in bad:
+        with pytest.raises((ValueError, TypeError)) as ei:
+            call(**kw)
+        assert "GPU tensor" not in str(ei.value), kw
+    # consistent host tensors pass every comparison and stop at the device check
+    with pytest.raises(TypeError, match="GPU tensor"):
+        call(lse=torch.zeros(2, 4), seqlens_k=torch.zeros(2, dtype=torch.int32))
+
+
+def test_binding_refuses_mismatched_prefill_tensors(B):
+    Bt, S, Hq, Hkv, D = 1, 32, 4, 2, 64
+    q = torch.zeros(Bt, S, Hq, D, dtype=torch.bfloat16)
+    c = [torch.zeros(Bt, S, Hkv, D, dtype=torch.bfloat16) for _ in range(4)]
+    w = [torch.zeros(Hkv, D) for _ in range(4)]
+    bad = [
+        dict(k1=torch.zeros(Bt, S - 1, Hkv, D, dtype=torch.bfloat16)),      # S_k != S_q
+        dict(lse=torch.zeros(Bt, Hq, S - 1)),                               # lse smaller than B*Hq*S
+        dict(out=torch.zeros(Bt, S, Hq, D - 8, dtype=torch.bfloat16)),
+    ]
+    for kw in bad:
+        args = dict(k1=c[0], kn=c[1], v1=c[2], vn=c[3], out=torch.zeros_like(q), lse=None)
+        args.update(kw)
+        with pytest.raises((ValueError, TypeError)) as ei:
+            B.fkv_prefill(q, args["k1"], args["kn"], args["v1"], args["vn"], w, out=args["out"], lse=args["lse"])
+        assert "GPU tensor" not in str(ei.value), kw
+    with pytest.raises(ValueError):
+        B.fkv_lite_prefill(q, c[0], torch.zeros(Bt, S, 1, D, dtype=torch.bfloat16), out=torch.zeros_like(q))
+    with pytest.raises(TypeError, match="GPU tensor"):
+        B.fkv_prefill(q, *c, w, out=torch.zeros_like(q), lse=torch.zeros(Bt, Hq, S))
+
+
+def test_binding_refuses_mismatched_backward_tensors(B):
+    Bt, S, Hq, Hkv, D = 1, 32, 4, 2, 64
+    q = torch.zeros(Bt, S, Hq, D, dtype=torch.bfloat16)
+    c = [torch.zeros(Bt, S, Hkv, D, dtype=torch.bfloat16) for _ in range(4)]
+    w = [torch.zeros(Hkv, D) for _ in range(4)]
+    lse = torch.zeros(Bt, Hq, S)
+    ws = torch.zeros(4096, dtype=torch.uint8)
+
+    def call(**kw):
+        a = dict(dq=torch.zeros_like(q), dk1=torch.zeros_like(c[0]), dkn=torch.zeros_like(c[1]),
+                 dv1=torch.zeros_like(c[2]), dvn=torch.zeros_like(c[3]), dweights=[torch.zeros(Hkv, D)] * 4,
+                 lse=lse, dout=torch.zeros_like(q))
+        a.update(kw)
+        B.fkv_prefill_backward(q, *c, w, torch.zeros_like(q), a.pop("lse"), a.pop("dout"), workspace=ws, **a)
+
+    bad = [dict(dq=torch.zeros(Bt, S, Hq, D, dtype=torch.float32)), dict(dout=torch.zeros(Bt, S - 1, Hq, D,
+                                                                                          dtype=torch.bfloat16)),
+           dict(dk1=torch.zeros(Bt, S, Hkv, D // 2, dtype=torch.bfloat16)), dict(lse=torch.zeros(Bt, Hq)),
+           dict(dweights=[torch.zeros(Hkv, D - 1)] * 4), dict(lse=None)]
+    for kw in bad:
+        with pytest.raises((ValueError, TypeError)) as ei:
+            call(**kw)
+        assert "GPU tensor" not in str(ei.value), kw
+    with pytest.raises(TypeError, match="GPU tensor"):
+        call()
+
+
+def test_binding_refuses_mismatched_kivi_tensors(B):
+    Bt, S, Hq, Hkv, D = 2, 40, 4, 2, 64
+    q = torch.zeros(Bt, 1, Hq, D, dtype=torch.bfloat16)
+    keys = [B.kivi_empty(Bt, S, Hkv, D, False, "cpu") for _ in range(2)]
+    vals = [B.kivi_empty(Bt, S, Hkv, D, True, "cpu") for _ in range(2)]
+    w = [torch.zeros(Hkv, D) for _ in range(4)]
+    ws = torch.zeros(4096, dtype=torch.uint8)
+    cases = [
+        (keys[0], keys[1], vals[0], B.kivi_empty(Bt, S + 64, Hkv, D, True, "cpu")),   # value blocks differ
+        (keys[0], B.kivi_empty(Bt, S - 1, Hkv, D, False, "cpu"), vals[0], vals[1]),   # key tokens differ
+        (keys[0], keys[1], keys[0], vals[1]),                                        # key cache as values
+        (keys[0], keys[1], vals[0], B.kivi_empty(Bt, S, Hkv + 1, D, True, "cpu")),   # head count
+    ]
+    for k1, kn, v1, vn in cases:
+        with pytest.raises((ValueError, TypeError)) as ei:
+            B.fkv_kivi_decode(q, k1, kn, v1, vn, w, out=torch.zeros_like(q), workspace=ws)
+        assert "GPU tensor" not in str(ei.value)
+    with pytest.raises(TypeError, match="GPU tensor"):
+        B.fkv_kivi_decode(q, keys[0], keys[1], vals[0], vals[1], w, out=torch.zeros_like(q), workspace=ws)

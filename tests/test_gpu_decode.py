@@ -208,6 +208,30 @@ def test_high_gqa_reference_max_raised_mid_sequence(D, monkeypatch):
     check(L, fused=False)
 
 
+@pytest.mark.xfail(reason="binary16 operand limit: scores near 100 log2 units carry ~2^-11 relative rounding "
+                          "of the fused keys and the queries, which moves exponents by ~0.05 and the output by "
+                          "2-3e-2; documented with fkv_decode for 64 query heads per KV head", strict=False)
+@pytest.mark.parametrize("D", [80, 128])
+def test_high_gqa_wide_score_range_binary16_limit(D, monkeypatch):
+    """Keys of 64-token tile j scaled by (1 + 3j) over five tiles (scores near
+    100 log2 units): the binary16 operand limit of the matrix-core decode,
+    kept as an expected failure with its measured error."""
+    monkeypatch.setenv("FKV_DECODE_SPLITS", "1")
+    say("decode high-GQA wide score range (keys x(1+3j) per tile) D=%d S=320" % D)
+    S = 320
+    L = inputs.make_layer(2, 1, S, 128, 2, D, torch.bfloat16, 980 + D, DEV)
+    ramp = (1.0 + 3.0 * (torch.arange(S, device=DEV) // 64).float()).to(torch.bfloat16).view(1, S, 1, 1)
+    for t in (L.k1, L.kn):
+        t.mul_(ramp)
+    out, lse = run_decode(L, fused=True)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    ro, rl = oracle_layer(L, fused=True)
+    e = rel_err(gpu_rows(out, 2, 128, 1, D), ro)
+    el = lse_err(lse.cpu().numpy().reshape(-1), rl)
+    say("  err=%.3e lse_err=%.3e" % (e, el))
+    assert e <= TOL[torch.bfloat16] and el <= TOL[torch.bfloat16], (e, el)
+
+
 def test_high_gqa_selector_weights_match_lite():
     """(a, a', b, b') = (0, 1, 1, 0): the fused kernel reads exactly K^n and
     V^1 and its fp16 tiles equal the Lite kernel's, bit for bit."""
@@ -280,3 +304,40 @@ def test_stack_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for i, (o, x) in enumerate(zip(outs, ref)):
             assert torch.equal(o, x), (r, i)
+
+
+# ---- post-RoPE fusion at long positions ([Deck] frame "Post-RoPE fusion
+# needs paired key weights", Eqs. (7)-(8); [Notes] section 2.4) ----
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("pairing", ["interleaved", "half"])
+def test_tied_weights_shift_invariant_at_long_positions(pairing, dtype):
+    """The same raw draws rotated at positions 0..S-1 (query at S-1) and at
+    131072-S..131071 (query at 131071).  With tied key weights every fused
+    score depends only on the query-key offset, so both decodes agree: in
+    float32 to float32 rounding (within 1e-4), in bfloat16 up to what the
+    different bf16 rounding of the rotated caches moves the oracle itself,
+    plus the 1e-2 tolerance.  Untied weights add a term in the absolute
+    position and the outputs move far apart.  Each GPU result is also checked
+    against the oracle."""
+    B, S, Hq, Hkv, D = 2, 1024, 16, 8, 128
+    shift = 131072 - S
+    say("decode tied-weight shift invariance pairing=%s dtype=%s B=%d S=%d D=%d shift=%d"
+        % (pairing, dtype, B, S, D, shift))
+    dev_gpu, dev_orc = {}, {}
+    for tied in (True, False):
+        outs, refs = [], []
+        for pos0 in (0, shift):
+            L = inputs.make_layer(B, 1, S, Hq, Hkv, D, dtype, 0x5EED, DEV, pairing=pairing, pos0=pos0,
+                                  tied=tied)
+            out, _ = check(L, fused=True)
+            outs.append(gpu_rows(out, B, Hq, 1, D))
+            refs.append(oracle_layer(L, fused=True)[0])
+        dev_gpu[tied] = rel_err(outs[1], outs[0])
+        dev_orc[tied] = rel_err(refs[1], refs[0])
+        say("  tied=%s shifted-vs-unshifted gpu %.3e oracle %.3e" % (tied, dev_gpu[tied], dev_orc[tied]))
+    if dtype == torch.float32:
+        assert dev_gpu[True] <= 1e-4
+    else:
+        assert dev_gpu[True] <= dev_orc[True] + TOL[dtype]
+    assert dev_gpu[False] >= 0.1 and dev_orc[False] >= 0.1

@@ -1,7 +1,6 @@
-"""GPU parity of fkv_prefill / fkv_lite_prefill (bf16 MFMA) against the fp64
-oracle, through the C ABI, with the tiles fused inside the attention kernel
-(no workspace) and fused once into a workspace first.  Every test prints its
-case before touching the GPU."""
+"""GPU parity of fkv_prefill / fkv_lite_prefill (bf16 data, binary16 matrix-core
+operands, tiles fused inside the attention kernel) against the fp64 oracle,
+through the C ABI.  Every test prints its case before touching the GPU."""
 import numpy as np
 import pytest
 import torch
@@ -14,39 +13,30 @@ DEV = "cuda:0"
 TOL = 1e-2
 
 
-def poisoned_workspace(L):
-    """A fuse-once workspace filled with NaN bytes, so that any position the
-    first kernel fails to write (padding rows included) shows up."""
-    ws = binding.prefill_workspace(L.q, L.k1)
-    ws.fill_(0xFF)
-    return ws
-
-
-def run_prefill(L, fused=True, causal=True, single=("kn", "v1"), ws=False):
+def run_prefill(L, fused=True, causal=True, single=("kn", "v1")):
     B, S, Hq, D = L.q.shape
     out = torch.full_like(L.q, float("nan"))
     lse = torch.full((B, Hq, S), float("nan"), dtype=torch.float32, device=DEV)
-    w = poisoned_workspace(L) if ws is True else (None if ws is False or ws is None else ws)
     if fused:
-        binding.fkv_prefill(L.q, L.k1, L.kn, L.v1, L.vn, L.weights, out=out, lse=lse, causal=causal, workspace=w)
+        binding.fkv_prefill(L.q, L.k1, L.kn, L.v1, L.vn, L.weights, out=out, lse=lse, causal=causal)
     else:
         binding.fkv_lite_prefill(L.q, getattr(L, single[0]), getattr(L, single[1]), out=out, lse=lse,
-                                 causal=causal, workspace=w)
+                                 causal=causal)
     torch.cuda.synchronize()
     return out, lse
 
 
-def check(L, fused=True, causal=True, single=("kn", "v1"), both=True):
-    """The oracle once; the kernel without a workspace and (both=True) with
-    a fuse-once workspace."""
+def errors(L, fused=True, causal=True, single=("kn", "v1")):
     B, S, Hq, D = L.q.shape
     ro, rl = oracle_layer(L, fused=fused, causal=causal, single=single)
-    for ws in ((False, True) if both else (False,)):
-        out, lse = run_prefill(L, fused, causal, single, ws=ws)
-        e = rel_err(gpu_rows(out, B, Hq, S, D), ro)
-        el = lse_err(lse.cpu().numpy().reshape(-1), rl)
-        say("  fuse_once=%s err=%.3e lse_err=%.3e" % (ws, e, el))
-        assert e <= TOL and el <= TOL, (ws, e, el)
+    out, lse = run_prefill(L, fused, causal, single)
+    return rel_err(gpu_rows(out, B, Hq, S, D), ro), lse_err(lse.cpu().numpy().reshape(-1), rl), out, lse
+
+
+def check(L, fused=True, causal=True, single=("kn", "v1")):
+    e, el, out, lse = errors(L, fused, causal, single)
+    say("  fused=%s err=%.3e lse_err=%.3e" % (fused, e, el))
+    assert e <= TOL and el <= TOL, (e, el)
     return out, lse
 
 
@@ -74,9 +64,7 @@ def test_reference_max_raised_mid_row(D, causal):
     in about half of the rows the second tile's max exceeds the running max
     by more than 8 log2 units, so the accumulator rescale (and, at D <= 96,
     the re-base of the score chains on a non-zero reference) runs in the
-    middle of a row.  Scores stay within ~30 log2 units: larger ones lose
-    more than the tolerance to binary16 operand rounding in any form of the
-    kernel (a CPU emulation of its roundings puts this case at 0.006-0.007)."""
+    middle of a row.  Scores stay within ~30 log2 units."""
     say("prefill mid-row max raises D=%d causal=%s S=320" % (D, causal))
     S = 320
     L = inputs.make_layer(1, S, S, 4, 2, D, torch.bfloat16, 500 + D, DEV, decode=False)
@@ -85,6 +73,34 @@ def test_reference_max_raised_mid_row(D, causal):
         t.mul_(ramp)
     check(L, fused=True, causal=causal)
     check(L, fused=False, causal=causal)
+
+
+def _wide_ramp_layer(D, seed):
+    """Keys of 64-key tile j scaled by (1 + 3j) over five tiles: late keys
+    reach ~13x their N(0,1) size, so causal rows see scores near 100 log2
+    units and a near one-hot softmax."""
+    S = 320
+    L = inputs.make_layer(1, S, S, 4, 2, D, torch.bfloat16, seed, DEV, decode=False)
+    ramp = (1.0 + 3.0 * (torch.arange(S, device=DEV) // 64).float()).to(torch.bfloat16).view(1, S, 1, 1)
+    for t in (L.k1, L.kn):
+        t.mul_(ramp)
+    return L
+
+
+@pytest.mark.xfail(reason="binary16 operand limit: scores near 100 log2 units carry ~2^-11 relative rounding "
+                          "of the fused keys and the queries, which moves exponents by ~0.05 and the output by "
+                          "2-3e-2 (measured 2.57e-2 at D = 80); documented with fkv_prefill", strict=False)
+@pytest.mark.parametrize("D", [80, 128])
+def test_wide_score_range_binary16_limit(D):
+    """The binary16 operand limit stated with fkv_prefill: a row whose scores
+    span ~100 log2 units.  Recorded as an expected failure with its measured
+    error; the finite-output part is asserted before the tolerance."""
+    say("prefill wide score range (keys x(1+3j) per tile) D=%d S=320" % D)
+    L = _wide_ramp_layer(D, 520 + D)
+    e, el, out, lse = errors(L, fused=True, causal=True)
+    say("  err=%.3e lse_err=%.3e (tolerance %.0e)" % (e, el, TOL))
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    assert e <= TOL and el <= TOL, (e, el)
 
 
 @pytest.mark.parametrize("D", [80, 128])
@@ -102,47 +118,18 @@ def test_layouts(layout):
     check(L, fused=True)
 
 
-@pytest.mark.parametrize("ws", [False, True])
-def test_selector_weights_equal_lite_bitwise(ws):
+def test_selector_weights_equal_lite_bitwise():
     """(0, 1, 1, 0) weights give K~ = K^n and V~ = V^1 exactly (also after the
     binary16 rounding of the fused tiles), so the fused kernel must equal the
     Lite kernel bit for bit."""
-    say("prefill selector weights vs lite fuse_once=%s" % ws)
+    say("prefill selector weights vs lite")
     L = inputs.make_layer(1, 333, 333, 8, 4, 80, torch.bfloat16, 600, DEV, decode=False)
     z = torch.zeros_like(L.weights[0])
     o = torch.ones_like(L.weights[0])
     L.weights = (z, o, o, z)
-    of, lf = run_prefill(L, fused=True, ws=ws)
-    ol, ll = run_prefill(L, fused=False, ws=ws)
+    of, lf = run_prefill(L, fused=True)
+    ol, ll = run_prefill(L, fused=False)
     assert torch.equal(of, ol) and torch.equal(lf, ll)
-
-
-@pytest.mark.parametrize("D", [64, 96, 128])
-def test_fuse_once_single_source_equals_in_kernel_bitwise(D):
-    """Single-source tiles convert from bf16 to binary16 exactly, so staging
-    them once in the workspace or in the kernel gives the same operands and
-    the same results bit for bit (S = 300 leaves a ragged last tile)."""
-    say("prefill lite fuse-once vs in-kernel D=%d S=300 G=2" % D)
-    L = inputs.make_layer(2, 300, 300, 8, 4, D, torch.bfloat16, 650 + D, DEV, decode=False)
-    o0, l0 = run_prefill(L, fused=False, ws=False)
-    o1, l1 = run_prefill(L, fused=False, ws=True)
-    assert torch.equal(o0, o1) and torch.equal(l0, l1)
-
-
-def test_fuse_once_workspace_reused_for_a_smaller_prompt():
-    """One workspace serves a call and then a call with a shorter prompt and
-    fewer heads; the second call's tiles overwrite what it reads."""
-    say("prefill fuse-once workspace reuse: S=520 Hkv=4 then S=130 Hkv=2 (D=96)")
-    big = inputs.make_layer(1, 520, 520, 8, 4, 96, torch.bfloat16, 660, DEV, decode=False)
-    ws = poisoned_workspace(big)
-    for L in (big, inputs.make_layer(1, 130, 130, 4, 2, 96, torch.bfloat16, 661, DEV, decode=False)):
-        B, S, Hq, D = L.q.shape
-        out, lse = run_prefill(L, fused=True, ws=ws)
-        ro, rl = oracle_layer(L, fused=True, causal=True)
-        e = rel_err(gpu_rows(out, B, Hq, S, D), ro)
-        el = lse_err(lse.cpu().numpy().reshape(-1), rl)
-        say("  S=%d err=%.3e lse_err=%.3e" % (S, e, el))
-        assert e <= TOL and el <= TOL
 
 
 def test_vanilla_control_on_own_caches():
@@ -152,38 +139,49 @@ def test_vanilla_control_on_own_caches():
 
 
 def _sample_rows(B, Hq, S, bm, rng, per_bh=16):
-    """Stratified rows: first/last rows, rows around tile boundaries and
+    """Stratified rows: first/last rows, rows around every tile boundary and
     random rows for a few (b, h) pairs."""
     rows = []
     bhs = [(0, 0), (B - 1, Hq - 1), (int(rng.integers(B)), int(rng.integers(Hq)))]
     for b, h in bhs:
         ps = {0, 1, S - 1, S - 2}
-        for t in range(bm, S, bm * 7):
+        for t in range(bm, S, bm):
             ps.update({t - 1, t})
         ps.update(int(x) for x in rng.integers(0, S, size=per_bh))
         rows += [(b * Hq + h) * S + p for p in sorted(ps) if 0 <= p < S]
     return np.array(sorted(set(rows)), dtype=np.int64)
 
 
+def _unit_rows(b, g, G, Hq, S):
+    """Every row of one (batch, KV head) unit: its G query heads x S rows."""
+    return np.array([(b * Hq + h) * S + p for h in range(g * G, (g + 1) * G) for p in range(S)], dtype=np.int64)
+
+
 def _full_size(B, S, Hq, Hkv, D, seed):
-    say("prefill full size B=%d S=%d Hq=%d Hkv=%d D=%d seed=%#x (sampled rows)" % (B, S, Hq, Hkv, D, seed))
+    """The benchmarked launch.  FusedKV: every row of two whole (batch, KV
+    head) units -- the first, and the last, which holds the last work item of
+    the XCD-aware mapping -- plus rows around every tile boundary of three
+    (b, h) pairs.  Lite: the stratified rows."""
+    say("prefill full size B=%d S=%d Hq=%d Hkv=%d D=%d seed=%#x" % (B, S, Hq, Hkv, D, seed))
+    G = Hq // Hkv
     L = inputs.make_layer(B, S, S, Hq, Hkv, D, torch.bfloat16, seed, DEV, decode=False)
     rng = np.random.default_rng(seed)
-    rows = _sample_rows(B, Hq, S, 256 // (Hq // Hkv), rng)
-    ws = binding.prefill_workspace(L.q, L.k1)
+    sample = _sample_rows(B, Hq, S, 256 // G, rng)
     for fused in (True, False):
-        ro, rl = oracle_layer(L, fused=fused, causal=True, rows=rows)
-        for w in (None, ws):
-            if w is not None:
-                w.fill_(0xFF)
-            out, lse = run_prefill(L, fused=fused, ws=w if w is not None else False)
-            assert torch.isfinite(out).all() and torch.isfinite(lse).all()
-            got = gpu_rows(out, B, Hq, S, D)[rows]
-            e = rel_err(got, ro)
-            el = lse_err(lse.cpu().numpy().reshape(-1)[rows], rl)
-            say("  fused=%s fuse_once=%s rows=%d err=%.3e lse_err=%.3e" % (fused, w is not None, rows.size, e, el))
+        out, lse = run_prefill(L, fused=fused)
+        assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+        got_all = gpu_rows(out, B, Hq, S, D)
+        lse_all = lse.cpu().numpy().reshape(-1)
+        sets = [("sample", sample)]
+        if fused:
+            sets += [("unit(0,0)", _unit_rows(0, 0, G, Hq, S)), ("unit(%d,%d)" % (B - 1, Hkv - 1),
+                                                                  _unit_rows(B - 1, Hkv - 1, G, Hq, S))]
+        for name, rows in sets:
+            ro, rl = oracle_layer(L, fused=fused, causal=True, rows=rows)
+            e = rel_err(got_all[rows], ro)
+            el = lse_err(lse_all[rows], rl)
+            say("  fused=%s %s rows=%d (G*S=%d) err=%.3e lse_err=%.3e" % (fused, name, rows.size, G * S, e, el))
             assert e <= TOL and el <= TOL
-    del ws
     del L
     torch.cuda.empty_cache()
 
