@@ -66,7 +66,9 @@ EXPORTS = ["fkv_abi_version", "fkv_status_string", "fkv_last_error", "fkv_decode
            "fkv_check_tied",
            "fkv_kivi_codes_bytes", "fkv_kivi_meta_bytes", "fkv_kivi_quantize", "fkv_kivi_decode",
            "fkv_kivi_lite_decode", "fkv_backward_workspace_size", "fkv_prefill_backward",
-           "fkv_lite_prefill_backward"]
+           "fkv_lite_prefill_backward", "fkv_decode_noalloc"]
+
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 _lib = None
 
@@ -92,6 +94,9 @@ def load_library(path: str = LIB_PATH):
     lib.fkv_decode.restype = ctypes.c_int
     lib.fkv_decode.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, fkv_cache, fkv_cache,
                                P(fkv_fusion), vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fkv_decode_noalloc.restype = ctypes.c_int
+    lib.fkv_decode_noalloc.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, fkv_cache, fkv_cache,
+                                       P(fkv_fusion), vp, vp, vp, vp]
     lib.fkv_lite_decode.restype = ctypes.c_int
     lib.fkv_lite_decode.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, vp, vp, vp, vp,
                                     ctypes.c_size_t, vp]
@@ -302,6 +307,20 @@ def fkv_decode(q, k1, kn, v1, vn, weights, *, out, workspace, lse=None, seqlens_
     _check(lib.fkv_decode(ctypes.byref(p), _dev(q, "q"), cache_view(k1), cache_view(kn), cache_view(v1),
                           cache_view(vn), ctypes.byref(f), _dev(seqlens_k, "seqlens_k"), _dev(out, "out"),
                           _dev(lse, "lse"), _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
+
+
+def fkv_decode_noalloc(q, k1, kn, v1, vn, weights, *, out, lse=None, seqlens_k=None, softmax_scale=0.0,
+                       stream=None):
+    """fkv_decode without a workspace: split partials go to the library's
+    static per-GPU scratch (fkv_decode_noalloc in include/fusedkv.h).  Calls
+    that may overlap on one GPU race on that scratch."""
+    lib = load_library()
+    _decode_checks(q, (k1, kn, v1, vn), ("k1", "kn", "v1", "vn"), out, lse, seqlens_k, None)
+    p = make_params(q, k1, softmax_scale=softmax_scale)
+    f = _fusion(weights, k1.shape[2], q.shape[3])
+    _check(lib.fkv_decode_noalloc(ctypes.byref(p), _dev(q, "q"), cache_view(k1), cache_view(kn), cache_view(v1),
+                                  cache_view(vn), ctypes.byref(f), _dev(seqlens_k, "seqlens_k"), _dev(out, "out"),
+                                  _dev(lse, "lse"), _stream(stream)))
 
 
 def fkv_lite_decode(q, k_src, v_src, *, out, workspace, lse=None, seqlens_k=None, softmax_scale=0.0,

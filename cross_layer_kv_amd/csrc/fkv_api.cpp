@@ -137,10 +137,12 @@ fkv::DecodePlan plan_decode(const fkv_params* p, bool fused, bool kivi = false)
     return pl;
 }
 
+// noalloc: the split partials go to the library's static device scratch
+// (fkv_decode_noalloc) instead of a caller workspace.
 fkv_status decode_common(const fkv_params* p, const void* q, const fkv_cache* caches,
                          const char* const* names, int ncaches, const fkv_fusion* fusion,
                          const int32_t* seqlens_k, void* out, float* lse, void* workspace,
-                         size_t workspace_bytes, void* stream)
+                         size_t workspace_bytes, void* stream, bool noalloc = false)
 {
     fkv_status s = check_shape(p);
     if (s) return s;
@@ -166,6 +168,14 @@ fkv_status decode_common(const fkv_params* p, const void* q, const fkv_cache* ca
             return fail(FKV_ERROR_INVALID_VALUE, "fusion weights are not 16-byte aligned");
     }
     const fkv::DecodePlan pl = plan_decode(p, fused);
+    if (noalloc && pl.total_bytes > 0) {
+        if (pl.total_bytes > fkv::kNoallocScratchBytes)
+            return fail(FKV_ERROR_WORKSPACE, "split partials need %zu bytes; the static scratch holds %zu "
+                        "(use fkv_decode with a workspace)", pl.total_bytes, fkv::kNoallocScratchBytes);
+        const int rc = fkv::scratch_pointer(&workspace);
+        if (rc) return fail(FKV_ERROR_LAUNCH, "static scratch address lookup failed (HIP error %d)", rc);
+        workspace_bytes = fkv::kNoallocScratchBytes;
+    }
     if (pl.total_bytes > 0) {
         if (!workspace || workspace_bytes < pl.total_bytes)
             return fail(FKV_ERROR_WORKSPACE, "workspace needs %zu bytes (got %zu)", pl.total_bytes,
@@ -536,6 +546,16 @@ fkv_status fkv_decode(const fkv_params* params, const void* q, fkv_cache k1, fkv
     static const char* const n[4] = {"k1", "kn", "v1", "vn"};
     return decode_common(params, q, c, n, 4, fusion, seqlens_k, out, lse, workspace,
                          workspace_bytes, stream);
+}
+
+fkv_status fkv_decode_noalloc(const fkv_params* params, const void* q, fkv_cache k1, fkv_cache kn,
+                              fkv_cache v1, fkv_cache vn, const fkv_fusion* fusion,
+                              const int32_t* seqlens_k, void* out, float* lse, void* stream)
+{
+    static_assert(fkv::kNoallocScratchBytes == FKV_NOALLOC_SCRATCH_BYTES, "scratch size in the header");
+    const fkv_cache c[4] = {k1, kn, v1, vn};
+    static const char* const n[4] = {"k1", "kn", "v1", "vn"};
+    return decode_common(params, q, c, n, 4, fusion, seqlens_k, out, lse, nullptr, 0, stream, true);
 }
 
 fkv_status fkv_lite_decode(const fkv_params* params, const void* q, fkv_cache k_src,

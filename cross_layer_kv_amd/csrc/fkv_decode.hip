@@ -37,10 +37,42 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "fkv_internal.h"
 
 namespace fkv {
+
+// ---- static scratch of the allocation-free decode entry point ----
+// Split partials of fkv_decode_noalloc live here instead of in a caller
+// workspace.  Each GPU the library runs on holds its own copy for the life of
+// the process.  In host code the array's name is only a stand-in for the
+// device symbol; its device address comes from hipGetSymbolAddress, taken once
+// per device with that device current, and only that address is handed to
+// kernels.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kNoallocScratchBytes];
+
+int scratch_pointer(void** out)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return (int)e;
+        if (!p) return (int)hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return 0;
+}
+
 namespace {
 
 constexpr int kCombineThreads = 256;

@@ -161,6 +161,14 @@ struct BwdArgs {
 // Keys per workgroup of the backward key-tile kernel (sizes the workspace).
 constexpr int kBwdKeyTile = 128;
 
+// Bytes of the static device scratch behind fkv_decode_noalloc (split-K
+// partials); it must match FKV_NOALLOC_SCRATCH_BYTES in fusedkv.h.
+constexpr size_t kNoallocScratchBytes = (size_t)8 << 20;
+
+// Device address of that scratch on the calling thread's current device,
+// looked up once per device.  Returns 0, or the HIP error code.
+int scratch_pointer(void** out);
+
 // Launchers (device code units).  They return 0 on success, else the HIP
 // error code of the failed launch.
 int launch_decode(const DecodeArgs& a, bool fused, int dtype, int waves, void* stream);

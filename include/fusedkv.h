@@ -157,6 +157,29 @@ fkv_status fkv_decode(const fkv_params* params, const void* q,
                       size_t workspace_bytes, void* stream);
 
 /*
+ * fkv_decode_noalloc -- fkv_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops and harnesses
+ * that forbid allocation.  It takes no workspace and allocates nothing: when
+ * the key axis is split, the split partials go to a static device scratch of
+ * FKV_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends (its device address is looked up once per device).
+ * The launch plan, kernels and results are those of fkv_decode with a
+ * workspace, bit for bit.  A call whose partials need more than the scratch
+ * (fkv_decode_workspace_size(params) > FKV_NOALLOC_SCRATCH_BYTES) returns
+ * FKV_ERROR_WORKSPACE before anything is enqueued.  The scratch needs no
+ * initialisation (each call writes every partial before reading it), but all
+ * calls on one GPU share it: calls that may overlap on one GPU (concurrent
+ * streams or threads) race and must be serialised by the caller.  Arguments
+ * and errors otherwise as fkv_decode.
+ */
+#define FKV_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+fkv_status fkv_decode_noalloc(const fkv_params* params, const void* q,
+                              fkv_cache k1, fkv_cache kn, fkv_cache v1,
+                              fkv_cache vn, const fkv_fusion* fusion,
+                              const int32_t* seqlens_k, void* out, float* lse,
+                              void* stream);
+
+/*
  * fkv_lite_decode -- one decode step over a single key cache and a single
  * value cache.  FusedKV-Lite passes (K^n, V^1) ([Deck] frame "Lite separates
  * the key source from the value source", Eq. (6)); plain attention of a
