@@ -158,24 +158,21 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
     const bool v_active = tid < NVITEM;
     const int vkey0 = (vo >> 1) * 16 + (vo & 1) * 4;   // octet's first key
 
-    // Fusion weights as bf16 pairs (w1 in the low half, w2 in the high half)
-    // split into hi + lo parts: w = hi + lo to ~2^-16 relative, so a fused
-    // element is two bf16 dot products of its (source 1, source n) pair.
-    uint32_t wk_hi[8], wk_lo[8], wv_hi[2], wv_lo[2];
+    // Float32 fusion weights of this thread's channels: a fused element is
+    // w1 * x1 + wn * xn in float32 (a multiply and an FMA on the widened bf16
+    // sources).  Plain FMAs co-issue with matrix-core work in flight on the
+    // SIMD; bf16 dot-product instructions do not on this part.
+    float wk1[8], wkn[8], wv1[2], wvn[2];
     if constexpr (FUSED) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            const float x = k_active ? a.kw1[g * D + kc * 8 + c] : 0.0f;
-            const float y = k_active ? a.kwn[g * D + kc * 8 + c] : 0.0f;
-            wk_hi[c] = pack2_bf16(x, y);
-            wk_lo[c] = pack2_bf16(x - bf16_lo(wk_hi[c]), y - bf16_hi(wk_hi[c]));
+            wk1[c] = k_active ? a.kw1[g * D + kc * 8 + c] : 0.0f;
+            wkn[c] = k_active ? a.kwn[g * D + kc * 8 + c] : 0.0f;
         }
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const float x = v_active ? a.vw1[g * D + 2 * vj + c] : 0.0f;
-            const float y = v_active ? a.vwn[g * D + 2 * vj + c] : 0.0f;
-            wv_hi[c] = pack2_bf16(x, y);
-            wv_lo[c] = pack2_bf16(x - bf16_lo(wv_hi[c]), y - bf16_hi(wv_hi[c]));
+            wv1[c] = v_active ? a.vw1[g * D + 2 * vj + c] : 0.0f;
+            wvn[c] = v_active ? a.vwn[g * D + 2 * vj + c] : 0.0f;
         }
     }
     // Per-tile buffer descriptors: the base advances by one tile of rows per
@@ -274,8 +271,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
                     uint32_t r[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        r[i] = pack2(fuse_pair(pair_lo(x1[i], xn[i]), wk_hi[2 * i], wk_lo[2 * i]),
-                                     fuse_pair(pair_hi(x1[i], xn[i]), wk_hi[2 * i + 1], wk_lo[2 * i + 1]));
+                        r[i] = pack2(fmaf(wk1[2 * i], bf16_lo(x1[i]), wkn[2 * i] * bf16_lo(xn[i])),
+                                     fmaf(wk1[2 * i + 1], bf16_hi(x1[i]), wkn[2 * i + 1] * bf16_hi(xn[i])));
                     o = make_uint4(r[0], r[1], r[2], r[3]);
                 } else {
                     o = bf16x8_to_f16x8(xk1[p]);
@@ -288,10 +285,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if constexpr (FUSED) {
-                    lo[i] = pack2(fuse_pair(pair_lo(xv1[2 * i], xvn[2 * i]), wv_hi[0], wv_lo[0]),
-                                  fuse_pair(pair_lo(xv1[2 * i + 1], xvn[2 * i + 1]), wv_hi[0], wv_lo[0]));
-                    hv[i] = pack2(fuse_pair(pair_hi(xv1[2 * i], xvn[2 * i]), wv_hi[1], wv_lo[1]),
-                                  fuse_pair(pair_hi(xv1[2 * i + 1], xvn[2 * i + 1]), wv_hi[1], wv_lo[1]));
+                    lo[i] = pack2(fmaf(wv1[0], bf16_lo(xv1[2 * i]), wvn[0] * bf16_lo(xvn[2 * i])),
+                                  fmaf(wv1[0], bf16_lo(xv1[2 * i + 1]), wvn[0] * bf16_lo(xvn[2 * i + 1])));
+                    hv[i] = pack2(fmaf(wv1[1], bf16_hi(xv1[2 * i]), wvn[1] * bf16_hi(xvn[2 * i])),
+                                  fmaf(wv1[1], bf16_hi(xv1[2 * i + 1]), wvn[1] * bf16_hi(xvn[2 * i + 1])));
                 } else {
                     lo[i] = pack2(bf16_lo(xv1[2 * i]), bf16_lo(xv1[2 * i + 1]));
                     hv[i] = pack2(bf16_hi(xv1[2 * i]), bf16_hi(xv1[2 * i + 1]));
@@ -428,11 +425,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
                         const float p0 = exp2_fast(sacc[kb][half * 8 + 2 * i] * pmul - psub);
                         const float p1 = exp2_fast(sacc[kb][half * 8 + 2 * i + 1] * pmul - psub);
                         w[i] = pack2(p0, p1);
-                        // row sum of the rounded probabilities the products use
-                        if (i & 1)
-                            l_run2 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[i]), kOnes2, l_run2, false);
-                        else
-                            l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[i]), kOnes2, l_run, false);
+                        // float32 row sums in two chains: plain adds co-issue
+                        // with the matrix-core products of the other block,
+                        // while dot-product instructions wait for the matrix
+                        // core on this part
+                        l_run += p0;
+                        l_run2 += p1;
                     }
                     pb[half] = as_f16x8(make_uint4(w[0], w[1], w[2], w[3]));
                 }
