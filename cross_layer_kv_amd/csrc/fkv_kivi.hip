@@ -584,7 +584,23 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
             const uint4 p16 = make_uint4(pack2(pv[0], pv[1]), pack2(pv[2], pv[3]), pack2(pv[4], pv[5]), pack2(pv[6], pv[7]));
 
             // ---- O += P' * codes, P' = p * (token's value scale), per group ----
-        if (l16 < NC) s_meta[wave][1][l16][hb] = y.vm;
+        if (l16 < NC) {
+            // A metadata chunk lists 8 tokens, t0 + 16 (e/4) + 4 hb + e%4 for
+            // entry e.  In the block that holds the end of the row, entries of
+            // tokens past it are zeroed: their p is 0, but 0 * inf or NaN
+            // metadata would still reach the sums.
+            uint4 vm = y.vm;
+            if (t0 + kGroup > t_end) {
+                uint32_t w[4];
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ta = t0 + 16 * ((2 * i) >> 2) + 4 * hb + ((2 * i) & 3);
+                    w[i] = (ta < t_end ? 0x0000ffffu : 0u) | (ta + 1 < t_end ? 0xffff0000u : 0u);
+                }
+                vm = make_uint4(vm.x & w[0], vm.y & w[1], vm.z & w[2], vm.w & w[3]);
+            }
+            s_meta[wave][1][l16][hb] = vm;
+        }
     #pragma unroll
             for (int s = 0; s < NS; ++s)
     #pragma unroll

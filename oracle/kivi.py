@@ -20,25 +20,17 @@ scheme, 4-bit, without its full-precision window of recent tokens):
   * mn is the group minimum and sc = (max - min) / 15, both stored as IEEE
     binary16; the code of x is rint((x - mn16) * (1 / sc16)) clamped to
     0..15, every step in float32 (so that a kernel taking the same decision
-    in float32 reproduces it), and 0 when sc16 == 0;
-  * two codes per byte, channel 2i in the low nibble and 2i+1 in the high one.
+    in float32 reproduces it), and 0 when sc16 == 0.
 Dequantisation mn16 + sc16 * q is exact in float64, and the attention of a
 layer over quantised sources is the plain oracle attention over the
 dequantised caches (fusion after dequantisation, as the pages compose them).
 
-Array layouts (those of the library's quantised caches; a storage choice,
-the pages fix none):
-  key codes    uint8   [B, H, S, D/2]            channel 2i low nibble, 2i+1 high
-  key meta     float16 [B, H, ceil(S/32), D]     (scale and minimum, one each)
-  value codes  uint8   [B, H, NB, D, 16]         NB = ceil(S/32) blocks of 32 tokens
-  value meta   float16 [B, H, NB, ceil(D/32), 32]
-Value codes are channel-major inside each 32-token block: the 16 bytes of
-(block, channel) are four 4-byte words w = 0..3, and word w holds the eight
-tokens  4w + (e % 4) + 16 (e // 4),  e = 0..7,  element e in nibble e // 2
-(bits 4 (e//2)) when e is even and in nibble 4 + e // 2 when e is odd.  The
-value scale and minimum of (block, channel group) list the block's 32 tokens
-in that same order, position 8w + e.  Tokens past S in the last block have
-code 0, scale 0 and minimum 0.
+Arrays here are the plain form of that definition, one code per element
+(how a library packs codes into bytes is its own storage choice):
+  key codes    uint8   [B, H, S, D]           0..15
+  key meta     float16 [B, H, ceil(S/32), D]  (scale, minimum) per token group and channel
+  value codes  uint8   [B, H, S, D]           0..15
+  value meta   float16 [B, H, S, ceil(D/32)]  (scale, minimum) per token and channel group
 """
 from __future__ import annotations
 
@@ -78,23 +70,10 @@ def _quantise_group(xs, axis):
     return q, np.squeeze(sc16, axis), np.squeeze(mn16, axis)
 
 
-def _pack(q):
-    """[..., D] codes 0..15 -> [..., D/2] bytes (even channel in the low nibble)."""
-    return (q[..., 0::2] | (q[..., 1::2] << 4)).astype(np.uint8)
-
-
-def _unpack(codes):
-    lo = codes & 0x0F
-    hi = codes >> 4
-    out = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), dtype=np.uint8)
-    out[..., 0::2] = lo
-    out[..., 1::2] = hi
-    return out
-
-
 def quantise_keys(k):
-    """k: [B, S, H, D] (bf16 bits or float32, any strides) -> (codes, scale,
-    minimum) with per-channel groups of 32 tokens."""
+    """k: [B, S, H, D] (bf16 bits or float32, any strides) -> (codes
+    [B, H, S, D], scale, minimum [B, H, ceil(S/32), D]): per-channel groups of
+    32 tokens."""
     x = np.ascontiguousarray(np.transpose(_as_f32(k), (0, 2, 1, 3)))  # [B, H, S, D]
     B, H, S, D = x.shape
     ng = (S + GROUP - 1) // GROUP
@@ -104,22 +83,12 @@ def quantise_keys(k):
     for j in range(ng):
         t0, t1 = j * GROUP, min(S, (j + 1) * GROUP)
         q[:, :, t0:t1], sc[:, :, j], mn[:, :, j] = _quantise_group(x[:, :, t0:t1], axis=2)
-    return _pack(q), sc, mn
-
-
-def block_token(w, e):
-    """Token (within its 32-token block) of element e of word w."""
-    return 4 * w + (e % 4) + 16 * (e // 4)
-
-
-def _nibble(e):
-    """Nibble position of element e inside its 4-byte word."""
-    return e // 2 if e % 2 == 0 else 4 + e // 2
+    return q, sc, mn
 
 
 def quantise_values(v):
-    """v: [B, S, H, D] -> (codes, scale, minimum) with per-token groups of 32
-    channels, in the block layout described above."""
+    """v: [B, S, H, D] -> (codes [B, H, S, D], scale, minimum
+    [B, H, S, ceil(D/32)]): per-token groups of 32 channels."""
     x = np.ascontiguousarray(np.transpose(_as_f32(v), (0, 2, 1, 3)))  # [B, H, S, D]
     B, H, S, D = x.shape
     ng = (D + GROUP - 1) // GROUP
@@ -129,68 +98,22 @@ def quantise_values(v):
     for c in range(ng):
         d0, d1 = c * GROUP, min(D, (c + 1) * GROUP)
         q[..., d0:d1], sc[..., c], mn[..., c] = _quantise_group(x[..., d0:d1], axis=3)
-    return _to_blocks(q, sc, mn)
+    return q, sc, mn
 
 
-def _to_blocks(q, sc, mn):
-    """Token-major codes [B, H, S, D] (0..15) and per-token metadata
-    [B, H, S, ng] -> the block layout."""
-    B, H, S, D = q.shape
-    ng = sc.shape[-1]
-    nb = (S + GROUP - 1) // GROUP
-    codes = np.zeros((B, H, nb, D, 16), dtype=np.uint8)
-    bsc = np.zeros((B, H, nb, ng, GROUP), dtype=np.float16)
-    bmn = np.zeros((B, H, nb, ng, GROUP), dtype=np.float16)
-    for j in range(nb):
-        for w in range(4):
-            for e in range(8):
-                t = j * GROUP + block_token(w, e)
-                if t >= S:
-                    continue
-                p = _nibble(e)
-                byte = 4 * w + p // 2
-                shift = 4 * (p % 2)
-                codes[:, :, j, :, byte] |= (q[:, :, t, :] << shift).astype(np.uint8)
-                bsc[:, :, j, :, 8 * w + e] = sc[:, :, t, :]
-                bmn[:, :, j, :, 8 * w + e] = mn[:, :, t, :]
-    return codes, bsc, bmn
-
-
-def value_tokens(codes, sc, mn, S):
-    """Block layout -> token-major codes [B, H, S, D] (0..15) and per-token
-    scale and minimum [B, H, S, ng]."""
-    B, H, nb, D, _ = codes.shape
-    ng = sc.shape[3]
-    q = np.zeros((B, H, nb * GROUP, D), dtype=np.uint8)
-    s = np.zeros((B, H, nb * GROUP, ng), dtype=np.float16)
-    m = np.zeros((B, H, nb * GROUP, ng), dtype=np.float16)
-    for j in range(nb):
-        for w in range(4):
-            for e in range(8):
-                t = j * GROUP + block_token(w, e)
-                p = _nibble(e)
-                q[:, :, t, :] = (codes[:, :, j, :, 4 * w + p // 2] >> (4 * (p % 2))) & 0x0F
-                s[:, :, t, :] = sc[:, :, j, :, 8 * w + e]
-                m[:, :, t, :] = mn[:, :, j, :, 8 * w + e]
-    return q[:, :, :S], s[:, :, :S], m[:, :, :S]
-
-
-def dequantise_keys(codes, sc, mn):
-    """-> float64 [B, S, H, D]: mn16 + sc16 * q, exact."""
-    q = _unpack(codes).astype(np.float64)  # [B, H, S, D]
+def dequantise_keys(q, sc, mn):
+    """-> float64 [B, S, H, D]: mn16 + sc16 * q of each token's group, exact."""
     S = q.shape[2]
     tok_group = np.arange(S) // GROUP
     x = mn.astype(np.float64)[:, :, tok_group, :] + sc.astype(np.float64)[:, :, tok_group, :] * q
     return np.transpose(x, (0, 2, 1, 3))
 
 
-def dequantise_values(codes, sc, mn, S):
-    """Block layout of an S-token value cache -> float64 [B, S, H, D]."""
-    q, s, m = value_tokens(codes, sc, mn, S)
-    q = q.astype(np.float64)
+def dequantise_values(q, sc, mn):
+    """-> float64 [B, S, H, D]: mn16 + sc16 * q of each channel's group, exact."""
     D = q.shape[3]
     ch_group = np.arange(D) // GROUP
-    x = m.astype(np.float64)[..., ch_group] + s.astype(np.float64)[..., ch_group] * q
+    x = mn.astype(np.float64)[..., ch_group] + sc.astype(np.float64)[..., ch_group] * q
     return np.transpose(x, (0, 2, 1, 3))
 
 
@@ -200,15 +123,15 @@ def _q_f64(q):
 
 def attend(q, k1, v1, kn=None, vn=None, **kw):
     """Oracle attention over quantised sources.  k1/kn are (codes, scale,
-    minimum) key triples, v1/vn value triples; keyword arguments as
-    ``oracle.attend`` (weights, causal, scale, seqlens_k, rows)."""
+    minimum) key triples, v1/vn value triples, in the plain form above;
+    keyword arguments as ``oracle.attend`` (weights, causal, scale,
+    seqlens_k, rows)."""
     qd = _q_f64(q)
     K1 = dequantise_keys(*k1)
-    S = K1.shape[1]
-    V1 = dequantise_values(*v1, S)
+    V1 = dequantise_values(*v1)
     if kn is None:
         return oracle.attend(qd, K1, V1, **kw)
-    return oracle.attend(qd, K1, V1, dequantise_keys(*kn), dequantise_values(*vn, S), **kw)
+    return oracle.attend(qd, K1, V1, dequantise_keys(*kn), dequantise_values(*vn), **kw)
 
 
 def payload_bytes(L, S, Hkv, D, method, bits):
@@ -218,9 +141,10 @@ def payload_bytes(L, S, Hkv, D, method, bits):
 
 
 def metadata_bytes(S, Hkv, D, B=1):
-    """fp16 scale and minimum of one quantised source: keys and values have
-    the same count when S and D are multiples of 32 (value metadata is
-    stored per 32-token block, so a partial last block counts whole)."""
+    """fp16 scale and minimum of one quantised source, for a store that keeps
+    value metadata per whole 32-token block (so a partial last block counts
+    whole): keys and values have the same count when S and D are multiples
+    of 32."""
     keys = B * Hkv * ((S + GROUP - 1) // GROUP) * D * 2 * 2
     values = B * Hkv * ((S + GROUP - 1) // GROUP) * GROUP * ((D + GROUP - 1) // GROUP) * 2 * 2
     return keys, values

@@ -341,3 +341,37 @@ def test_tied_weights_shift_invariant_at_long_positions(pairing, dtype):
     else:
         assert dev_gpu[True] <= dev_orc[True] + TOL[dtype]
     assert dev_gpu[False] >= 0.1 and dev_orc[False] >= 0.1
+
+
+# ---- rows past a sequence's length are never read (or never reach a sum) ----
+
+def _poison_tails(L, value):
+    """Fill every cache row t >= seqlens_k[b] of every source with `value`,
+    inside the tensors (the caches keep their shape and strides)."""
+    sl = L.seqlens_k.cpu().tolist()
+    for name in ("k1", "kn", "v1", "vn"):
+        t = getattr(L, name)
+        for b, n in enumerate(sl):
+            t[b, n:].fill_(value)
+
+
+@pytest.mark.parametrize("G,D,splits", [(2, 96, "1"), (2, 128, "7"), (8, 80, "3"), (64, 128, "1"), (64, 80, "5")])
+def test_nan_rows_past_seqlens_are_ignored(G, D, splits, monkeypatch):
+    """Ragged rows whose cache entries past seqlens_k hold NaN (and +inf in a
+    second run): the result equals the run on clean caches bit for bit and
+    matches the oracle, for FusedKV and Lite, direct and split paths, the
+    G <= 8 kernel (predicated loads) and the 64-head matrix-core kernel
+    (rows past the end read through the buffer range check)."""
+    monkeypatch.setenv("FKV_DECODE_SPLITS", splits)
+    Hkv = 2 if G == 64 else 4
+    say("decode NaN tails G=%d D=%d splits=%s" % (G, D, splits))
+    L = inputs.make_layer(4, 1, 700, G * Hkv, Hkv, D, torch.bfloat16, 1700 + G + D, DEV,
+                          seqlens_k=[700, 0, 131, 64])
+    clean = {f: run_decode(L, fused=f) for f in (True, False)}
+    for value in (float("nan"), float("inf")):
+        _poison_tails(L, value)
+        for fused in (True, False):
+            out, lse = run_decode(L, fused=fused)
+            assert torch.equal(out, clean[fused][0]) and torch.equal(lse, clean[fused][1]), (value, fused)
+    out, lse = check(L, fused=True)
+    assert torch.isfinite(out).all()

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import kivi_layout as kl
 from cross_layer_kv_amd import binding, inputs
 from oracle import kivi
 from parity import TOL, gpu_rows, lse_err, rel_err, say
@@ -28,10 +29,17 @@ def oracle_q4(L, name, batch=None):
     return kivi.quantise_keys(a) if name in KEYS else kivi.quantise_values(a)
 
 
+def to_lib(trip, is_value):
+    """The oracle's plain arrays in the library's packed storage."""
+    return kl.values_to_lib(*trip) if is_value else kl.keys_to_lib(*trip)
+
+
 def upload(trip, is_value):
-    codes, sc, mn = trip
+    """Oracle plain triple -> device cache in the library's storage."""
+    codes, sc, mn = to_lib(trip, is_value)
+    S = trip[0].shape[2]
     return binding.Q4Cache(torch.from_numpy(codes).to(DEV), torch.from_numpy(sc).to(DEV),
-                           torch.from_numpy(mn).to(DEV), is_value)
+                           torch.from_numpy(mn).to(DEV), is_value, S)
 
 
 def quantised_layer(L):
@@ -85,7 +93,9 @@ def check(L, host, dev, fused=True, single=("kn", "v1"), tol=None):
 
 
 def same_q4(got: binding.Q4Cache, ref):
-    codes, sc, mn = ref
+    """The GPU quantiser's packed cache equals the oracle's plain triple (ref)
+    packed into the same storage, bit for bit."""
+    codes, sc, mn = to_lib(ref, got.is_value)
     assert np.array_equal(got.codes.cpu().numpy(), codes)
     assert np.array_equal(got.scale.cpu().numpy().view(np.uint16), sc.view(np.uint16))
     assert np.array_equal(got.minv.cpu().numpy().view(np.uint16), mn.view(np.uint16))
@@ -128,7 +138,7 @@ def test_quantiser_degenerate_groups():
     assert torch.all(kc.codes[:, :, 64] == 0)
     vc = binding.fkv_kivi_quantize(xd, True)
     torch.cuda.synchronize()
-    q, _, _ = kivi.value_tokens(vc.codes.cpu().numpy(), vc.scale.cpu().numpy(), vc.minv.cpu().numpy(), 65)
+    q, _, _ = kl.values_from_lib(vc.codes.cpu().numpy(), vc.scale.cpu().numpy(), vc.minv.cpu().numpy(), 65)
     assert np.all(q[0, 0, 32:48, 0::2] == 0) and np.all(q[0, 0, 32:48, 1::2] == 15)
 
 
@@ -164,6 +174,42 @@ def test_decode_forced_splits_and_ragged(splits, monkeypatch):
     out, lse = check(L, host, dev, fused=True)
     assert torch.all(out[1] == 0) and torch.all(torch.isneginf(lse[1]))
     check(L, host, dev, fused=False)
+
+
+def test_decode_poisoned_metadata_past_seqlens(monkeypatch):
+    """Ragged rows whose 4-bit caches hold garbage past seqlens_k: NaN and
+    +inf value scales and minima for every dead token, NaN key metadata for
+    key groups wholly past the end, all-ones codes for dead tokens.  Dead
+    tokens get probability 0 and their metadata must not reach the sums
+    (0 * NaN): the result equals the clean run bit for bit."""
+    monkeypatch.setenv("FKV_DECODE_SPLITS", "3")
+    say("kivi decode poisoned metadata past seqlens B=4 S=700 D=96 G=2")
+    L = inputs.make_layer(4, 1, 700, 8, 4, 96, torch.bfloat16, 1480, DEV, seqlens_k=[700, 0, 131, 77])
+    host, dev = quantised_layer(L)
+    clean = {f: run(L, dev, fused=f) for f in (True, False)}
+    sl = L.seqlens_k.cpu().tolist()
+    for value in (float("nan"), float("inf")):
+        for n in ("k1", "kn", "v1", "vn"):
+            c = dev[n]
+            for b, ln in enumerate(sl):
+                if n in KEYS:
+                    c.codes[b, :, ln:] = 0xFF
+                    g0 = (ln + 31) // 32           # first key group wholly past the end
+                    c.scale[b, :, g0:] = value
+                    c.minv[b, :, g0:] = value
+                else:
+                    # value metadata lists the 32 tokens of a block in the
+                    # header's order: token 4w + e%4 + 16(e//4) at 8w + e
+                    for j in range(ln // 32, c.codes.shape[2]):
+                        for w in range(4):
+                            for e in range(8):
+                                if j * 32 + kl.block_token(w, e) >= ln:
+                                    c.scale[b, :, j, :, 8 * w + e] = value
+                                    c.minv[b, :, j, :, 8 * w + e] = value
+        for fused in (True, False):
+            out, lse = run(L, dev, fused=fused)
+            assert torch.equal(out, clean[fused][0]) and torch.equal(lse, clean[fused][1]), (value, fused)
+    check(L, host, dev, fused=True)
 
 
 def test_decode_empty_cache():

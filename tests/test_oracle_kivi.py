@@ -39,8 +39,7 @@ def test_key_codes_on_exact_grid():
     rng = np.random.default_rng(1)
     x, k, mn, sc = _grid_keys(rng, 2, 70, 3, 64)   # groups of 32, 32 and 6 tokens
     codes, s16, m16 = kivi.quantise_keys(_bf16_bits(x))
-    q = kivi._unpack(codes)
-    assert np.array_equal(q, k)
+    assert np.array_equal(codes, k)
     assert np.array_equal(s16.astype(np.float64), np.repeat(sc[:, :, None, :], 3, axis=2))
     assert np.array_equal(m16.astype(np.float64), np.repeat(mn[:, :, None, :], 3, axis=2))
     assert np.array_equal(kivi.dequantise_keys(codes, s16, m16), x.astype(np.float64))
@@ -62,10 +61,9 @@ def test_value_codes_on_exact_grid():
         x[..., d0:d1] = mn + sc * k[..., d0:d1]
     xs = np.transpose(x, (0, 2, 1, 3)).astype(np.float32)
     codes, s16, m16 = kivi.quantise_values(_bf16_bits(xs))
-    assert codes.shape == (B, H, 1, D, 16) and s16.shape == (B, H, 1, 3, 32)
-    q, st, _ = kivi.value_tokens(codes, s16, m16, S)
-    assert np.array_equal(q, k) and st.shape == (B, H, S, 3)
-    assert np.array_equal(kivi.dequantise_values(codes, s16, m16, S), xs.astype(np.float64))
+    assert codes.shape == (B, H, S, D) and s16.shape == (B, H, S, 3)
+    assert np.array_equal(codes, k)
+    assert np.array_equal(kivi.dequantise_values(codes, s16, m16), xs.astype(np.float64))
 
 
 def test_constant_group_has_zero_scale():
@@ -92,10 +90,9 @@ def test_error_bound_on_random_data(axis):
         gmax = np.repeat(grp_max, 32, axis=1)
     else:
         codes, s16, m16 = kivi.quantise_values(x)
-        xh = kivi.dequantise_values(codes, s16, m16, 96)
-        _, st16, mt16 = kivi.value_tokens(codes, s16, m16, 96)
-        s = np.repeat(st16.astype(np.float64), 32, axis=3).transpose(0, 2, 1, 3)
-        m = np.repeat(mt16.astype(np.float64), 32, axis=3).transpose(0, 2, 1, 3)
+        xh = kivi.dequantise_values(codes, s16, m16)
+        s = np.repeat(s16.astype(np.float64), 32, axis=3).transpose(0, 2, 1, 3)
+        m = np.repeat(m16.astype(np.float64), 32, axis=3).transpose(0, 2, 1, 3)
         gmin = np.repeat(x.reshape(2, 96, 4, 4, 32).min(axis=4), 32, axis=3)
         gmax = np.repeat(x.reshape(2, 96, 4, 4, 32).max(axis=4), 32, axis=3)
     # fp16 rounding of the stored minimum and scale (relative 2^-11)
@@ -105,8 +102,7 @@ def test_error_bound_on_random_data(axis):
     err = np.abs(xh - x)
     assert np.all(err <= s / 2 * (1 + 1e-5) + slack + 1e-12)
     # and the codes use the whole range
-    q = kivi._unpack(codes) if axis == "keys" else kivi.value_tokens(codes, s16, m16, 96)[0]
-    assert q.min() == 0 and q.max() == 15
+    assert codes.min() == 0 and codes.max() == 15
 
 
 def test_attention_over_grid_caches_equals_plain_attention():
@@ -127,7 +123,7 @@ def test_attention_over_grid_caches_equals_plain_attention():
     # compare against the dequantised caches, and check keys exactly
     assert np.array_equal(kivi.dequantise_keys(*kq), xk.astype(np.float64))
     o_q, l_q = kivi.attend(qb, kq, vq)
-    o_p, l_p = oracle.attend(kivi._q_f64(qb), kivi.dequantise_keys(*kq), kivi.dequantise_values(*vq, S))
+    o_p, l_p = oracle.attend(kivi._q_f64(qb), kivi.dequantise_keys(*kq), kivi.dequantise_values(*vq))
     assert np.array_equal(o_q, o_p) and np.array_equal(l_q, l_p)
     o_b, l_b = oracle.attend(qb, kb, vb)
     # keys exact; values within the value quantiser's bound, which moves O by
@@ -157,41 +153,3 @@ def test_metadata_counts():
     k, v = kivi.metadata_bytes(S, Hkv, D)
     payload = S * Hkv * D // 2
     assert k == v == payload // 4
-
-
-def test_nibble_order():
-    """Two codes per byte: channel 2i in the low nibble, 2i+1 in the high."""
-    q = np.array([[1, 2, 15, 0, 7, 9]], np.uint8)
-    assert list(kivi._pack(q)[0]) == [0x21, 0x0F, 0x97]
-    assert np.array_equal(kivi._unpack(kivi._pack(q)), q)
-
-
-def test_value_block_layout():
-    """Value codes are channel-major per 32-token block: word w of (block,
-    channel) holds tokens 4w + e%4 + 16(e//4), element e in nibble e//2 (even
-    e) or 4 + e//2 (odd e); metadata lists the tokens in the same order.
-    Built by hand for single marked tokens, a 37-token cache (one full block
-    and a 5-token tail whose padding is zero)."""
-    B, S, H, D = 1, 37, 1, 32
-    x = np.zeros((B, S, H, D), np.float32)
-    # channel 3 of token t = 15 and token 32 + 18 -> is past S; use 33
-    x[0, :, 0, 3] = 0.0
-    x[0, 15, 0, :] = np.arange(D) * 0.5      # token 15: codes 0..15 ramp over 32 channels
-    x[0, 33, 0, :] = -np.arange(D) * 0.25    # token 33: codes 15..0
-    codes, sc, mn = kivi.quantise_values(x)
-    assert codes.shape == (1, 1, 2, D, 16) and sc.shape == (1, 1, 2, 1, 32)
-    # token 15 = 4w + e%4 + 16(e//4) with w = 3, e = 3 -> nibble 4 + 1 = 5 of
-    # word 3 -> byte 12 + 2, high half; its code at channel c is rint(c / 2 * 15 / 15.5)
-    q15 = np.rint(np.arange(D) * 0.5 / np.float32(15.5 / 15)).clip(0, 15)
-    got = (codes[0, 0, 0, :, 14] >> 4) & 0xF
-    assert np.array_equal(got, q15.astype(np.uint8))
-    assert sc[0, 0, 0, 0, 8 * 3 + 3] == np.float16(15.5 / 15) and sc[0, 0, 0, 0, 0] == 0
-    # token 33 -> block 1, position 1 = (w 0, e 1): nibble 4 of word 0 -> byte 2, low half
-    got33 = codes[0, 0, 1, :, 2] & 0xF
-    assert got33[0] == 15 and got33[-1] == 0
-    # padding tokens (37..63) have zero codes and metadata
-    assert np.all(sc[0, 0, 1, 0, [8 * w + e for w in range(4) for e in range(8)
-                                   if 32 + kivi.block_token(w, e) >= S]] == 0)
-    # the inverse recovers the token-major view
-    q, _, _ = kivi.value_tokens(codes, sc, mn, S)
-    assert q.shape == (1, 1, S, D) and np.array_equal(q[0, 0, 15], q15.astype(np.uint8))
