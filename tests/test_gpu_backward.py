@@ -1,18 +1,21 @@
 """GPU parity of fkv_prefill_backward / fkv_lite_prefill_backward against the
 fp64 backward oracle (oracle/backward.py), through the C ABI.  The forward
 output O and LSE the backward call consumes come from the forward oracle
-(O rounded to bfloat16, LSE to float32), so that the rounding of O -- an
-input of the backward call -- is the same one the rounding-budget model
-sees; the training flow, with O and LSE from the library's own fkv_prefill,
-has tests of its own.  Every test prints its case before touching the GPU.
+(O rounded to bfloat16, LSE to float32); the training flow, with O and LSE
+from the library's own fkv_prefill, has tests of its own.  Every test prints
+its case before touching the GPU.
 
-Tolerance, derived from the arithmetic (tests/bwd_rounding.py): per output
-tensor, the elementwise error max|x - r| / max(|r|, rms(r)) must stay within
-max(1e-2, 2 x the error of the same formulas evaluated with bfloat16
-rounding at the kernels' rounding points), and the normwise error
-||x - r|| / ||r|| within 1e-2.  Softmax gradients cancel, so the bfloat16
-operand roundings alone reach a few percent elementwise on early causal rows;
-the normwise bound stays tight.
+Tolerance, fixed and stated once (the pages and the configuration give none
+for gradients).  Every product that involves a gradient keeps bfloat16
+operands (unit roundoff u = 2^-8), and each gradient passes through four
+bfloat16 roundings: a fused or source operand, a probability or dS operand,
+the dO or Q operand, and the output.  Per output tensor:
+  normwise      ||x - r||_2 / ||r||_2              <= 1e-2
+  max-relative  max_i |x_i - r_i| / max_i |r_i|    <= 4u = 1.5625e-2
+The per-element error against each element's own row scale is printed for
+information only: softmax gradient rows sum to zero, so small elements of
+early causal rows carry a few percent of relative error that no fixed
+bfloat16 bound excludes.
 
 [Deck] "FusedKV: Reconstructing KV Caches with Cross-Layer Fusion", frame
 "FusedKV learns two-source, channel-wise fusion" (Eqs. (4)-(5), trained end
@@ -29,7 +32,8 @@ from parity import say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-TOL = 1e-2
+TOL = 1e-2                 # normwise
+MAXREL = 4 * 2.0 ** -8     # max-relative: four bfloat16 roundings
 WNAMES = ("dk_w1", "dk_wn", "dv_w1", "dv_wn")
 
 
@@ -99,8 +103,8 @@ class Case:
                   v_w1=w[2], v_wn=w[3], causal=self.causal, heads=heads)
 
     def reference(self, batch=None, heads=None):
-        """(exact oracle, rounding-budget model) gradients."""
-        return self.oracle(batch, heads), self.oracle(batch, heads, fn=rb.model)
+        """Exact fp64 oracle gradients."""
+        return self.oracle(batch, heads)
 
 
 def rows(x):
@@ -111,16 +115,21 @@ def rows(x):
     return x.reshape(-1, x.shape[-1])
 
 
-def compare(got, refs, names, factor=2.0):
-    ref, budget = refs
+def maxrel(x, r):
+    x = np.asarray(x, np.float64).ravel()
+    r = np.asarray(r, np.float64).ravel()
+    m = float(np.max(np.abs(r))) if r.size else 0.0
+    return float(np.max(np.abs(x - r))) / (m if m > 0 else 1.0) if r.size else 0.0
+
+
+def compare(got, ref, names):
+    """The fixed bar above, per output tensor, against the exact oracle."""
     for n in names:
         x, r = rows(got[n]), rows(ref[n])
-        e, en = rb.elementwise(x, r), rb.normwise(x, r)
-        eb = rb.elementwise(rows(budget[n]), r)
-        tol = max(TOL, factor * eb)
-        say("  %-6s elementwise=%.3e (budget %.3e, tol %.3e) normwise=%.3e" % (n, e, eb, tol, en))
+        en, em, ee = rb.normwise(x, r), maxrel(x, r), rb.elementwise(x, r)
+        say("  %-6s normwise=%.3e max-relative=%.3e (per-row elementwise %.3e, not bounded)" % (n, en, em, ee))
         assert np.isfinite(x).all(), n
-        assert e <= tol and en <= TOL, (n, e, tol, en)
+        assert en <= TOL and em <= MAXREL, (n, en, em)
 
 
 FUSED_NAMES = ("dq", "dk1", "dkn", "dv1", "dvn") + WNAMES
@@ -185,12 +194,10 @@ def test_selector_weights_match_lite_bitwise():
 @pytest.mark.parametrize("lite", [False, True])
 def test_training_flow_with_library_forward(lite):
     """O and LSE from the library's fkv_prefill, as a training step uses
-    them.  That forward rounds O independently of the budget model, so the
-    elementwise bound is three times the model's error; the normwise bound
-    stays 1e-2."""
+    them; the same fixed bar."""
     say("backward after library forward lite=%s B=2 S=333 Hq=8 Hkv=4 D=128" % lite)
     c = Case(2, 333, 8, 4, 128, 2450, lite=lite, fwd="library")
-    compare(c.run(), c.reference(), LITE_NAMES if lite else FUSED_NAMES, factor=3.0)
+    compare(c.run(), c.reference(), LITE_NAMES if lite else FUSED_NAMES)
 
 
 def test_deterministic():
@@ -201,37 +208,73 @@ def test_deterministic():
         assert torch.equal(a[n], b[n]), n
 
 
+def _weight_partials(ws, B, Hq, Hkv, S, D):
+    """The call's per-(batch, KV head, 128-key tile) weight-gradient partials,
+    read from its workspace (fkv_backward_workspace_size's layout: per-row
+    LSE and rowsum(dO * O) arrays, each 256-byte aligned, then the partials
+    [B, Hkv, ceil(S/128), (a, a', b, b'), D] float32)."""
+    r256 = lambda x: (x + 255) // 256 * 256
+    rows_b = B * Hq * S * 4
+    off = 2 * r256(rows_b)
+    nkt = (S + 127) // 128
+    n = B * Hkv * nkt * 4 * D
+    return ws[off:off + 4 * n].view(torch.float32).view(B, Hkv, nkt, 4, D), nkt
+
+
 def test_full_size_1p5b_backward():
     """1.5B shape (B=4, S=8192, 16/8 heads, D=128, causal), the benchmarked
     launch, after the library's own forward.  The oracle computes dQ, dK, dV
-    of two sampled (batch, KV head) units in full; the weight gradients, sums over every unit, are checked
-    through their definition against the call's own source gradients
-    (da = sum dK^1 * K^1 / a, and likewise), a property at any size."""
+    of two (batch, KV head) units in full.  The weight gradients sum over
+    all 32 units: the per-unit partials the call leaves in its workspace
+    (one per 128-key tile) are checked against the oracle's sums over the
+    same keys for both units, and the returned gradients against the fp64
+    sum of all partials (the reduction)."""
     B, S, Hq, Hkv, D = 4, 8192, 16, 8, 128
     say("backward full size B=%d S=%d Hq=%d Hkv=%d D=%d (sampled units)" % (B, S, Hq, Hkv, D))
     c = Case(B, S, Hq, Hkv, D, 0xF0003, fwd="library")
-    g = c.run()
+    L = c.L
+    g = {"dq": torch.empty_like(L.q)}
+    for n in ("dk1", "dkn", "dv1", "dvn"):
+        g[n] = torch.empty(B, S, Hkv, D, dtype=torch.bfloat16, device=DEV)
+    for n in WNAMES:
+        g[n] = torch.empty(Hkv, D, dtype=torch.float32, device=DEV)
+    ws = binding.backward_workspace(L.q, L.k1)
+    binding.fkv_prefill_backward(L.q, L.k1, L.kn, L.v1, L.vn, L.weights, c.out, c.lse, c.dout, dq=g["dq"],
+                                 dk1=g["dk1"], dkn=g["dkn"], dv1=g["dv1"], dvn=g["dvn"],
+                                 dweights=[g[n] for n in WNAMES], workspace=ws, causal=True)
+    torch.cuda.synchronize()
+    part, nkt = _weight_partials(ws, B, Hq, Hkv, S, D)
+    part = part.double().cpu().numpy()
     G = Hq // Hkv
+    h = inputs.host_array
     for b, kv in ((0, 0), (B - 1, Hkv - 1)):
-        ref, bud = c.reference(batch=[b], heads=[kv])
+        ref = c.reference(batch=[b], heads=[kv])
         got = {"dq": g["dq"][b:b + 1, :, kv * G:(kv + 1) * G], "dk1": g["dk1"][b:b + 1, :, kv:kv + 1],
                "dkn": g["dkn"][b:b + 1, :, kv:kv + 1], "dv1": g["dv1"][b:b + 1, :, kv:kv + 1],
                "dvn": g["dvn"][b:b + 1, :, kv:kv + 1]}
         r = {"dq": ref["dq"][:, :, kv * G:(kv + 1) * G]}
-        m = {"dq": bud["dq"][:, :, kv * G:(kv + 1) * G]}
         for n in ("dk1", "dkn", "dv1", "dvn"):
             r[n] = ref[n][:, :, kv:kv + 1]
-            m[n] = bud[n][:, :, kv:kv + 1]
         say(" unit b=%d g=%d" % (b, kv))
-        compare(got, (r, m), ("dq", "dk1", "dkn", "dv1", "dvn"), factor=3.0)
-    # weight gradients through their definition, from this call's outputs
-    w = [x.double() for x in c.L.weights]
-    src = {"dk_w1": (c.L.k1, "dk1", w[0]), "dk_wn": (c.L.kn, "dkn", w[1]),
-           "dv_w1": (c.L.v1, "dv1", w[2]), "dv_wn": (c.L.vn, "dvn", w[3])}
-    for n, (x, gname, wt) in src.items():
-        prop = (g[gname].double() / wt * x.double()).sum(dim=(0, 1))
-        e = rb.normwise(g[n].double().cpu().numpy(), prop.cpu().numpy())
-        say("  %s vs sum(d src * src / w) normwise=%.3e" % (n, e))
-        assert e <= TOL, (n, e)
-    del c, g
+        compare(got, r, ("dq", "dk1", "dkn", "dv1", "dvn"))
+        # this unit's weight-gradient partials, tile by tile, from the oracle's
+        # fused-key and fused-value gradients and the unit's own sources
+        srcs = {"dk_w1": ("dkf", L.k1), "dk_wn": ("dkf", L.kn), "dv_w1": ("dvf", L.v1), "dv_wn": ("dvf", L.vn)}
+        for w, n in enumerate(WNAMES):
+            gf, src = srcs[n]
+            x = bw._f64(h(src[b:b + 1, :, kv:kv + 1]))[0, :, 0, :]       # [S, D]
+            d = ref[gf][0, :, kv, :]                                     # [S, D]
+            want = np.stack([(d[t * 128:(t + 1) * 128] * x[t * 128:(t + 1) * 128]).sum(axis=0)
+                             for t in range(nkt)])                       # [nkt, D]
+            gotp = part[b, kv, :, w, :]
+            en, em = rb.normwise(gotp, want), maxrel(gotp, want)
+            say("  %s partials (%d tiles) normwise=%.3e max-relative=%.3e" % (n, nkt, en, em))
+            assert en <= TOL and em <= MAXREL, (n, en, em)
+    # the returned weight gradients are the sums of every unit's partials
+    for w, n in enumerate(WNAMES):
+        want = part[:, :, :, w, :].sum(axis=(0, 2))   # over batch rows and key tiles: [Hkv, D]
+        e = rb.normwise(g[n].double().cpu().numpy(), want)
+        say("  %s vs fp64 sum of the %d partials: normwise=%.3e" % (n, B * nkt, e))
+        assert e <= 1e-5, (n, e)
+    del c, g, ws
     torch.cuda.empty_cache()

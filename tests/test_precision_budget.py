@@ -55,11 +55,13 @@ def test_binary16_operands_fit_the_tolerance_bfloat16_do_not(orc, seed):
 def test_backward_rounding_budget():
     """The backward kernels keep bfloat16 operands for every product that
     involves a gradient (dO and dS can be far below binary16's normal range
-    in training).  Evaluated with those roundings, the exact formulas miss
-    the 1e-2 elementwise bound on causal inputs -- softmax gradient rows sum
-    to zero, so early rows cancel -- while the normwise error stays well
-    inside it.  The GPU backward tests therefore bound the elementwise error
-    by twice this model's, and the normwise error by 1e-2."""
+    in training).  The GPU tests bound each gradient tensor by a fixed bar:
+    normwise error <= 1e-2 and max_i |x_i - r_i| / max_i |r_i| <= 4u (u = 2^-8,
+    four bfloat16 roundings on each gradient's path).  The exact formulas
+    evaluated with bfloat16 rounding at those points stay inside that bar
+    with margin, while their error against each element's own row scale
+    exceeds 1e-2 -- softmax gradient rows sum to zero, so early causal rows
+    cancel -- which is why no per-element bound is asserted."""
     import bwd_rounding as rb
     from oracle import backward as bw
     L = inputs.make_layer(2, 200, 200, 4, 2, 64, torch.bfloat16, 2265, "cpu", decode=False)
@@ -69,7 +71,10 @@ def test_backward_rounding_budget():
     args = (h(L.q), h(L.k1), h(L.v1), h(dout), h(L.kn), h(L.vn))
     kw = dict(k_w1=w[0], k_wn=w[1], v_w1=w[2], v_wn=w[3], causal=True)
     ref, mod = bw.backward(*args, **kw), rb.model(*args, **kw)
+    names = ("dq", "dk1", "dkn", "dv1", "dvn", "dk_w1", "dk_wn", "dv_w1", "dv_wn")
     el = {n: rb.elementwise(mod[n], ref[n]) for n in ("dq", "dk1", "dv1")}
-    nw = {n: rb.normwise(mod[n], ref[n]) for n in ("dq", "dk1", "dv1", "dk_w1", "dv_w1")}
+    nw = {n: rb.normwise(mod[n], ref[n]) for n in names}
+    mx = {n: float(np.max(np.abs(mod[n] - ref[n])) / np.max(np.abs(ref[n]))) for n in names}
     assert max(el.values()) > 1e-2
     assert max(nw.values()) < 5e-3
+    assert max(mx.values()) < (4 * 2.0 ** -8) / 1.5
