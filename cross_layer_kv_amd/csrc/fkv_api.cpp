@@ -381,7 +381,7 @@ fkv_status kivi_decode_common(const fkv_params* p, const void* q, const fkv_q4_c
 // ---- backward ----
 
 struct BwdLayout {
-    size_t lse2, delta, wpart, kf, vf, total;
+    size_t lse2, delta, wpart, total;
     int32_t nkt;
 };
 
@@ -395,10 +395,7 @@ BwdLayout backward_layout(const fkv_params* p)
     l.lse2 = 0;
     l.delta = round256(rows);
     l.wpart = l.delta + round256(rows);
-    l.kf = l.wpart + round256((size_t)p->batch * p->num_kv_heads * l.nkt * 4 * p->head_dim * 4);
-    const size_t fused_rows = (size_t)p->batch * p->num_kv_heads * p->seqlen_k * p->head_dim * 2;
-    l.vf = l.kf + round256(fused_rows);
-    l.total = l.vf + round256(fused_rows);
+    l.total = l.wpart + round256((size_t)p->batch * p->num_kv_heads * l.nkt * 4 * p->head_dim * 4);
     return l;
 }
 
@@ -483,10 +480,6 @@ fkv_status backward_common(const fkv_params* p, const void* q, const fkv_cache* 
     a.lse2 = reinterpret_cast<float*>(ws + lay.lse2);
     a.delta = reinterpret_cast<float*>(ws + lay.delta);
     a.wpart = reinterpret_cast<float*>(ws + lay.wpart);
-    if (fused) {
-        a.kf = ws + lay.kf;
-        a.vf = ws + lay.vf;
-    }
     a.B = p->batch;
     a.S = p->seqlen_q;
     a.Hq = p->num_q_heads;

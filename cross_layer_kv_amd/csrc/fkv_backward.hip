@@ -34,12 +34,9 @@
 //      four source gradients and its partial column sums for the weight
 //      gradients.
 //   3. query tiles: a workgroup of 8 waves owns 256 (query row, head)
-//      columns and walks 64-key tiles staged in LDS, accumulating dQ.  For
-//      four sources a first kernel fuses every key and value row once into
-//      bf16 rows in the workspace, which this kernel reads as one source
-//      (every query tile would otherwise fuse the same tiles again).  dQ is
-//      thus written once, with no float atomics, and every result is
-//      run-to-run deterministic.
+//      columns and walks 64-key tiles staged in LDS, accumulating dQ; four
+//      sources are fused as each tile is staged.  dQ is thus written once,
+//      with no float atomics, and every result is run-to-run deterministic.
 //   4. reduce: the weight-gradient partials summed in a fixed order.
 //
 // Operand layouts (v_mfma_f32_32x32x16_bf16, A 32x16, B 16x32, C 32x32): a
@@ -224,9 +221,12 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
     // waves also stage the block's fused values in LDS ----
     uint4 kreg[KS];
     {
-        // four sources: the rows bwd_prefuse_kernel fused, as one source
-        const View ks_ = FUSED ? View{a.kf, (int64_t)a.Hkv * S * D, D, (int64_t)S * D} : a.k1;
-        const View vs_ = FUSED ? View{a.vf, (int64_t)a.Hkv * S * D, D, (int64_t)S * D} : a.v1;
+        // This block's 32 keys as B operands (lane: key l32); key waves also
+        // stage the block's values in LDS.  Four sources are fused here, one
+        // 8-channel chunk at a time, in float32 and rounded to bf16: the
+        // fused rows exist only in registers and LDS.  The scheduling fence
+        // after each chunk keeps the compiler from hoisting every chunk's
+        // loads and weights at once.
         const int key = kw + l32;
         const bool ok = key < S;
 #pragma unroll
@@ -234,11 +234,23 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
             const int ch = ks * 16 + hi * 8;
             uint4 k = make_uint4(0u, 0u, 0u, 0u), v = k;
             if (ok) {
-                k = *reinterpret_cast<const uint4*>(row_ptr(ks_, b, key, g) + ch);
-                if (kwave) v = *reinterpret_cast<const uint4*>(row_ptr(vs_, b, key, g) + ch);
+                k = *reinterpret_cast<const uint4*>(row_ptr(a.k1, b, key, g) + ch);
+                if (kwave) v = *reinterpret_cast<const uint4*>(row_ptr(a.v1, b, key, g) + ch);
+                if constexpr (FUSED) {
+                    float w1[8], wn[8];
+                    load8f(a.kw1 + g * D + ch, w1);
+                    load8f(a.kwn + g * D + ch, wn);
+                    k = fuse8_bf16(k, *reinterpret_cast<const uint4*>(row_ptr(a.kn, b, key, g) + ch), w1, wn);
+                    if (kwave) {
+                        load8f(a.vw1 + g * D + ch, w1);
+                        load8f(a.vwn + g * D + ch, wn);
+                        v = fuse8_bf16(v, *reinterpret_cast<const uint4*>(row_ptr(a.vn, b, key, g) + ch), w1, wn);
+                    }
+                }
             }
             kreg[ks] = k;
             if (kwave) *reinterpret_cast<uint4*>(vsm + (kb * 32 + l32) * P + ch) = v;
+            if constexpr (FUSED) __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -500,9 +512,10 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
 }
 
 // ---- 3. query tiles: dQ ----
-// Reads one bf16 key and one value source through a.k1 / a.v1: the Lite
-// sources, or the rows bwd_prefuse_kernel fused.
-template <int D, int G>
+// Stages each 64-key tile of the sources in LDS; with four sources the keys
+// and values are fused in float32 (weights from LDS) as the tile is stored,
+// rounded once to bf16 like the key-tile kernel's operands.
+template <int D, int G, bool FUSED>
 __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const BwdArgs a)
 {
     constexpr int DP = (D + 31) / 32 * 32;
@@ -570,34 +583,64 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const BwdArgs a)
     const int kend = a.causal ? q_last + 1 : S;
     const int nt = (kend + kKTile - 1) / kKTile;
 
-    constexpr int NITEM = kKTile * CPR;
-    constexpr int NPASS = (NITEM + kDqThreads - 1) / kDqThreads;
-    uint4 xr[2][NPASS];
+    // staging: a thread owns one 16-byte chunk column (fixed channels, so
+    // fixed fusion weights) of rows sr + p * RPP of each source
+    constexpr int RPP = kDqThreads / CPR;
+    constexpr int NPASS = (kKTile + RPP - 1) / RPP;
+    constexpr int NSRC = FUSED ? 4 : 2;  // k1, v1 (, kn, vn)
+    const int sc = tid % CPR, sr = tid / CPR;
+    const bool s_active = sr < RPP;
+    __shared__ __attribute__((aligned(16))) float Wsm[FUSED ? 4 * D : 4];  // a, a', b, b'
+    if constexpr (FUSED) {
+        for (int i = tid; i < 4 * D; i += kDqThreads) {
+            const float* w = i < D ? a.kw1 : (i < 2 * D ? a.kwn : (i < 3 * D ? a.vw1 : a.vwn));
+            Wsm[i] = w[g * D + i % D];
+        }
+        __syncthreads();
+    }
+    uint4 xr[NSRC][NPASS];
     auto load_tile = [&](int t) {
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
-            const int e = tid + p * kDqThreads;
-            const int r = e / CPR, c = e - (e / CPR) * CPR;
+            const int r = sr + p * RPP;
             const int key = t * kKTile + r;
-            const bool ok = e < NITEM && key < S;
-            xr[0][p] = make_uint4(0u, 0u, 0u, 0u);
-            xr[1][p] = xr[0][p];
-            if (ok) {
-                xr[0][p] = *reinterpret_cast<const uint4*>(row_ptr(a.k1, b, key, g) + c * 8);
-                xr[1][p] = *reinterpret_cast<const uint4*>(row_ptr(a.v1, b, key, g) + c * 8);
+            const bool ok = s_active && r < kKTile && key < S;
+#pragma unroll
+            for (int s_ = 0; s_ < NSRC; ++s_) {
+                const View& v = s_ == 0 ? a.k1 : (s_ == 1 ? a.v1 : (s_ == 2 ? a.kn : a.vn));
+                xr[s_][p] = ok ? *reinterpret_cast<const uint4*>(row_ptr(v, b, key, g) + sc * 8)
+                               : make_uint4(0u, 0u, 0u, 0u);
             }
         }
     };
     auto store_tile = [&](int buf) {
         uint16_t* kt_ = smem + (buf * 2 + 0) * TILE;
         uint16_t* vt_ = smem + (buf * 2 + 1) * TILE;
+        if constexpr (FUSED) {
+            float wk1[8], wkn[8], wv1[8], wvn[8];
+            const int c0 = s_active ? sc * 8 : 0;
 #pragma unroll
-        for (int p = 0; p < NPASS; ++p) {
-            const int e = tid + p * kDqThreads;
-            if (e >= NITEM) continue;
-            const int r = e / CPR, c = e - (e / CPR) * CPR;
-            *reinterpret_cast<uint4*>(kt_ + r * P + c * 8) = xr[0][p];
-            *reinterpret_cast<uint4*>(vt_ + r * P + c * 8) = xr[1][p];
+            for (int i = 0; i < 8; ++i) {
+                wk1[i] = Wsm[c0 + i];
+                wkn[i] = Wsm[D + c0 + i];
+                wv1[i] = Wsm[2 * D + c0 + i];
+                wvn[i] = Wsm[3 * D + c0 + i];
+            }
+#pragma unroll
+            for (int p = 0; p < NPASS; ++p) {
+                const int r = sr + p * RPP;
+                if (!s_active || r >= kKTile) continue;
+                *reinterpret_cast<uint4*>(kt_ + r * P + sc * 8) = fuse8_bf16(xr[0][p], xr[2][p], wk1, wkn);
+                *reinterpret_cast<uint4*>(vt_ + r * P + sc * 8) = fuse8_bf16(xr[1][p], xr[3][p], wv1, wvn);
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < NPASS; ++p) {
+                const int r = sr + p * RPP;
+                if (!s_active || r >= kKTile) continue;
+                *reinterpret_cast<uint4*>(kt_ + r * P + sc * 8) = xr[0][p];
+                *reinterpret_cast<uint4*>(vt_ + r * P + sc * 8) = xr[1][p];
+            }
         }
     };
 
@@ -696,36 +739,6 @@ __global__ __launch_bounds__(256) void bwd_wreduce_kernel(const BwdArgs a)
     }
 }
 
-// ---- fused key and value rows for the query-tile kernel ----
-// Every query-tile workgroup walks all the keys it sees, so the four-source
-// tiles are fused once here (the same float32 fusion and bfloat16 rounding
-// as the key-tile kernel's) and the query-tile kernel reads them as a
-// single source.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prefuse_kernel(const BwdArgs a)
-{
-    constexpr int CPR = D / 8;
-    const int64_t items = (int64_t)a.B * a.Hkv * a.S * CPR;
-    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < items; i += (int64_t)gridDim.x * 256) {
-        const int c = (int)(i % CPR);
-        const int64_t row = i / CPR;  // ((b * Hkv + g) * S + t)
-        const int t = (int)(row % a.S);
-        const int64_t unit = row / a.S;
-        const int b = (int)(unit / a.Hkv), g = (int)(unit % a.Hkv);
-        float w1[8], wn[8];
-        load8f(a.kw1 + g * D + c * 8, w1);
-        load8f(a.kwn + g * D + c * 8, wn);
-        const uint4 k1 = stream16(row_ptr(a.k1, b, t, g) + c * 8);
-        const uint4 kn = stream16(row_ptr(a.kn, b, t, g) + c * 8);
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.kf) + row * D + c * 8) = fuse8_bf16(k1, kn, w1, wn);
-        load8f(a.vw1 + g * D + c * 8, w1);
-        load8f(a.vwn + g * D + c * 8, wn);
-        const uint4 v1 = stream16(row_ptr(a.v1, b, t, g) + c * 8);
-        const uint4 vn = stream16(row_ptr(a.vn, b, t, g) + c * 8);
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.vf) + row * D + c * 8) = fuse8_bf16(v1, vn, w1, wn);
-    }
-}
-
 template <int D, bool FUSED, int G>
 int launch_bwd3(const BwdArgs& a, hipStream_t st)
 {
@@ -737,14 +750,6 @@ int launch_bwd3(const BwdArgs& a, hipStream_t st)
     }
     int rc = (int)hipGetLastError();
     if (rc) return rc;
-    if constexpr (FUSED) {
-        // fuse once; both tile kernels then read the fused rows
-        const int64_t items = (int64_t)a.B * a.Hkv * a.S * (D / 8);
-        const int64_t blocks = (items + 255) / 256;
-        hipLaunchKernelGGL(bwd_prefuse_kernel<D>, dim3((unsigned)(blocks < (1 << 20) ? blocks : (1 << 20))),
-                           dim3(256), 0, st, a);
-        if ((rc = (int)hipGetLastError())) return rc;
-    }
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, FUSED, G>), dim3((unsigned)(a.B * a.Hkv * a.nkt)), dim3(kDkvThreads), 0,
                        st, a);
     if ((rc = (int)hipGetLastError())) return rc;
@@ -752,15 +757,7 @@ int launch_bwd3(const BwdArgs& a, hipStream_t st)
     constexpr int BM = (kDqWaves / HPW) * 32;
     const int nqt = (a.S + BM - 1) / BM;
     const dim3 qgrid((unsigned)(a.B * a.Hkv * (G / HPW) * nqt));
-    if constexpr (FUSED) {
-        BwdArgs f = a;
-        const int64_t slab = (int64_t)a.S * D;
-        f.k1 = View{a.kf, a.Hkv * slab, D, slab};
-        f.v1 = View{a.vf, a.Hkv * slab, D, slab};
-        hipLaunchKernelGGL((bwd_dq_kernel<D, G>), qgrid, dim3(kDqThreads), 0, st, f);
-    } else {
-        hipLaunchKernelGGL((bwd_dq_kernel<D, G>), qgrid, dim3(kDqThreads), 0, st, a);
-    }
+    hipLaunchKernelGGL((bwd_dq_kernel<D, G, FUSED>), qgrid, dim3(kDqThreads), 0, st, a);
     if ((rc = (int)hipGetLastError())) return rc;
     if constexpr (FUSED) {
         hipLaunchKernelGGL(bwd_wreduce_kernel, dim3((unsigned)(4 * a.Hkv)), dim3(256), 0, st, a);

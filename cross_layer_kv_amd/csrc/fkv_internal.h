@@ -150,8 +150,6 @@ struct BwdArgs {
     float* lse2;            // workspace [B, Hq, S]: LSE * log2(e)
     float* delta;           // workspace [B, Hq, S]: rowsum(dO * O)
     float* wpart;           // workspace [B, Hkv, nkt, 4, D]: weight-gradient partials
-    void* kf;               // workspace [B, Hkv, S, D] bf16: fused keys (four-source calls)
-    void* vf;               // workspace [B, Hkv, S, D] bf16: fused values
     int32_t B, S, Hq, Hkv, D, G, causal;
     int32_t nkt;            // key tiles of 128 per (batch, KV head)
     float scale;            // softmax scale

@@ -361,10 +361,10 @@ typedef struct {
 
 /* Workspace bytes for fkv_prefill_backward / fkv_lite_prefill_backward with
  * these params (0 when the params are invalid or empty): per-row softmax
- * statistics (2 x B*H_q*S_q float32), the weight-gradient partials
- * (B*H_kv*ceil(S/128) x 4 x D float32) and, used by fkv_prefill_backward, the
- * layer's fused keys and values as bfloat16 rows (2 x B*H_kv*S*D), each part
- * 256-byte aligned. */
+ * statistics (2 x B*H_q*S_q float32) and the weight-gradient partials
+ * (B*H_kv*ceil(S/128) x 4 x D float32), each part 256-byte aligned.  The
+ * fused keys and values are rebuilt tile by tile inside the kernels and
+ * never stored. */
 size_t fkv_backward_workspace_size(const fkv_params* params);
 
 /*

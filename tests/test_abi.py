@@ -240,10 +240,10 @@ def test_backward_validation_codes(lib, B):
     p = _params(B, **ok)
     need = lib.fkv_backward_workspace_size(ctypes.byref(p))
     # LSE*log2(e) and rowsum(dO*O) rows (B*Hq*S floats each, 256-byte
-    # rounded), the weight-gradient partials (B*Hkv key tiles x 4 x D) and
-    # the fused key and value rows (B*Hkv*S*D bf16 each)
+    # rounded) and the weight-gradient partials (B*Hkv key tiles x 4 x D);
+    # no fused rows are stored
     rows = 2 * 4 * 64 * 4
-    assert need == 2 * (-(-rows // 256) * 256) + 2 * 2 * 1 * 4 * 64 * 4 + 2 * (2 * 2 * 64 * 64 * 2)
+    assert need == 2 * (-(-rows // 256) * 256) + 2 * 2 * 1 * 4 * 64 * 4
     assert _bwd(lib, B, p, ws_bytes=need - 1) == WS
     assert _bwd(lib, B, p, ws=FAKE + 64) == WS
     assert _bwd(lib, B, p, ws=None) == WS
