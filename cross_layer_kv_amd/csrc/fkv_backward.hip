@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
     constexpr int NPASS = (NITEM + kDkvThreads - 1) / kDkvThreads;
     uint4 xq[NPASS], xo[NPASS];
     float xl = 0.0f, xd = 0.0f;
-    auto load_tile = [&](int it) {
+    auto load_tile = [&](int it, int tid) {
         const int qb = q_begin + (it / G) * kQRows;
         const int h = g * G + it % G;
 #pragma unroll
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
             xd = row < S ? a.delta[r] : 0.0f;
         }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int buf, int tid) {
         uint16_t* qs = smem + (buf * 2 + 0) * TILE;
         uint16_t* os = smem + (buf * 2 + 1) * TILE;
 #pragma unroll
@@ -312,13 +312,21 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
 
     const float sl2 = a.scale_log2;
     if (nit > 0) {
-        load_tile(0);
-        store_tile(0);
+        load_tile(0, tid);
+        store_tile(0, tid);
     }
     for (int it = 0; it < nit; ++it) {
         const int buf = it & 1;
+        // Lane indices re-derived per tile from an opaque copy of the thread
+        // index: the loop's address terms are then recomputed (a few VALU
+        // instructions) instead of held in registers across the loop, where
+        // they pushed the four-source kernel into scratch spills whose
+        // reloads waited on the next tile's loads.
+        int tid_o = tid;
+        asm volatile("" : "+v"(tid_o));
+        const int l32 = tid_o & 31, hi = (tid_o >> 5) & 1;
         __syncthreads();  // tile `it` stored; tile it-1's readers are done
-        if (it + 1 < nit) load_tile(it + 1);
+        if (it + 1 < nit) load_tile(it + 1, tid_o);
         const int qb = q_begin + (it / G) * kQRows;
         const uint16_t* qs = smem + (buf * 2 + 0) * TILE;
         const uint16_t* os = smem + (buf * 2 + 1) * TILE;
@@ -402,7 +410,7 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
             tile(std::true_type{});
         else
             tile(std::false_type{});
-        if (it + 1 < nit) store_tile(buf ^ 1);
+        if (it + 1 < nit) store_tile(buf ^ 1, tid_o);
     }
 
     // ---- epilogue: transpose each accumulator through LDS (float32) ----
