@@ -59,14 +59,14 @@ class fkv_fusion(ctypes.Structure):
                 ("v_w1", ctypes.c_void_p), ("v_wn", ctypes.c_void_p)]
 
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 EXPORTS = ["fkv_abi_version", "fkv_status_string", "fkv_last_error", "fkv_decode_workspace_size",
            "fkv_decode", "fkv_lite_decode", "fkv_prefill", "fkv_lite_prefill",
            "fkv_check_tied",
            "fkv_kivi_codes_bytes", "fkv_kivi_meta_bytes", "fkv_kivi_quantize", "fkv_kivi_decode",
            "fkv_kivi_lite_decode", "fkv_backward_workspace_size", "fkv_prefill_backward",
-           "fkv_lite_prefill_backward", "fkv_decode_noalloc"]
+           "fkv_lite_prefill_backward", "fkv_decode_noalloc", "fkv_store_kv"]
 
 NOALLOC_SCRATCH_BYTES = 8 << 20
 
@@ -125,6 +125,8 @@ def load_library(path: str = LIB_PATH):
     lib.fkv_prefill_backward.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, fkv_cache, fkv_cache,
                                          P(fkv_fusion), vp, vp, vp, vp, fkv_grad, fkv_grad, fkv_grad, fkv_grad,
                                          P(fkv_fusion_grad), vp, ctypes.c_size_t, vp]
+    lib.fkv_store_kv.restype = ctypes.c_int
+    lib.fkv_store_kv.argtypes = [P(fkv_params), ctypes.c_int32, fkv_cache, fkv_cache, fkv_grad, fkv_grad, vp]
     lib.fkv_lite_prefill_backward.restype = ctypes.c_int
     lib.fkv_lite_prefill_backward.argtypes = [P(fkv_params), vp, fkv_cache, fkv_cache, vp, vp, vp, vp, fkv_grad,
                                               fkv_grad, vp, ctypes.c_size_t, vp]
@@ -560,3 +562,36 @@ def fkv_lite_prefill_backward(q, k_src, v_src, out, lse, dout, *, dq, dk, dv, wo
                                          _dev(out, "out"), _dev(lse, "lse"), _dev(dout, "dout"), _dev(dq, "dq"),
                                          grad_view(dk), grad_view(dv), _dev(workspace, "workspace"),
                                          workspace.numel(), _stream(stream)))
+
+
+# ---- storage layers ----
+
+def _store_checks(k_new, v_new, k_cache, v_cache, pos0):
+    """k_new / v_new [B, S_new, H_kv, D] and k_cache / v_cache [B, S, H_kv, D]
+    views of one dtype with contiguous channel axes; pos0 + S_new <= S."""
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError("%s must be a [B, S, H_kv, D] view with a contiguous channel axis" % n)
+        _same_dtype(k_new, t, n)
+    if tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError("v_new shape %s differs from k_new's %s" % (tuple(v_new.shape), tuple(k_new.shape)))
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("v_cache shape %s differs from k_cache's %s" % (tuple(v_cache.shape), tuple(k_cache.shape)))
+    B, Sn, H, D = k_new.shape
+    if (k_cache.shape[0], k_cache.shape[2], k_cache.shape[3]) != (B, H, D):
+        raise ValueError("caches %s do not match the new rows %s" % (tuple(k_cache.shape), tuple(k_new.shape)))
+    if pos0 < 0 or pos0 + Sn > k_cache.shape[1]:
+        raise ValueError("positions %d..%d are outside the caches' %d tokens" % (pos0, pos0 + Sn - 1,
+                                                                                 k_cache.shape[1]))
+
+
+def fkv_store_kv(k_new, v_new, k_cache, v_cache, *, pos0=0, stream=None):
+    """Write a storage layer's new keys and values (token-major or any
+    strides) into its caches at positions pos0.. (fkv_store_kv in
+    fusedkv.h), bit for bit."""
+    lib = load_library()
+    _store_checks(k_new, v_new, k_cache, v_cache, int(pos0))
+    B, Sn, H, D = k_new.shape
+    p = fkv_params(B, Sn, k_cache.shape[1], H, H, D, _dtype(k_new), 0.0, 0)
+    _check(lib.fkv_store_kv(ctypes.byref(p), int(pos0), cache_view(k_new), cache_view(v_new), grad_view(k_cache),
+                            grad_view(v_cache), _stream(stream)))

@@ -25,7 +25,7 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
              "-I" + os.path.join(ROOT, "include")]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I" + os.path.join(ROOT, "include")]
 
-HIP_SOURCES = ["fkv_decode.hip", "fkv_decode_mfma.hip", "fkv_kivi.hip", "fkv_prefill.hip", "fkv_backward.hip"]
+HIP_SOURCES = ["fkv_decode.hip", "fkv_decode_mfma.hip", "fkv_kivi.hip", "fkv_prefill.hip", "fkv_backward.hip", "fkv_store.hip"]
 CXX_SOURCES = ["fkv_api.cpp"]
 
 

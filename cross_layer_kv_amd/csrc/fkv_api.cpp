@@ -695,4 +695,37 @@ fkv_status fkv_lite_prefill_backward(const fkv_params* params, const void* q, fk
                            workspace_bytes, stream);
 }
 
+fkv_status fkv_store_kv(const fkv_params* params, int32_t pos0, fkv_cache k_new, fkv_cache v_new,
+                        fkv_grad k_cache, fkv_grad v_cache, void* stream)
+{
+    fkv_status s = check_shape(params);
+    if (s) return s;
+    if (pos0 < 0) return fail(FKV_ERROR_INVALID_VALUE, "pos0 must be >= 0");
+    if ((int64_t)pos0 + params->seqlen_q > params->seqlen_k)
+        return fail(FKV_ERROR_INVALID_VALUE, "pos0 + seqlen_q (%lld) exceeds the cache's %d tokens",
+                    (long long)pos0 + params->seqlen_q, params->seqlen_k);
+    if (params->batch == 0 || params->seqlen_q == 0) return ok();
+    // the new rows are checked as caches of seqlen_q tokens, the caches as
+    // writable views of seqlen_k tokens
+    fkv_params pn = *params;
+    pn.seqlen_k = params->seqlen_q;
+    if ((s = check_cache(&pn, k_new, "k_new")) || (s = check_cache(&pn, v_new, "v_new"))) return s;
+    if (!k_new.data || !v_new.data) return fail(FKV_ERROR_INVALID_VALUE, "k_new / v_new data is NULL");
+    if ((s = check_grad(params, k_cache, "k_cache")) || (s = check_grad(params, v_cache, "v_cache"))) return s;
+    fkv::StoreArgs a{};
+    a.k_new = view_of(k_new);
+    a.v_new = view_of(v_new);
+    a.k_cache = out_of(k_cache);
+    a.v_cache = out_of(v_cache);
+    a.B = params->batch;
+    a.S_new = params->seqlen_q;
+    a.H = params->num_kv_heads;
+    a.D = params->head_dim;
+    a.pos0 = pos0;
+    a.elt = (int)elt_size(params->dtype);
+    const int rc = fkv::launch_store_kv(a, stream);
+    if (rc) return fail(FKV_ERROR_LAUNCH, "cache-write launch failed (HIP error %d)", rc);
+    return ok();
+}
+
 }  // extern "C"

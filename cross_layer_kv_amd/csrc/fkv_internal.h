@@ -179,6 +179,15 @@ int launch_kivi_quantize(const KiviQuantArgs& a, void* stream);
 int launch_kivi_decode(const KiviDecodeArgs& a, bool fused, int waves, void* stream);
 int launch_prefill(const PrefillArgs& a, bool fused, void* stream);
 int launch_backward(const BwdArgs& a, bool fused, void* stream);
+
+// Storage-layer cache write: tokens 0..S_new-1 of k_new / v_new to cache
+// positions pos0..pos0+S_new-1; elt = element bytes (2 or 4).
+struct StoreArgs {
+    View k_new, v_new;
+    OutView k_cache, v_cache;
+    int B, S_new, H, D, pos0, elt;
+};
+int launch_store_kv(const StoreArgs& a, void* stream);
 // Query rows per prefill workgroup for a GQA ratio (0 when unsupported).
 int prefill_rows_per_tile(int G);
 

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define FKV_ABI_VERSION 6
+#define FKV_ABI_VERSION 7
 
 typedef enum {
     FKV_SUCCESS = 0,
@@ -407,6 +407,33 @@ fkv_status fkv_lite_prefill_backward(const fkv_params* params, const void* q,
                                      const void* dout, void* dq, fkv_grad dk,
                                      fkv_grad dv, void* workspace,
                                      size_t workspace_bytes, void* stream);
+
+/*
+ * ---- Storage layers ----
+ * fkv_store_kv -- write one storage layer's new keys and values into its
+ * caches.  In the FusedKV schedule the lower layers 1..n run a full prefill
+ * and keep their caches, which the upper layers then read: for the first
+ * token an upper layer needs only the last prompt position, one decode over
+ * the caches of layer 1 and layer n ([Deck] backup frame "Prefill skipping
+ * has a specific scope"; [Notes] section 2.5).  This call is that cache
+ * write, run before the layer's attention (fkv_lite_prefill over the written
+ * caches, or a decode step's append).
+ *
+ *   params   batch, seqlen_q = S_new (tokens written), seqlen_k = the
+ *            caches' token capacity, num_kv_heads, head_dim and dtype are
+ *            used (num_q_heads must still be a valid multiple)
+ *   pos0     first cache position written; pos0 + S_new <= seqlen_k
+ *   k_new, v_new      [B, S_new, H_kv, D] views (fkv_cache rules), e.g. the
+ *                     token-major output of the key/value projection, keys
+ *                     already rotated (the caches hold post-RoPE keys)
+ *   k_cache, v_cache  writable [B, seqlen_k, H_kv, D] views (fkv_grad rules)
+ * Cache positions pos0 .. pos0+S_new-1 receive the new rows bit for bit;
+ * every other position is left as it was.  The new rows and the caches must
+ * not overlap.  Errors as fkv_decode.  Asynchronous on `stream`.
+ */
+fkv_status fkv_store_kv(const fkv_params* params, int32_t pos0,
+                        fkv_cache k_new, fkv_cache v_new, fkv_grad k_cache,
+                        fkv_grad v_cache, void* stream);
 
 #ifdef __cplusplus
 }

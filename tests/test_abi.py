@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib, B):
     assert set(names) == set(B.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.fkv_abi_version() == B.ABI_VERSION == 6
+    assert lib.fkv_abi_version() == B.ABI_VERSION == 7
     for s in range(5):
         assert lib.fkv_status_string(s)
     assert lib.fkv_status_string(99) == b"unknown status"
@@ -430,3 +430,48 @@ def test_binding_refuses_mismatched_kivi_tensors(B):
         assert "GPU tensor" not in str(ei.value)
     with pytest.raises(TypeError, match="GPU tensor"):
         B.fkv_kivi_decode(q, keys[0], keys[1], vals[0], vals[1], w, out=torch.zeros_like(q), workspace=ws)
+
+
+def test_store_kv_validation_codes(lib, B):
+    INV = B.FKV_ERROR_INVALID_VALUE
+
+    def store(p, pos0=0, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, new_stride_s=None):
+        if p is None:
+            c = B.fkv_cache(FAKE, 0, 64, 0)
+            return lib.fkv_store_kv(None, 0, c, c, B.fkv_grad(FAKE, 0, 64, 0), B.fkv_grad(FAKE, 0, 64, 0), None)
+        ss = new_stride_s if new_stride_s is not None else p.num_kv_heads * p.head_dim
+        new = [B.fkv_cache(x, p.seqlen_q * ss, ss, p.head_dim) for x in (kn, vn)]   # token-major new rows
+        cache = [B.fkv_grad(x, p.num_kv_heads * p.seqlen_k * p.head_dim, p.head_dim, p.seqlen_k * p.head_dim)
+                 for x in (kc, vc)]                                                  # head-major caches
+        return lib.fkv_store_kv(ctypes.byref(p), pos0, new[0], new[1], cache[0], cache[1], None)
+
+    p = _params(B, sq=16, sk=64)
+    assert store(None) == INV
+    assert store(p, pos0=-1) == INV
+    assert store(p, pos0=49) == INV                    # 49 + 16 > 64 tokens
+    assert store(p, kn=0) == INV
+    assert store(p, vc=0) == INV
+    assert store(p, kc=FAKE + 8) == INV                # misaligned cache base
+    assert store(p, new_stride_s=60) == INV            # rows overlap
+    assert store(_params(B, sq=16, sk=64, d=72)) == B.FKV_ERROR_UNSUPPORTED
+    # nothing to write launches nothing
+    assert store(_params(B, batch=0, sq=16, sk=64)) == B.FKV_SUCCESS
+    assert store(_params(B, sq=0, sk=64), pos0=64) == B.FKV_SUCCESS
+
+
+def test_binding_refuses_mismatched_store_tensors(B):
+    Bt, S, Hkv, D = 2, 32, 2, 64
+    new = torch.zeros(Bt, 8, Hkv, D, dtype=torch.bfloat16)
+    cache = torch.zeros(Bt, Hkv, S, D, dtype=torch.bfloat16).transpose(1, 2)
+    cases = [
+        dict(k_new=new, v_new=new, k_cache=cache, v_cache=cache, pos0=25),                    # past the end
+        dict(k_new=new, v_new=new[:, :4], k_cache=cache, v_cache=cache, pos0=0),              # new rows differ
+        dict(k_new=new, v_new=new, k_cache=cache, v_cache=cache.float(), pos0=0),             # dtype
+        dict(k_new=new, v_new=new, k_cache=cache[:, :, :1], v_cache=cache[:, :, :1], pos0=0),  # heads
+    ]
+    for c in cases:
+        with pytest.raises((ValueError, TypeError)) as ei:
+            B.fkv_store_kv(c["k_new"], c["v_new"], c["k_cache"], c["v_cache"], pos0=c["pos0"])
+        assert "GPU tensor" not in str(ei.value)
+    with pytest.raises(TypeError, match="GPU tensor"):
+        B.fkv_store_kv(new, new, cache, cache, pos0=24)
