@@ -293,13 +293,6 @@ __device__ __forceinline__ uint4 pk_mul4(uint4 x, uint4 y)
 {
     return make_uint4(pk_mul(x.x, y.x), pk_mul(x.y, y.y), pk_mul(x.z, y.z), pk_mul(x.w, y.w));
 }
-__device__ __forceinline__ float dot8(uint4 x, uint4 y, float acc)
-{
-    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x.x), __builtin_bit_cast(f16x2, y.x), acc, false);
-    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x.y), __builtin_bit_cast(f16x2, y.y), acc, false);
-    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x.z), __builtin_bit_cast(f16x2, y.z), acc, false);
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x.w), __builtin_bit_cast(f16x2, y.w), acc, false);
-}
 __device__ __forceinline__ float sum4(float v)  // over the 4 lanes l, l^16, l^32, l^48
 {
     v += __shfl_xor(v, 16);
@@ -474,14 +467,16 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
                         hb * 8);
     };
 
+    // oacc: O of each source (rows: heads 4 hb + i, columns: channels);
+    // mp: the value-minimum terms sum_t p_t m_t of each source, one column
+    // per 32-channel group (column l16 = group, rows heads 4 hb + i)
     f32x4 oacc[NS][NVB];
-    float Mp[NS][KS];
+    f32x4 mp[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
 #pragma unroll
         for (int n = 0; n < NVB; ++n) oacc[s][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int k = 0; k < KS; ++k) Mp[s][k] = 0.0f;
+        mp[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
     float m_run = -INFINITY, l_part = 0.0f;
 
@@ -507,10 +502,17 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
             s_meta[wave][0][l16][hb] = k;
         }
     };
-    auto compute = [&](const Blk& x, const VBlk& y, int t0) {
+    // One block.  PART: the block holds the end of the row (tokens past
+    // t_end are masked); full blocks skip every per-token test.
+    constexpr bool ALLCH = D % 32 == 0;  // every lane quarter holds real channels
+    auto compute = [&](const Blk& x, const VBlk& y, int t0, auto part) {
+            constexpr bool PART = decltype(part)::value;
             // ---- scores: two 16-token tiles, heads on the columns ----
+            // cacc: sum over channels of q a m (log2 units) per head, the
+            // same in every token row: the key minima as a matrix operand
+            // whose 16 rows are equal
             f32x4 sc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
-            float cst = 0.0f;  // sum over this lane's channels of q a m (log2 units)
+            f32x4 cacc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     #pragma unroll
             for (int s = 0; s < NS; ++s)
     #pragma unroll
@@ -519,18 +521,17 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
                     const uint4 kmn = s_meta[wave][0][(s * KS + ks) * 2 + 1][hb];
                     const uint4 qav = s_qa[s][ks][lane];
                     const uint4 u = pk_mul4(qav, ksc);
-                    cst = dot8(qav, kmn, cst);
+                    cacc = mma16(kmn, qav, cacc);
     #pragma unroll
                     for (int tl = 0; tl < 2; ++tl) {
                         // this lane's 8 codes: row 16 tl + l16, bytes 16 ks + 4 hb
-                        const bool chan = ks * 32 + hb * 8 < D;
-                        const bool live = chan && t0 + tl * 16 + l16 < t_end;
+                        const bool chan = ALLCH || ks * 32 + hb * 8 < D;
+                        const bool live = chan && (!PART || t0 + tl * 16 + l16 < t_end);
                         const uint32_t kc =
                             s_kc[wave][s * 4 * D + (tl * 16 + l16) * (D / 8) + (chan ? ks * 4 + hb : 0)];
                         sc[tl] = mma16(codes_f16_k(live ? kc : 0u), u, sc[tl]);
                     }
                 }
-            cst = sum4(cst);
             // lane: head l16; entries: tokens t0 + 16 tl + 4 hb + i
             float sv[8];
             float bmax = -INFINITY;
@@ -539,7 +540,7 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
     #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int t = t0 + tl * 16 + hb * 4 + i;
-                    const float x = (hv && t < t_end) ? sc[tl][i] * kTwo24 + cst : -INFINITY;
+                    const float x = (hv && (!PART || t < t_end)) ? sc[tl][i] * kTwo24 + cacc[i] : -INFINITY;
                     sv[tl * 4 + i] = x;
                     bmax = fmaxf(bmax, x);
                 }
@@ -548,10 +549,6 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
             if (__any(m_new > m_run)) {
                 const float corr = rel_weight(m_run, m_new);
                 l_part *= corr;
-    #pragma unroll
-                for (int s = 0; s < NS; ++s)
-    #pragma unroll
-                    for (int k = 0; k < KS; ++k) Mp[s][k] *= corr;
                 // output rows are heads 4 hb + i: fetch those heads' factors
                 // (lane h holds head h's factor: l16 = h, hb = 0)
                 float cr[G];
@@ -567,18 +564,21 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
                     rc[i] = r;
                 }
     #pragma unroll
-                for (int s = 0; s < NS; ++s)
+                for (int s = 0; s < NS; ++s) {
     #pragma unroll
                     for (int n = 0; n < NVB; ++n)
     #pragma unroll
                         for (int i = 0; i < 4; ++i) oacc[s][n][i] *= rc[i];
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) mp[s][i] *= rc[i];
+                }
                 m_run = m_new;
             }
             const float msub = m_run == -INFINITY ? 0.0f : m_run;
             float pv[8];
     #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                pv[e] = sv[e] == -INFINITY ? 0.0f : exp2_fast(sv[e] - msub);
+                pv[e] = exp2_fast(sv[e] - msub);  // (2^-inf = 0: masked entries)
                 l_part += pv[e];
             }
             const uint4 p16 = make_uint4(pack2(pv[0], pv[1]), pack2(pv[2], pv[3]), pack2(pv[4], pv[5]), pack2(pv[6], pv[7]));
@@ -590,7 +590,7 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
             // tokens past it are zeroed: their p is 0, but 0 * inf or NaN
             // metadata would still reach the sums.
             uint4 vm = y.vm;
-            if (t0 + kGroup > t_end) {
+            if (PART && t0 + kGroup > t_end) {
                 uint32_t w[4];
     #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -602,17 +602,21 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
             s_meta[wave][1][l16][hb] = vm;
         }
     #pragma unroll
-            for (int s = 0; s < NS; ++s)
+            for (int s = 0; s < NS; ++s) {
+                // minimum terms of every group at once: column l16 = group
+                // l16's minima of this lane quarter's 8 tokens
+                const uint4 mcol = l16 < KS ? s_meta[wave][1][(s * KS + (l16 < KS ? l16 : 0)) * 2 + 1][hb]
+                                            : make_uint4(0u, 0u, 0u, 0u);
+                mp[s] = mma16(p16, mcol, mp[s]);
     #pragma unroll
                 for (int k = 0; k < KS; ++k) {
                     const uint4 vsc = s_meta[wave][1][(s * KS + k) * 2 + 0][hb];
-                    const uint4 vmn = s_meta[wave][1][(s * KS + k) * 2 + 1][hb];
                     const uint4 pa = pk_mul4(p16, vsc);
-                    Mp[s][k] = dot8(p16, vmn, Mp[s][k]);
     #pragma unroll
                     for (int n = 2 * k; n < 2 * k + 2 && n < NVB; ++n)
                         oacc[s][n] = mma16(pa, codes_f16(y.vc[s][n]), oacc[s][n]);
                 }
+            }
     };
 
     // The next block's key-side loads are in flight while a block is
@@ -639,24 +643,26 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
             if constexpr (VPRE) load_values(t0 + step, vnxt);
         }
         if constexpr (!VPRE) load_values(t0, vcur);
-        compute(cur, vcur, t0);
+        if (t0 + kGroup <= t_end)
+            compute(cur, vcur, t0, std::false_type{});
+        else
+            compute(cur, vcur, t0, std::true_type{});
         cur = nxt;
         if constexpr (VPRE) vcur = vnxt;
     }
 
     // ---- wave results: (m, l) and the minimum terms per head ----
     const float l_tot = sum4(l_part);
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int k = 0; k < KS; ++k) Mp[s][k] = sum4(Mp[s][k]);
     if (hb == 0 && hv) {
         s_ml[wave][l16][0] = m_run;
         s_ml[wave][l16][1] = l_tot;
+    }
+    if (l16 < KS) {
 #pragma unroll
         for (int s = 0; s < NS; ++s)
 #pragma unroll
-            for (int k = 0; k < KS; ++k) s_M[wave][s][l16][k] = Mp[s][k];
+            for (int i = 0; i < 4; ++i)
+                if (4 * hb + i < G) s_M[wave][s][4 * hb + i][l16] = mp[s][i];
     }
     __syncthreads();
     // lane: output column c = 16 n + l16 of heads 4 hb + i
