@@ -81,44 +81,52 @@ constexpr float kLn2 = 0.69314718055994530942f;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Raw bits of 8 channels of one row: one 16-byte load for bf16, two for f32.
-template <typename T>
-struct Raw8 {
-    static constexpr int NV = sizeof(T) == 2 ? 1 : 2;
-    uint4 v[NV];
+// Raw bits of C channels of one row: 8 channels are one 16-byte load for
+// bf16 (two for f32); 6 bf16 channels are one 12-byte load.
+template <typename T, int C>
+struct RawC {
+    static constexpr int NW = C * (int)sizeof(T) / 4;  // 32-bit words
+    uint32_t w[NW];
 };
 
 // Every source byte is read once per call: the loads are non-temporal
 // ("nt"), which streams them past the caches (80% of HBM peak against 71%
 // with plain loads at the 650M shape).
-template <typename T>
-__device__ __forceinline__ void load8(Raw8<T>& r, const T* p, bool pred)
+template <typename T, int C>
+__device__ __forceinline__ void loadc(RawC<T, C>& r, const T* p, bool pred)
 {
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int NW = RawC<T, C>::NW;
+    if constexpr (NW % 4 == 0) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int i = 0; i < Raw8<T>::NV; ++i)
-        r.v[i] = pred ? __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + i))
-                      : make_uint4(0u, 0u, 0u, 0u);
+        for (int i = 0; i < NW / 4; ++i) {
+            const u32x4 v = pred ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + i) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) r.w[4 * i + k] = v[k];
+        }
+    } else {
+        static_assert(NW == 3, "12-byte rows pieces");
+        // 4-byte aligned 12-byte pieces (row starts are 16-byte aligned, a
+        // piece starts at 12 * lane within the row)
+        typedef unsigned int u32x3 __attribute__((ext_vector_type(3), aligned(4)));
+        const u32x3 v = pred ? __builtin_nontemporal_load(reinterpret_cast<const u32x3*>(p)) : u32x3{0u, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 3; ++k) r.w[k] = v[k];
+    }
 }
 
-template <typename T>
-__device__ __forceinline__ void widen8(const Raw8<T>& r, float* f)
+template <typename T, int C>
+__device__ __forceinline__ void widenc(const RawC<T, C>& r, float* f)
 {
     if constexpr (sizeof(T) == 2) {
-        const uint32_t w[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[2 * i] = bf16_lo(w[i]);
-            f[2 * i + 1] = bf16_hi(w[i]);
+        for (int i = 0; i < C / 2; ++i) {
+            f[2 * i] = bf16_lo(r.w[i]);
+            f[2 * i + 1] = bf16_hi(r.w[i]);
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            f[4 * i + 0] = __uint_as_float(r.v[i].x);
-            f[4 * i + 1] = __uint_as_float(r.v[i].y);
-            f[4 * i + 2] = __uint_as_float(r.v[i].z);
-            f[4 * i + 3] = __uint_as_float(r.v[i].w);
-        }
+        for (int i = 0; i < C; ++i) f[i] = __uint_as_float(r.w[i]);
     }
 }
 
@@ -160,7 +168,10 @@ template <typename T, int D, bool FUSED, int G, int NW>
 __global__ __launch_bounds__(64 * NW) void decode_kernel(const DecodeArgs a)
 {
     constexpr int NT = 64 * NW;
-    constexpr int NP = D / 8;              // 8-channel pieces per row
+    // channels per lane: 8, or 6 for bf16 rows of 96 channels, so that the
+    // 16 lanes of a token group are all busy (one 12-byte load each)
+    constexpr int CPL = (sizeof(T) == 2 && D == 96) ? 6 : 8;
+    constexpr int NP = D / CPL;            // pieces per row
     constexpr int LPT = NP <= 8 ? 8 : 16;  // lanes per token group
     constexpr int TPW = 64 / LPT;          // tokens per wave step
     constexpr int WT = decode_wave_tokens(sizeof(T) == 4, FUSED, G);  // tokens per wave per iteration
@@ -176,7 +187,7 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const DecodeArgs a)
     const int lane = tid & 63, wave = tid >> 6;
     const int grp = lane / LPT, pc = lane % LPT;
     const bool active = pc < NP;
-    const int c0 = active ? pc * 8 : 0;
+    const int c0 = active ? pc * CPL : 0;
 
     int len = a.seqlens ? a.seqlens[b] : a.Sk;
     len = len < 0 ? 0 : (len > a.Sk ? a.Sk : len);
@@ -185,23 +196,23 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const DecodeArgs a)
 
     // Query of the G heads, pre-scaled into the log2 domain, and the lane's
     // fusion weights.
-    float qs[G][8];
+    float qs[G][CPL];
     {
         const T* qp = static_cast<const T*>(a.q) + ((int64_t)b * a.Hq + (int64_t)g * G) * D + c0;
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
-            Raw8<T> r;
-            load8(r, qp + (int64_t)hh * D, active);
-            widen8(r, qs[hh]);
+            RawC<T, CPL> r;
+            loadc(r, qp + (int64_t)hh * D, active);
+            widenc(r, qs[hh]);
 #pragma unroll
-            for (int c = 0; c < 8; ++c) qs[hh][c] *= a.scale_log2;
+            for (int c = 0; c < CPL; ++c) qs[hh][c] *= a.scale_log2;
         }
     }
-    float wk1[8], wkn[8], wv1[8], wvn[8];
+    float wk1[CPL], wkn[CPL], wv1[CPL], wvn[CPL];
     if constexpr (FUSED) {
         const int64_t wo = (int64_t)g * D + c0;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
+        for (int c = 0; c < CPL; ++c) {
             wk1[c] = active ? a.kw1[wo + c] : 0.0f;
             wkn[c] = active ? a.kwn[wo + c] : 0.0f;
             wv1[c] = active ? a.vw1[wo + c] : 0.0f;
@@ -218,28 +229,28 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const DecodeArgs a)
         vnp = static_cast<const T*>(a.vn.data) + (int64_t)b * a.vn.sb + (int64_t)g * a.vn.sh + c0;
     }
 
-    float m[G], l[G], acc[G][8];
+    float m[G], l[G], acc[G][CPL];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
         m[hh] = -INFINITY;
         l[hh] = 0.0f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[hh][c] = 0.0f;
+        for (int c = 0; c < CPL; ++c) acc[hh][c] = 0.0f;
     }
 
     // The loads of one wave step: U token slices of each source.
     struct Blk {
-        Raw8<T> k1[U], kn[U], v1[U], vn[U];
+        RawC<T, CPL> k1[U], kn[U], v1[U], vn[U];
     };
     auto load_blk = [&](int t0, Blk& x) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int t = t0 + u * TPW + grp;
             const bool pr = active && t < t_end;
-            load8(x.k1[u], k1p + (int64_t)t * a.k1.ss, pr);
-            if constexpr (FUSED) load8(x.kn[u], knp + (int64_t)t * a.kn.ss, pr);
-            load8(x.v1[u], v1p + (int64_t)t * a.v1.ss, pr);
-            if constexpr (FUSED) load8(x.vn[u], vnp + (int64_t)t * a.vn.ss, pr);
+            loadc(x.k1[u], k1p + (int64_t)t * a.k1.ss, pr);
+            if constexpr (FUSED) loadc(x.kn[u], knp + (int64_t)t * a.kn.ss, pr);
+            loadc(x.v1[u], v1p + (int64_t)t * a.v1.ss, pr);
+            if constexpr (FUSED) loadc(x.vn[u], vnp + (int64_t)t * a.vn.ss, pr);
         }
     };
     // Single-source bf16 steps at G <= 4 keep the next step's loads in flight
@@ -260,10 +271,10 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const DecodeArgs a)
         } else {
             load_blk(t0, cur);
         }
-        const Raw8<T>(&rk1)[U] = cur.k1;
-        const Raw8<T>(&rkn)[U] = cur.kn;
-        const Raw8<T>(&rv1)[U] = cur.v1;
-        const Raw8<T>(&rvn)[U] = cur.vn;
+        const RawC<T, CPL>(&rk1)[U] = cur.k1;
+        const RawC<T, CPL>(&rkn)[U] = cur.kn;
+        const RawC<T, CPL>(&rv1)[U] = cur.v1;
+        const RawC<T, CPL>(&rvn)[U] = cur.vn;
         bool ok[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) ok[u] = t0 + u * TPW + grp < t_end;
@@ -272,19 +283,19 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const DecodeArgs a)
         float s[U][G];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float kf[8];
-            widen8(rk1[u], kf);
+            float kf[CPL];
+            widenc(rk1[u], kf);
             if constexpr (FUSED) {
-                float kn[8];
-                widen8(rkn[u], kn);
+                float kn[CPL];
+                widenc(rkn[u], kn);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) kf[c] = wk1[c] * kf[c] + wkn[c] * kn[c];
+                for (int c = 0; c < CPL; ++c) kf[c] = wk1[c] * kf[c] + wkn[c] * kn[c];
             }
 #pragma unroll
             for (int hh = 0; hh < G; ++hh) {
                 float d = 0.0f;
 #pragma unroll
-                for (int c = 0; c < 8; ++c) d += qs[hh][c] * kf[c];
+                for (int c = 0; c < CPL; ++c) d += qs[hh][c] * kf[c];
                 d = group_sum<LPT>(d);
                 s[u][hh] = ok[u] ? d : -INFINITY;
             }
@@ -301,27 +312,27 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const DecodeArgs a)
                 const float corr = rel(m[hh], mx);
                 l[hh] *= corr;
 #pragma unroll
-                for (int c = 0; c < 8; ++c) acc[hh][c] *= corr;
+                for (int c = 0; c < CPL; ++c) acc[hh][c] *= corr;
                 m[hh] = mx;
             }
             msub[hh] = m[hh] == -INFINITY ? 0.0f : m[hh];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float vf[8];
-            widen8(rv1[u], vf);
+            float vf[CPL];
+            widenc(rv1[u], vf);
             if constexpr (FUSED) {
-                float vn[8];
-                widen8(rvn[u], vn);
+                float vn[CPL];
+                widenc(rvn[u], vn);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) vf[c] = wv1[c] * vf[c] + wvn[c] * vn[c];
+                for (int c = 0; c < CPL; ++c) vf[c] = wv1[c] * vf[c] + wvn[c] * vn[c];
             }
 #pragma unroll
             for (int hh = 0; hh < G; ++hh) {
                 const float p = exp2_fast(s[u][hh] - msub[hh]);
                 l[hh] += p;
 #pragma unroll
-                for (int c = 0; c < 8; ++c) acc[hh][c] += p * vf[c];
+                for (int c = 0; c < CPL; ++c) acc[hh][c] += p * vf[c];
             }
         }
         if constexpr (PREF) cur = nxt;
@@ -338,7 +349,7 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const DecodeArgs a)
             const float fa = rel(m[hh], M), fb = rel(mo, M);
             l[hh] = l[hh] * fa + lo * fb;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) acc[hh][c] = acc[hh][c] * fa + __shfl_xor(acc[hh][c], off) * fb;
+            for (int c = 0; c < CPL; ++c) acc[hh][c] = acc[hh][c] * fa + __shfl_xor(acc[hh][c], off) * fb;
             m[hh] = M;
         }
     }
@@ -346,7 +357,7 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const DecodeArgs a)
 #pragma unroll
         for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-            for (int c = 0; c < 8; ++c) s_acc[wave][hh][c0 + c] = acc[hh][c];
+            for (int c = 0; c < CPL; ++c) s_acc[wave][hh][c0 + c] = acc[hh][c];
     }
     if (lane == 0) {
 #pragma unroll
