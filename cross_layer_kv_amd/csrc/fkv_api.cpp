@@ -111,7 +111,7 @@ fkv::DecodePlan plan_decode(const fkv_params* p, bool fused, bool kivi = false)
     // G = 64 runs the matrix-core kernel: 64-token tiles, and it aims at two
     // workgroups per CU
     const bool wide = G == fkv::kHighGqa;
-    const int64_t iter = wide ? 64 : (int64_t)pl.waves * (kivi ? 32 : fkv::decode_wave_tokens(p->dtype == FKV_F32, fused, (int)G));
+    const int64_t iter = wide ? 64 : (int64_t)pl.waves * (kivi ? 32 : fkv::decode_wave_tokens(p->dtype == FKV_F32, fused, (int)G, p->head_dim));
     // (the 8-wave 4-bit single-source kernel fits two workgroups per CU)
     const int64_t target = (wide || (kivi && !fused && pl.waves == 8)) ? 512 : 256;
     const int64_t max_splits = S > 0 ? (S + iter - 1) / iter : 1;

@@ -174,7 +174,7 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const DecodeArgs a)
     constexpr int NP = D / CPL;            // pieces per row
     constexpr int LPT = NP <= 8 ? 8 : 16;  // lanes per token group
     constexpr int TPW = 64 / LPT;          // tokens per wave step
-    constexpr int WT = decode_wave_tokens(sizeof(T) == 4, FUSED, G);  // tokens per wave per iteration
+    constexpr int WT = decode_wave_tokens(sizeof(T) == 4, FUSED, G, D);  // tokens per wave per iteration
     constexpr int U = WT / TPW;            // steps per iteration
 
     __shared__ float s_acc[NW][G][D];

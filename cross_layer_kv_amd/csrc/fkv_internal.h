@@ -60,11 +60,13 @@ constexpr int decode_waves(int dtype_f32, bool fused, int G)
 }
 
 // Tokens a wave takes per iteration of the decode loop.  The bf16
-// four-source kernel with G <= 2 takes 8, which halves its load registers
-// (123 VGPRs) so that 4 waves per SIMD fit; the others take 16.
-constexpr int decode_wave_tokens(int dtype_f32, bool fused, int G)
+// four-source kernel with G <= 2 takes 8 when a lane owns 8 channels, which
+// halves its load registers (123 VGPRs) so that 4 waves per SIMD fit; at
+// D = 96 a lane owns 6 channels and 16 tokens fit the same budget (121);
+// the others take 16.
+constexpr int decode_wave_tokens(int dtype_f32, bool fused, int G, int D)
 {
-    return (!dtype_f32 && fused && G <= 2) ? 8 : 16;
+    return (!dtype_f32 && fused && G <= 2 && D != 96) ? 8 : 16;
 }
 
 // Waves per workgroup of the 4-bit decode kernel (a wave takes 32-token
