@@ -441,13 +441,17 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
             }
         }
         // metadata chunk of this lane column (columns past NC fetch a copy of
-        // chunk column mod NC and are never read)
+        // chunk column mod NC and are never read).  Metadata loads are plain,
+        // cached loads: a block's 192-byte metadata rows share cache lines
+        // with the neighbouring blocks', which other waves read at about the
+        // same time (streamed past the caches, those lines were fetched
+        // twice: 1.029x the algorithmic bytes against 1.000x).
         const int j = t0 / kGroup;
         const int c = l16 % NC;
         const int s = c / (2 * KS), ks = (c >> 1) - (c / (2 * KS)) * KS, sm = c & 1;
         const Q4View& kv = *ksrc[s];
         const bool chan = ks * 32 + hb * 8 < D;
-        const uint4 km = stream16(static_cast<const uint16_t*>(sm ? kv.minv : kv.scale) + (bh * ngk + j) * D +
+        const uint4 km = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(sm ? kv.minv : kv.scale) + (bh * ngk + j) * D +
                                   (chan ? ks * 32 + hb * 8 : 0));
         x.km = chan ? km : make_uint4(0u, 0u, 0u, 0u);
     };
@@ -463,7 +467,7 @@ __global__ __launch_bounds__(64 * NW) void q4_decode_kernel(const KiviDecodeArgs
         const int c = l16 % NC;
         const int s = c / (2 * KS), ks = (c >> 1) - (c / (2 * KS)) * KS, sm = c & 1;
         const Q4View& vv = *vsrc[s];
-        x.vm = stream16(static_cast<const uint16_t*>(sm ? vv.minv : vv.scale) + ((bh * nbv + j) * KS + ks) * kGroup +
+        x.vm = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(sm ? vv.minv : vv.scale) + ((bh * nbv + j) * KS + ks) * kGroup +
                         hb * 8);
     };
 
