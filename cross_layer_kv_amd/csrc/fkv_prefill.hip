@@ -17,23 +17,28 @@
 // are what this file keeps off the matrix-core critical path.
 //
 // Layout of the work
-//   * A workgroup of 8 waves owns one (batch, KV head, tile of BM query
-//     rows) and all G query heads of that KV head: 8 * 32 = 256 query
-//     columns, BM = 256 / G rows.  Each fused K/V tile is built once in LDS
-//     and consumed by all 256 columns.
+//   * A workgroup of 12 waves owns one (batch, KV head, tile of BM query
+//     rows) and all G query heads of that KV head.  Waves 0-7 are the
+//     matrix-core waves: 8 * 32 = 256 query columns, BM = 256 / G rows.
+//     Waves 8-11, one per SIMD, stage the K/V tiles: they load the sources,
+//     fuse them in float32 and store binary16 tiles in LDS, each tile once
+//     for all 256 columns.  Their vector work then runs beside the other
+//     waves' matrix-core products on the same SIMD instead of between them;
+//     they run at a raised wave priority, because the matrix-core waves'
+//     softmax would otherwise take the vector ALU first and stall staging.
 //   * Scores are computed transposed, S^T = K~ Q^T, with
 //     v_mfma_f32_32x32x16_f16: a lane then holds 16 scores of ONE query, so
 //     the row max and row sum are lane-local except for one exchange with
 //     the lane 32 apart.  The probabilities feed the P*V product straight
 //     from registers: the V tile is stored transposed in LDS with its keys
 //     permuted to match the accumulator layout of the score product.
-//   * Tiles are double-buffered in LDS; the global loads of tile j+1 are in
-//     flight while tile j is multiplied, and fused into the other buffer
-//     afterwards (one barrier per tile).
+//   * Tiles are double-buffered in LDS: while tile j is multiplied, tile
+//     j+1 is fused into the other buffer and the loads of tile j+2 are
+//     issued (one barrier per tile).
 //   * Softmax is in the log2 domain with scale * log2 e folded into one FMA;
 //     a row's reference max is raised only when a tile max exceeds it by more
 //     than 8, so the accumulator is rarely rescaled, and the row sums are
-//     packed fp16 dot products of the probabilities the products consume.
+//     float32 adds of the probabilities.
 //   * Matrix-core operands are IEEE binary16: bf16 inputs (Q, unfused K/V)
 //     convert to it exactly inside its range, and the float32 fused tiles and
 //     probabilities keep 11 significant bits instead of bf16's 8.  The
@@ -56,8 +61,11 @@ namespace {
 using namespace dev;
 
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kCWaves = 8;                 // matrix-core (consumer) waves
+constexpr int kPWaves = 4;                 // staging (producer) waves
+constexpr int kCThreads = 64 * kCWaves;
+constexpr int kPThreads = 64 * kPWaves;
+constexpr int kThreads = kCThreads + kPThreads;
 constexpr int BN = 64;  // keys per tile
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -73,20 +81,26 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
 {
     constexpr bool FUSED = MODE == kModeFused;
     constexpr int BM = 256 / G;          // query rows per workgroup
-    constexpr int WPH = kWaves / G;      // waves per query head
+    constexpr int WPH = kCWaves / G;     // matrix-core waves per query head
     constexpr int DP = (D + 31) / 32 * 32;
     constexpr int KS = D / 16;           // k-steps of the score product
     constexpr int NDB = DP / 32;         // 32-channel blocks of the output
     constexpr int KROW = D + 8;          // LDS row pitch of K~ (elements)
     constexpr int VROW = BN + 8;         // LDS row pitch of V~^T
     constexpr int CPR = D / 8;           // 16-byte chunks per key row
-    constexpr int RPP = kThreads / CPR;  // key rows per load pass
+    constexpr int RPP = kPThreads / CPR; // key rows per staging pass
     constexpr int KPASS = (BN + RPP - 1) / RPP;
     constexpr int NVITEM = (D / 2) * (BN / 8);  // (channel pair, key octet) items
-    static_assert(NVITEM <= kThreads, "one V item per thread");
+    constexpr int VPASS = (NVITEM + kPThreads - 1) / kPThreads;
 
     __shared__ __attribute__((aligned(16))) uint16_t Kt[2][BN * KROW];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[2][DP * VROW];
+    // At D = 128 the query fragments of the last QL k-steps of each wave
+    // live in LDS (each wave reads back only its own): held in registers
+    // they would push the matrix-core waves past their register budget.
+    constexpr int QL = D >= 128 ? 2 : 0;
+    constexpr int QR = KS - QL;
+    __shared__ __attribute__((aligned(16))) uint4 Qs[QL > 0 ? kCWaves * QL * 64 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -105,11 +119,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
     const int b = unit / a.Hkv, g = unit - (unit / a.Hkv) * a.Hkv;
     const int S = a.S;
     const int q0 = qt * BM;
-
-    // this wave's 32 query rows of local head hh
-    const int hh = wave / WPH;
-    const int h = g * G + hh;
-    const int r0 = q0 + (wave - hh * WPH) * 32;
+    const int kend = a.causal ? min(S, q0 + BM) : S;
+    const int nt = (kend + BN - 1) / BN;
 
     // zero the padded channel rows of V~^T (D < DP); they are never written
     if constexpr (DP > D) {
@@ -119,18 +130,180 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
         }
     }
 
+    if (wave >= kCWaves) {
+        // ================= staging waves =================
+        // They load the sources of tile j+2 while the matrix-core waves work
+        // on tile j, and fuse tile j+1 into the other LDS buffer: their
+        // vector work runs beside the other waves' matrix-core products on
+        // the same SIMDs instead of between them.
+        const int pt = tid - kCThreads;
+        __builtin_amdgcn_s_setprio(2);
+        const int kc = pt % CPR, kr = pt / CPR;  // key chunk column / first row
+        const bool k_active = kr < RPP;
+        int vj[VPASS], vo[VPASS];
+        bool v_active[VPASS];
+#pragma unroll
+        for (int v = 0; v < VPASS; ++v) {
+            const int it = pt + v * kPThreads;
+            v_active[v] = it < NVITEM;
+            vj[v] = v_active[v] ? it % (D / 2) : 0;   // channel pair
+            vo[v] = v_active[v] ? it / (D / 2) : 0;   // key octet
+        }
+
+        // float32 fusion weights of this thread's channels: a fused element
+        // is w1 * x1 + wn * xn in float32 (a multiply and an FMA on the
+        // widened bf16 sources), rounded once to binary16
+        float wk1[8], wkn[8], wv1[VPASS][2], wvn[VPASS][2];
+        if constexpr (FUSED) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                wk1[c] = k_active ? a.kw1[g * D + kc * 8 + c] : 0.0f;
+                wkn[c] = k_active ? a.kwn[g * D + kc * 8 + c] : 0.0f;
+            }
+#pragma unroll
+            for (int v = 0; v < VPASS; ++v)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    wv1[v][c] = v_active[v] ? a.vw1[g * D + 2 * vj[v] + c] : 0.0f;
+                    wvn[v][c] = v_active[v] ? a.vwn[g * D + 2 * vj[v] + c] : 0.0f;
+                }
+        }
+        // Per-tile buffer descriptors: the base advances by one tile of rows
+        // per tile (scalar work) and the size shrinks with it, so the lanes
+        // keep fixed offsets and rows past S-1 read as zero.
+        const uint16_t* b_k1 = static_cast<const uint16_t*>(a.k1.data) + (int64_t)b * a.k1.sb + (int64_t)g * a.k1.sh;
+        const uint16_t* b_v1 = static_cast<const uint16_t*>(a.v1.data) + (int64_t)b * a.v1.sb + (int64_t)g * a.v1.sh;
+        const uint16_t* b_kn = b_k1;
+        const uint16_t* b_vn = b_v1;
+        if constexpr (FUSED) {
+            b_kn = static_cast<const uint16_t*>(a.kn.data) + (int64_t)b * a.kn.sb + (int64_t)g * a.kn.sh;
+            b_vn = static_cast<const uint16_t*>(a.vn.data) + (int64_t)b * a.vn.sb + (int64_t)g * a.vn.sh;
+        }
+        auto tile_rsrc = [&](const uint16_t* base, int64_t ss, int j) {
+            const int64_t total = ((int64_t)(S - 1) * ss + D) * 2;
+            const int64_t skip = (int64_t)j * BN * ss * 2;
+            const int64_t left = total - skip;
+            return slab_rsrc(base + (int64_t)j * BN * ss, (uint32_t)(left > 0 ? left : 0));
+        };
+        // byte offsets of this thread's rows inside a tile (kOffNone when idle)
+        uint32_t koff1[KPASS], koffn[KPASS], voff1[VPASS][8], voffn[VPASS][8];
+#pragma unroll
+        for (int p = 0; p < KPASS; ++p) {
+            const int row = kr + p * RPP;
+            const bool ok = k_active && row < BN;
+            koff1[p] = ok ? (uint32_t)(row * a.k1.ss * 2 + kc * 16) : kOffNone;
+            koffn[p] = ok ? (uint32_t)(row * a.kn.ss * 2 + kc * 16) : kOffNone;
+        }
+#pragma unroll
+        for (int v = 0; v < VPASS; ++v) {
+            const int vkey0 = (vo[v] >> 1) * 16 + (vo[v] & 1) * 4;  // octet's first key
+#pragma unroll
+            for (int s8 = 0; s8 < 8; ++s8) {
+                const int row = vkey0 + (s8 & 3) + (s8 >> 2) * 8;
+                voff1[v][s8] = v_active[v] ? (uint32_t)(row * a.v1.ss * 2 + vj[v] * 4) : kOffNone;
+                voffn[v][s8] = v_active[v] ? (uint32_t)(row * a.vn.ss * 2 + vj[v] * 4) : kOffNone;
+            }
+        }
+
+        uint4 xk1[KPASS], xkn[KPASS];
+        uint32_t xv1[VPASS][8], xvn[VPASS][8];
+        auto issue_loads = [&](int j) {
+            const __amdgpu_buffer_rsrc_t rk1 = tile_rsrc(b_k1, a.k1.ss, j);
+            const __amdgpu_buffer_rsrc_t rv1 = tile_rsrc(b_v1, a.v1.ss, j);
+            __amdgpu_buffer_rsrc_t rkn = rk1, rvn = rv1;
+            if constexpr (FUSED) {
+                rkn = tile_rsrc(b_kn, a.kn.ss, j);
+                rvn = tile_rsrc(b_vn, a.vn.ss, j);
+            }
+#pragma unroll
+            for (int p = 0; p < KPASS; ++p) {
+                xk1[p] = ld16(rk1, koff1[p]);
+                if constexpr (FUSED) xkn[p] = ld16(rkn, koffn[p]);
+            }
+#pragma unroll
+            for (int v = 0; v < VPASS; ++v)
+#pragma unroll
+                for (int s8 = 0; s8 < 8; ++s8) {
+                    xv1[v][s8] = ld4(rv1, voff1[v][s8]);
+                    if constexpr (FUSED) xvn[v][s8] = ld4(rvn, voffn[v][s8]);
+                }
+        };
+        // fuse the loaded registers (float32) and store fp16 tiles into buffer nb
+        auto store_tile = [&](int nb) {
+#pragma unroll
+            for (int p = 0; p < KPASS; ++p) {
+                const int row = kr + p * RPP;
+                if (k_active && row < BN) {
+                    uint4 o;
+                    if constexpr (FUSED) {
+                        const uint32_t x1[4] = {xk1[p].x, xk1[p].y, xk1[p].z, xk1[p].w};
+                        const uint32_t xn[4] = {xkn[p].x, xkn[p].y, xkn[p].z, xkn[p].w};
+                        uint32_t r[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            r[i] = pack2(fmaf(wk1[2 * i], bf16_lo(x1[i]), wkn[2 * i] * bf16_lo(xn[i])),
+                                         fmaf(wk1[2 * i + 1], bf16_hi(x1[i]), wkn[2 * i + 1] * bf16_hi(xn[i])));
+                        o = make_uint4(r[0], r[1], r[2], r[3]);
+                    } else {
+                        o = bf16x8_to_f16x8(xk1[p]);
+                    }
+                    *reinterpret_cast<uint4*>(&Kt[nb][row * KROW + kc * 8]) = o;
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < VPASS; ++v) {
+                if (v_active[v]) {
+                    uint32_t lo[4], hv[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if constexpr (FUSED) {
+                            lo[i] = pack2(fmaf(wv1[v][0], bf16_lo(xv1[v][2 * i]), wvn[v][0] * bf16_lo(xvn[v][2 * i])),
+                                          fmaf(wv1[v][0], bf16_lo(xv1[v][2 * i + 1]), wvn[v][0] * bf16_lo(xvn[v][2 * i + 1])));
+                            hv[i] = pack2(fmaf(wv1[v][1], bf16_hi(xv1[v][2 * i]), wvn[v][1] * bf16_hi(xvn[v][2 * i])),
+                                          fmaf(wv1[v][1], bf16_hi(xv1[v][2 * i + 1]), wvn[v][1] * bf16_hi(xvn[v][2 * i + 1])));
+                        } else {
+                            lo[i] = pack2(bf16_lo(xv1[v][2 * i]), bf16_lo(xv1[v][2 * i + 1]));
+                            hv[i] = pack2(bf16_hi(xv1[v][2 * i]), bf16_hi(xv1[v][2 * i + 1]));
+                        }
+                    }
+                    *reinterpret_cast<uint4*>(&Vt[nb][(2 * vj[v]) * VROW + vo[v] * 8]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+                    *reinterpret_cast<uint4*>(&Vt[nb][(2 * vj[v] + 1) * VROW + vo[v] * 8]) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+                }
+            }
+        };
+
+        issue_loads(0);
+        store_tile(0);
+        if (nt > 1) issue_loads(1);
+        __syncthreads();
+        for (int j = 0; j < nt; ++j) {
+            if (j + 1 < nt) {
+                store_tile((j + 1) & 1);
+                if (j + 2 < nt) issue_loads(j + 2);
+            }
+            __syncthreads();
+        }
+        return;
+    }
+
+    // ================= matrix-core waves =================
+    // this wave's 32 query rows of local head hh
+    const int hh = wave / WPH;
+    const int h = g * G + hh;
+    const int r0 = q0 + (wave - hh * WPH) * 32;
+
     // msub: the running reference max, 0 while there is none.  With SPLAT the
     // queries are pre-multiplied by scale * log2(e) and the score chains start
     // from -msub, so the accumulators hold exponent arguments directly (the
     // splat changes only when the reference is raised).  That removes one VALU
     // instruction per score, which pays where the softmax weighs most against
     // the matrix-core work of a tile (D = 80, S = 16384: +4.5%).  At D = 128 it
-    // measured 0.5-0.9% slower (and the in-kernel fusion mode would spill), so
-    // there the scores are scaled and shifted by one FMA before each exponential.
+    // measured 0.5-0.9% slower, so there the scores are scaled and shifted by
+    // one FMA before each exponential.
     constexpr bool SPLAT = D <= 96;
 
     // ---- queries: B operand of S^T = K~ Q^T, 8 channels per lane per k-step
-    f16x8 qreg[KS];
+    f16x8 qreg[QR];
     {
         const int row = r0 + l32;
         const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (((int64_t)b * S + row) * a.Hq + h) * D + hi * 8;
@@ -144,164 +317,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
                 uint32_t o[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) o[i] = pack2(bf16_lo(w[i]) * qs, bf16_hi(w[i]) * qs);
-                qreg[ks] = as_f16x8(make_uint4(o[0], o[1], o[2], o[3]));
+                const uint4 qv = make_uint4(o[0], o[1], o[2], o[3]);
+                if (ks < QR) qreg[ks] = as_f16x8(qv);
+                else Qs[(wave * QL + ks - QR) * 64 + lane] = qv;
             } else {
-                qreg[ks] = as_f16x8(bf16x8_to_f16x8(u));
+                const uint4 qv = bf16x8_to_f16x8(u);
+                if (ks < QR) qreg[ks] = as_f16x8(qv);
+                else Qs[(wave * QL + ks - QR) * 64 + lane] = qv;
             }
         }
     }
-
-    // ---- tile loaders: buffer descriptors over this (b, g) slab ----
-    const int kc = tid % CPR, kr = tid / CPR;  // key chunk column / first row
-    const bool k_active = kr < RPP;
-    const int vj = tid % (D / 2), vo = tid / (D / 2);  // channel pair, key octet
-    const bool v_active = tid < NVITEM;
-    const int vkey0 = (vo >> 1) * 16 + (vo & 1) * 4;   // octet's first key
-
-    // Float32 fusion weights of this thread's channels: a fused element is
-    // w1 * x1 + wn * xn in float32 (a multiply and an FMA on the widened bf16
-    // sources).  Plain FMAs co-issue with matrix-core work in flight on the
-    // SIMD; bf16 dot-product instructions do not on this part.
-    float wk1[8], wkn[8], wv1[2], wvn[2];
-    if constexpr (FUSED) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            wk1[c] = k_active ? a.kw1[g * D + kc * 8 + c] : 0.0f;
-            wkn[c] = k_active ? a.kwn[g * D + kc * 8 + c] : 0.0f;
-        }
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            wv1[c] = v_active ? a.vw1[g * D + 2 * vj + c] : 0.0f;
-            wvn[c] = v_active ? a.vwn[g * D + 2 * vj + c] : 0.0f;
-        }
-    }
-    // Per-tile buffer descriptors: the base advances by one tile of rows per
-    // tile (scalar work) and the size shrinks with it, so the lanes keep
-    // fixed offsets and rows past S-1 read as zero.
-    const uint16_t* b_k1 = static_cast<const uint16_t*>(a.k1.data) + (int64_t)b * a.k1.sb + (int64_t)g * a.k1.sh;
-    const uint16_t* b_v1 = static_cast<const uint16_t*>(a.v1.data) + (int64_t)b * a.v1.sb + (int64_t)g * a.v1.sh;
-    const uint16_t* b_kn = b_k1;
-    const uint16_t* b_vn = b_v1;
-    if constexpr (FUSED) {
-        b_kn = static_cast<const uint16_t*>(a.kn.data) + (int64_t)b * a.kn.sb + (int64_t)g * a.kn.sh;
-        b_vn = static_cast<const uint16_t*>(a.vn.data) + (int64_t)b * a.vn.sb + (int64_t)g * a.vn.sh;
-    }
-    auto tile_rsrc = [&](const uint16_t* base, int64_t ss, int j) {
-        const int64_t total = ((int64_t)(S - 1) * ss + D) * 2;
-        const int64_t skip = (int64_t)j * BN * ss * 2;
-        const int64_t left = total - skip;
-        return slab_rsrc(base + (int64_t)j * BN * ss, (uint32_t)(left > 0 ? left : 0));
-    };
-    // byte offsets of this thread's rows inside a tile (kOffNone when idle)
-    uint32_t koff1[KPASS], koffn[KPASS], voff1[8], voffn[8];
-#pragma unroll
-    for (int p = 0; p < KPASS; ++p) {
-        const int row = kr + p * RPP;
-        const bool ok = k_active && row < BN;
-        koff1[p] = ok ? (uint32_t)(row * a.k1.ss * 2 + kc * 16) : kOffNone;
-        koffn[p] = ok ? (uint32_t)(row * a.kn.ss * 2 + kc * 16) : kOffNone;
-    }
-#pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) {
-        const int row = vkey0 + (s8 & 3) + (s8 >> 2) * 8;
-        voff1[s8] = v_active ? (uint32_t)(row * a.v1.ss * 2 + vj * 4) : kOffNone;
-        voffn[s8] = v_active ? (uint32_t)(row * a.vn.ss * 2 + vj * 4) : kOffNone;
-    }
-
-    uint4 xk1[KPASS], xkn[KPASS];
-    uint32_t xv1[8], xvn[8];
-
-    // The loads of the next tile, one at a time (index i < NKL: key loads).
-    // They are spread over the k-steps of the score product instead of being
-    // issued together at the start of a tile, where all waves of the
-    // workgroup would stall on the vector-memory queue at once.
-    constexpr int NSRCK = FUSED ? 2 : 1;
-    constexpr int NKL = KPASS * NSRCK, NL = NKL + 8 * NSRCK;
-    __amdgpu_buffer_rsrc_t nk1, nkn, nv1, nvn;
-    auto next_rsrc = [&](int j) {
-        nk1 = tile_rsrc(b_k1, a.k1.ss, j);
-        nv1 = tile_rsrc(b_v1, a.v1.ss, j);
-        nkn = nk1; nvn = nv1;
-        if constexpr (FUSED) {
-            nkn = tile_rsrc(b_kn, a.kn.ss, j);
-            nvn = tile_rsrc(b_vn, a.vn.ss, j);
-        }
-    };
-    auto load_one = [&](int i) {
-        if (i < NKL) {
-            const int p = i / NSRCK, s = i % NSRCK;
-            if (s == 0) xk1[p] = ld16(nk1, koff1[p]);
-            else xkn[p] = ld16(nkn, koffn[p]);
-        } else {
-            const int s8 = (i - NKL) / NSRCK, s = (i - NKL) % NSRCK;
-            if (s == 0) xv1[s8] = ld4(nv1, voff1[s8]);
-            else xvn[s8] = ld4(nvn, voffn[s8]);
-        }
-    };
-    auto issue_loads = [&](int j) {
-        const __amdgpu_buffer_rsrc_t rk1 = tile_rsrc(b_k1, a.k1.ss, j);
-        const __amdgpu_buffer_rsrc_t rv1 = tile_rsrc(b_v1, a.v1.ss, j);
-        __amdgpu_buffer_rsrc_t rkn = rk1, rvn = rv1;
-        if constexpr (FUSED) {
-            rkn = tile_rsrc(b_kn, a.kn.ss, j);
-            rvn = tile_rsrc(b_vn, a.vn.ss, j);
-        }
-#pragma unroll
-        for (int p = 0; p < KPASS; ++p) {
-            xk1[p] = ld16(rk1, koff1[p]);
-            if constexpr (FUSED) xkn[p] = ld16(rkn, koffn[p]);
-        }
-#pragma unroll
-        for (int s8 = 0; s8 < 8; ++s8) {
-            xv1[s8] = ld4(rv1, voff1[s8]);
-            if constexpr (FUSED) xvn[s8] = ld4(rvn, voffn[s8]);
-        }
-    };
-
-    // fuse the loaded registers (float32) and store fp16 tiles into buffer nb
-    auto store_tile = [&](int nb) {
-#pragma unroll
-        for (int p = 0; p < KPASS; ++p) {
-            const int row = kr + p * RPP;
-            if (k_active && row < BN) {
-                uint4 o;
-                if constexpr (FUSED) {
-                    const uint32_t x1[4] = {xk1[p].x, xk1[p].y, xk1[p].z, xk1[p].w};
-                    const uint32_t xn[4] = {xkn[p].x, xkn[p].y, xkn[p].z, xkn[p].w};
-                    uint32_t r[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        r[i] = pack2(fmaf(wk1[2 * i], bf16_lo(x1[i]), wkn[2 * i] * bf16_lo(xn[i])),
-                                     fmaf(wk1[2 * i + 1], bf16_hi(x1[i]), wkn[2 * i + 1] * bf16_hi(xn[i])));
-                    o = make_uint4(r[0], r[1], r[2], r[3]);
-                } else {
-                    o = bf16x8_to_f16x8(xk1[p]);
-                }
-                *reinterpret_cast<uint4*>(&Kt[nb][row * KROW + kc * 8]) = o;
-            }
-        }
-        if (v_active) {
-            uint32_t lo[4], hv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if constexpr (FUSED) {
-                    lo[i] = pack2(fmaf(wv1[0], bf16_lo(xv1[2 * i]), wvn[0] * bf16_lo(xvn[2 * i])),
-                                  fmaf(wv1[0], bf16_lo(xv1[2 * i + 1]), wvn[0] * bf16_lo(xvn[2 * i + 1])));
-                    hv[i] = pack2(fmaf(wv1[1], bf16_hi(xv1[2 * i]), wvn[1] * bf16_hi(xvn[2 * i])),
-                                  fmaf(wv1[1], bf16_hi(xv1[2 * i + 1]), wvn[1] * bf16_hi(xvn[2 * i + 1])));
-                } else {
-                    lo[i] = pack2(bf16_lo(xv1[2 * i]), bf16_lo(xv1[2 * i + 1]));
-                    hv[i] = pack2(bf16_hi(xv1[2 * i]), bf16_hi(xv1[2 * i + 1]));
-                }
-            }
-            *reinterpret_cast<uint4*>(&Vt[nb][(2 * vj) * VROW + vo * 8]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-            *reinterpret_cast<uint4*>(&Vt[nb][(2 * vj + 1) * VROW + vo * 8]) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
-        }
-    };
-
-    // ---- main loop over key tiles ----
-    const int kend = a.causal ? min(S, q0 + BM) : S;
-    const int nt = (kend + BN - 1) / BN;
 
     f32x16 oacc[NDB];
 #pragma unroll
@@ -312,49 +337,46 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
     const int qrow = r0 + l32;
     const float sl2 = a.scale_log2;
 
-    issue_loads(0);
-    store_tile(0);
-    __syncthreads();
+    __syncthreads();  // tile 0 staged
 
     for (int j = 0; j < nt; ++j) {
         const int buf = j & 1;
-        const bool more = j + 1 < nt;
-        if (more) next_rsrc(j + 1);
-
         const int kbase = j * BN;
         const bool wave_live = !a.causal || kbase <= r0 + 31;
-        if (!wave_live && more) {
-#pragma unroll
-            for (int i = 0; i < NL; ++i) load_one(i);
-        }
         if (wave_live) {
-            // S^T = K~ Q^T over two 32-key blocks; LDS fragments are read two
+            // lane terms of the LDS addresses, re-derived per tile from an
+            // opaque copy of the lane index: held across the loop they would
+            // be spilled, and their reloads would wait at every tile
+            int lo_ = lane;
+            asm volatile("" : "+v"(lo_));
+            const int l32t = lo_ & 31, hit = lo_ >> 5;
+            // S^T = K~ Q^T over two 32-key blocks; LDS fragments are read KA
             // k-steps ahead of the matrix-core instructions that use them
+            constexpr int KA = D >= 128 ? 1 : 2;
             f32x16 sacc[2] = {SPLAT ? msplat : f32x16{}, SPLAT ? msplat : f32x16{}};
-            const uint16_t* kt = &Kt[buf][0] + l32 * KROW + hi * 8;
+            const uint16_t* kt = &Kt[buf][0] + l32t * KROW + hit * 8;
             uint4 kf[KS][2];
 #pragma unroll
-            for (int ks = 0; ks < KS && ks < 2; ++ks)
+            for (int ks = 0; ks < KS && ks < KA; ++ks)
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
                     kf[ks][kb] = *reinterpret_cast<const uint4*>(kt + kb * 32 * KROW + ks * 16);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                if (more) {
-#pragma unroll
-                    for (int i = ks * NL / KS; i < (ks + 1) * NL / KS; ++i) load_one(i);
-                }
-                if (ks + 2 < KS) {
+                if (ks + KA < KS) {
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
-                        kf[ks + 2][kb] = *reinterpret_cast<const uint4*>(kt + kb * 32 * KROW + (ks + 2) * 16);
+                        kf[ks + KA][kb] = *reinterpret_cast<const uint4*>(kt + kb * 32 * KROW + (ks + KA) * 16);
                 }
+                f16x8 qop;
+                if (ks < QR) qop = qreg[ks < QR ? ks : 0];
+                else qop = as_f16x8(Qs[(wave * QL + (ks >= QR ? ks - QR : 0)) * 64 + lo_]);
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
-                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(kf[ks][kb]), qreg[ks], sacc[kb], 0, 0, 0);
+                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(kf[ks][kb]), qop, sacc[kb], 0, 0, 0);
             }
             // V~^T fragments for the first 32-key block, read while softmax runs
-            const uint16_t* vt = &Vt[buf][0] + l32 * VROW + hi * 8;
+            const uint16_t* vt = &Vt[buf][0] + l32t * VROW + hit * 8;
             uint4 vf[4][NDB];
 #pragma unroll
             for (int c = 0; c < 2; ++c)
@@ -434,6 +456,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
                     }
                     pb[half] = as_f16x8(make_uint4(w[0], w[1], w[2], w[3]));
                 }
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int d = 0; d < NDB; ++d)
+                        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vf[kb * 2 + half][d]), pb[half],
+                                                                         oacc[d], 0, 0, 0);
+                // the second block's fragments, read while its exponentials run
                 if (kb == 0) {
 #pragma unroll
                     for (int c = 2; c < 4; ++c)
@@ -441,15 +470,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
                         for (int d = 0; d < NDB; ++d)
                             vf[c][d] = *reinterpret_cast<const uint4*>(vt + d * 32 * VROW + c * 16);
                 }
-#pragma unroll
-                for (int half = 0; half < 2; ++half)
-#pragma unroll
-                    for (int d = 0; d < NDB; ++d)
-                        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vf[kb * 2 + half][d]), pb[half],
-                                                                         oacc[d], 0, 0, 0);
             }
         }
-        if (j + 1 < nt) store_tile(buf ^ 1);
         __syncthreads();
     }
 
