@@ -356,6 +356,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
             f32x16 sacc[2] = {SPLAT ? msplat : f32x16{}, SPLAT ? msplat : f32x16{}};
             const uint16_t* kt = &Kt[buf][0] + l32t * KROW + hit * 8;
             uint4 kf[KS][2];
+            // the query fragments kept in LDS, read with the first key fragments
+            uint4 qf[QL > 0 ? QL : 1];
+#pragma unroll
+            for (int i = 0; i < QL; ++i) qf[i] = Qs[(wave * QL + i) * 64 + lo_];
 #pragma unroll
             for (int ks = 0; ks < KS && ks < KA; ++ks)
 #pragma unroll
@@ -370,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a)
                 }
                 f16x8 qop;
                 if (ks < QR) qop = qreg[ks < QR ? ks : 0];
-                else qop = as_f16x8(Qs[(wave * QL + (ks >= QR ? ks - QR : 0)) * 64 + lo_]);
+                else qop = as_f16x8(qf[ks >= QR ? ks - QR : 0]);
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
                     sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(kf[ks][kb]), qop, sacc[kb], 0, 0, 0);
