@@ -180,7 +180,12 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
     constexpr int DP = (D + 31) / 32 * 32;  // channels padded to whole 32-column blocks
     constexpr int NDB = DP / 32;
     constexpr int KS = D / 16;
-    constexpr int P = DP + 8;               // LDS row pitch (elements)
+    // LDS row pitch (elements).  The Q / dO tiles are read both by rows
+    // (16 bytes per lane) and by the transposing reads (8 bytes per lane, 4
+    // rows per 16-lane group); at 128 channels a 152-element pitch keeps the
+    // row reads conflict-free and halves the transposing reads' bank
+    // conflicts against DP + 8 (17% faster in an in-bounds probe).
+    constexpr int P = DP == 128 ? DP + 24 : DP + 8;
     constexpr int CPR = D / 8;              // 16-byte chunks per row
     constexpr int TILE = kQRows * P;
     constexpr int SP = DP + 4;              // pitch of the float32 transpose buffer
@@ -529,7 +534,7 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const BwdArgs a)
     constexpr int DP = (D + 31) / 32 * 32;
     constexpr int NDB = DP / 32;
     constexpr int KS = D / 16;
-    constexpr int P = DP + 8;
+    constexpr int P = DP == 128 ? DP + 24 : DP + 8;  // row pitch, as in the key-tile kernel
     constexpr int CPR = D / 8;
     constexpr int TILE = kKTile * P;
     constexpr int HPW = G < kDqWaves ? G : kDqWaves;  // heads per workgroup
