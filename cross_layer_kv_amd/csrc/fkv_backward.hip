@@ -274,21 +274,26 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
     constexpr int NPASS = (NITEM + kDkvThreads - 1) / kDkvThreads;
     uint4 xq[NPASS], xo[NPASS];
     float xl = 0.0f, xd = 0.0f;
+    // Q and dO rows of one tile through buffer descriptors whose base is the
+    // tile's first row (scalar work) and whose size ends at its last row
+    // inside S: rows past S-1 read as zero, and the lanes keep 32-bit
+    // offsets instead of 64-bit address arithmetic per load.
     auto load_tile = [&](int it, int tid) {
         const int qb = q_begin + (it / G) * kQRows;
         const int h = g * G + it % G;
+        const int64_t base = (((int64_t)b * S + qb) * a.Hq + h) * D;
+        const int rows = min(S - qb, kQRows);
+        const uint32_t rstride = (uint32_t)a.Hq * D * 2;  // bytes between rows
+        const uint32_t bytes = (uint32_t)(rows - 1) * rstride + D * 2;
+        const __amdgpu_buffer_rsrc_t rq = slab_rsrc(static_cast<const uint16_t*>(a.q) + base, bytes);
+        const __amdgpu_buffer_rsrc_t ro = slab_rsrc(static_cast<const uint16_t*>(a.dout) + base, bytes);
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
             const int e = tid + p * kDkvThreads;
             const int r = e / CPR, c = e - (e / CPR) * CPR;
-            const int row = qb + r;
-            xq[p] = make_uint4(0u, 0u, 0u, 0u);
-            xo[p] = xq[p];
-            if (e < NITEM && row < S) {
-                const int64_t off = (((int64_t)b * S + row) * a.Hq + h) * D + c * 8;
-                xq[p] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + off);
-                xo[p] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.dout) + off);
-            }
+            const uint32_t off = e < NITEM ? (uint32_t)r * rstride + c * 16 : kOffNone;
+            xq[p] = ld16(rq, off);
+            xo[p] = ld16(ro, off);
         }
         if (tid < kQRows) {
             const int row = qb + tid;
@@ -612,17 +617,24 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const BwdArgs a)
         __syncthreads();
     }
     uint4 xr[NSRC][NPASS];
+    // each source's tile through a buffer descriptor based at the tile's
+    // first key and ending at its last key inside S (keys past S-1 read as
+    // zero): 32-bit lane offsets instead of 64-bit address arithmetic
     auto load_tile = [&](int t) {
+        const int k0t = t * kKTile;
+        const int rows = min(S - k0t, kKTile);
 #pragma unroll
-        for (int p = 0; p < NPASS; ++p) {
-            const int r = sr + p * RPP;
-            const int key = t * kKTile + r;
-            const bool ok = s_active && r < kKTile && key < S;
+        for (int s_ = 0; s_ < NSRC; ++s_) {
+            const View& v = s_ == 0 ? a.k1 : (s_ == 1 ? a.v1 : (s_ == 2 ? a.kn : a.vn));
+            const uint32_t rs = (uint32_t)v.ss * 2;  // bytes between keys
+            const __amdgpu_buffer_rsrc_t rr = slab_rsrc(
+                static_cast<const uint16_t*>(v.data) + (int64_t)b * v.sb + (int64_t)k0t * v.ss + (int64_t)g * v.sh,
+                (uint32_t)(rows - 1) * rs + D * 2);
 #pragma unroll
-            for (int s_ = 0; s_ < NSRC; ++s_) {
-                const View& v = s_ == 0 ? a.k1 : (s_ == 1 ? a.v1 : (s_ == 2 ? a.kn : a.vn));
-                xr[s_][p] = ok ? *reinterpret_cast<const uint4*>(row_ptr(v, b, key, g) + sc * 8)
-                               : make_uint4(0u, 0u, 0u, 0u);
+            for (int p = 0; p < NPASS; ++p) {
+                const int r = sr + p * RPP;
+                const uint32_t off = (s_active && r < kKTile) ? (uint32_t)r * rs + sc * 16 : kOffNone;
+                xr[s_][p] = ld16(rr, off);
             }
         }
     };
