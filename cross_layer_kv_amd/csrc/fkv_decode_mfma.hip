@@ -25,7 +25,7 @@
 //     one head; the row max / sum take one exchange with the lane 32 apart.
 //     O^T += V~^T P^T reads V~ row-major through transposing LDS reads.
 //   * Tiles are fused into double-buffered LDS; the next tile's source loads
-//     are spread over the score k-steps.  One barrier per tile.
+//     are issued as the tile's score product starts.  One barrier per tile.
 //   * The two key halves of a head block merge in LDS at the end; with
 //     several splits, partial (max, sum, O) rows go to the workspace and a
 //     second kernel merges them per group of 8 heads.
@@ -227,7 +227,8 @@ __global__ __launch_bounds__(kHThreads, 2) void hgqa_decode_kernel(const DecodeA
         const bool more = t + 1 < nt;
         const int tbase = k0 + t * kHBN;
         // S^T for this wave's 32 keys x 32 heads; the next tile's loads are
-        // spread over the k-steps
+        // all issued with the first k-step, so they are in flight for the
+        // whole tile (1% faster than spreading them over the k-steps)
         f32x16 sacc = f32x16{};
         const uint16_t* kt = &Kt[buf][0] + (kh * 32 + l32) * KP + hi * 8;
         uint4 kf[KS];
@@ -235,9 +236,9 @@ __global__ __launch_bounds__(kHThreads, 2) void hgqa_decode_kernel(const DecodeA
         for (int ks = 0; ks < KS && ks < 2; ++ks) kf[ks] = *reinterpret_cast<const uint4*>(kt + ks * 16);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            if (more) {
+            if (more && ks == 0) {
 #pragma unroll
-                for (int i = ks * NL / KS; i < (ks + 1) * NL / KS; ++i) load_one(t + 1, i);
+                for (int i = 0; i < NL; ++i) load_one(t + 1, i);
             }
             if (ks + 2 < KS) kf[ks + 2] = *reinterpret_cast<const uint4*>(kt + (ks + 2) * 16);
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(kf[ks]), qreg[ks], sacc, 0, 0, 0);
