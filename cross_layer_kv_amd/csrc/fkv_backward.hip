@@ -325,31 +325,75 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
         load_tile(0, tid);
         store_tile(0, tid);
     }
-    for (int it = 0; it < nit; ++it) {
-        const int buf = it & 1;
-        // Lane indices re-derived per tile from an opaque copy of the thread
-        // index: the loop's address terms are then recomputed (a few VALU
-        // instructions) instead of held in registers across the loop, where
-        // they pushed the four-source kernel into scratch spills whose
-        // reloads waited on the next tile's loads.
-        int tid_o = tid;
-        asm volatile("" : "+v"(tid_o));
-        const int l32 = tid_o & 31, hi = (tid_o >> 5) & 1;
-        __syncthreads();  // tile `it` stored; tile it-1's readers are done
-        if (it + 1 < nit) load_tile(it + 1, tid_o);
-        const int qb = q_begin + (it / G) * kQRows;
-        const uint16_t* qs = smem + (buf * 2 + 0) * TILE;
-        const uint16_t* os = smem + (buf * 2 + 1) * TILE;
-        // one tile for one role (KW: key wave), compiled per role so each
-        // keeps only its own operands live
-        auto tile = [&](auto role) {
-            constexpr bool KW = decltype(role)::value;
-            // P (value waves) or dS (key waves) of sub-block sb (32 query
-            // rows) from its score (and dP) accumulators, then the product
-            auto finish = [&](const f32x16& sacc, const f32x16& pacc, int sb, bool masked) {
+    // The query-tile loop, instantiated once per wave role (KW: key wave)
+    // with one straight-line tile body: the accumulators then stay in one
+    // register set across the loop (branches merging inside the body made
+    // the compiler keep a second copy and move it every tile), and the
+    // registers left over hold LDS fragments read ahead of the matrix-core
+    // instructions that use them.
+    auto run = [&](auto role) {
+        constexpr bool KW = decltype(role)::value;
+        constexpr int PF = 2;  // k-steps of score fragments in flight
+        for (int it = 0; it < nit; ++it) {
+            const int buf = it & 1;
+            // Lane indices re-derived per tile from an opaque copy of the
+            // thread index: the loop's address terms are then recomputed (a
+            // few VALU instructions) instead of held in registers across the
+            // loop.
+            int tid_o = tid;
+            asm volatile("" : "+v"(tid_o));
+            const int l32 = tid_o & 31, hi = (tid_o >> 5) & 1;
+            __syncthreads();  // tile `it` stored; tile it-1's readers are done
+            if (it + 1 < nit) load_tile(it + 1, tid_o);
+            const int qb = q_begin + (it / G) * kQRows;
+            const uint16_t* qs = smem + (buf * 2 + 0) * TILE;
+            const uint16_t* os = smem + (buf * 2 + 1) * TILE;
+            // Tiles with any invisible (row, key) pair (causal diagonal, rows
+            // or keys past S) select zeros there; everything else is the same
+            // code, so a sub-block with no visible pair is computed and
+            // contributes zeros.
+            const bool masked = !(qb + 63 < S && kw + 31 < S && (!a.causal || qb >= kw + 31));
+            const int key = kw + l32;
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                // scores S^T (and dP^T) of 32 keys x 32 rows
+                f32x16 sacc, pacc;
+                uint4 fq[PF + 1], fo[PF + 1], fv[PF + 1];
+#pragma unroll
+                for (int ks = 0; ks < PF; ++ks) {
+                    fq[ks] = row_frag(qs, P, sb * 32, ks, l32, hi);
+                    if constexpr (KW) {
+                        fo[ks] = row_frag(os, P, sb * 32, ks, l32, hi);
+                        fv[ks] = row_frag(vsm, P, kb * 32, ks, l32, hi);
+                    }
+                }
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    if (ks + PF < KS) {
+                        const int n = (ks + PF) % (PF + 1);
+                        fq[n] = row_frag(qs, P, sb * 32, ks + PF, l32, hi);
+                        if constexpr (KW) {
+                            fo[n] = row_frag(os, P, sb * 32, ks + PF, l32, hi);
+                            fv[n] = row_frag(vsm, P, kb * 32, ks + PF, l32, hi);
+                        }
+                    }
+                    // the chains start from a zero operand, not zeroed registers
+                    const int c = ks % (PF + 1);
+                    sacc = mma(fq[c], kreg[ks], ks == 0 ? f32x16{} : sacc);
+                    if constexpr (KW) pacc = mma(fo[c], fv[c], ks == 0 ? f32x16{} : pacc);
+                }
+                // the product's transposed operand fragments (dK += dS^T Q,
+                // dV += P^T dO), read while the exponentials run
+                const uint16_t* other = KW ? qs : os;
+                uint4 tf[2][NDB];
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int nb = 0; nb < NDB; ++nb)
+                        tf[c][nb] = tr_frag(other, P, sb * 32 + 16 * c, nb * 32, l32, hi);
+                // P (value waves) or dS (key waves); lane: key kw + l32,
+                // entries: query rows qs0 + 8j + 4hi + i
                 const int qs0 = qb + sb * 32;
-                // lane: key kw + l32; entries: query rows qs0 + 8j + 4hi + i
-                const int key = kw + l32;
                 float xv[16];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -362,66 +406,39 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
                     }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int q = qs0 + 8 * j + 4 * hi + i;
-                        const bool vis = !masked || (key < S && q < S && (!a.causal || key <= q));
-                        const float p = vis ? exp2_fast(sacc[4 * j + i] * sl2 - Lv[i]) : 0.0f;
-                        if constexpr (KW)
-                            xv[4 * j + i] = p * (pacc[4 * j + i] - Dv[i]);
-                        else
-                            xv[4 * j + i] = p;
+                        const float p = exp2_fast(sacc[4 * j + i] * sl2 - Lv[i]);
+                        xv[4 * j + i] = KW ? p * (pacc[4 * j + i] - Dv[i]) : p;
                     }
                 }
-                const uint16_t* other = KW ? qs : os;  // dK += dS^T Q, dV += P^T dO
+                // invisible pairs select zero (their exponentials may be
+                // infinite); the branch is uniform and holds no accumulator
+                if (masked) {
+                    const bool key_ok = key < S;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int q = qs0 + 8 * (e >> 2) + 4 * hi + (e & 3);
+                        const bool vis = key_ok && q < S && (!a.causal || key <= q);
+                        xv[e] = vis ? xv[e] : 0.0f;
+                    }
+                }
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
                     const uint4 xa = make_uint4(pack2_bf16(xv[8 * c + 0], xv[8 * c + 1]), pack2_bf16(xv[8 * c + 2], xv[8 * c + 3]),
                                                 pack2_bf16(xv[8 * c + 4], xv[8 * c + 5]), pack2_bf16(xv[8 * c + 6], xv[8 * c + 7]));
 #pragma unroll
-                    for (int nb = 0; nb < NDB; ++nb)
-                        acc[nb] = mma(xa, tr_frag(other, P, sb * 32 + 16 * c, nb * 32, l32, hi), acc[nb]);
+                    for (int nb = 0; nb < NDB; ++nb) acc[nb] = mma(xa, tf[c][nb], acc[nb]);
                 }
-            };
-            auto scores = [&](int sb, f32x16& sacc, f32x16& pacc) {
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    sacc = mma(row_frag(qs, P, sb * 32, ks, l32, hi), kreg[ks], sacc);
-                    if constexpr (KW)
-                        pacc = mma(row_frag(os, P, sb * 32, ks, l32, hi), row_frag(vsm, P, kb * 32, ks, l32, hi), pacc);
-                }
-                // a fence for the scheduler: hoisting the next chain's (or the
-                // product's) fragment loads above this one runs a key wave out
-                // of registers at D = 128
+                // keeps the next sub-block's fragment reads below this one's
+                // products (hoisted, they run a wave out of registers)
                 __builtin_amdgcn_sched_barrier(0);
-            };
-            // Full tiles (every row and key inside S, and causally every key
-            // at or before every row) take the unmasked path.
-            const bool full = qb + 63 < S && kw + 31 < S && (!a.causal || qb >= kw + 31);
-            if (full) {
-#pragma unroll
-                for (int sb = 0; sb < 2; ++sb) {
-                    f32x16 sacc = f32x16{}, pacc = f32x16{};
-                    scores(sb, sacc, pacc);
-                    finish(sacc, pacc, sb, false);
-                }
-            } else {
-#pragma unroll
-                for (int sb = 0; sb < 2; ++sb) {
-                    const int qs0 = qb + sb * 32;
-                    // wave-uniform skips: rows past the end, or (causal) every
-                    // key of the block after every row of the sub-block
-                    if (qs0 >= S || (a.causal && qs0 + 31 < kw) || kw >= S) continue;
-                    f32x16 sacc = f32x16{}, pacc = f32x16{};
-                    scores(sb, sacc, pacc);
-                    finish(sacc, pacc, sb, true);
-                }
             }
-        };
-        if (kwave)
-            tile(std::true_type{});
-        else
-            tile(std::false_type{});
-        if (it + 1 < nit) store_tile(buf ^ 1, tid_o);
-    }
+            if (it + 1 < nit) store_tile(buf ^ 1, tid_o);
+        }
+    };
+    if (kwave)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
 
     // ---- epilogue: transpose each accumulator through LDS (float32) ----
     float* st = reinterpret_cast<float*>(smem);
@@ -684,23 +701,45 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const BwdArgs a)
         for (int kb = 0; kb < 2; ++kb) {
             const int kk0 = t * kKTile + kb * 32;
             if (kk0 >= S || r0 >= S || (a.causal && kk0 > r0 + 31)) continue;  // wave-uniform
-            f32x16 st = f32x16{}, dpt = f32x16{};
+            // S^T and dP^T chains; LDS fragments read PF k-steps ahead of the
+            // matrix-core instructions that use them
+            constexpr int PF = 2;
+            f32x16 st, dpt;
+            uint4 fk[PF + 1], fv[PF + 1];
+#pragma unroll
+            for (int ks = 0; ks < PF; ++ks) {
+                fk[ks] = row_frag(kt_, P, kb * 32, ks, l32, hi);
+                fv[ks] = row_frag(vt_, P, kb * 32, ks, l32, hi);
+            }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                st = mma(row_frag(kt_, P, kb * 32, ks, l32, hi), qreg[ks], st);
-                dpt = mma(row_frag(vt_, P, kb * 32, ks, l32, hi), oreg[ks], dpt);
+                if (ks + PF < KS) {
+                    fk[(ks + PF) % (PF + 1)] = row_frag(kt_, P, kb * 32, ks + PF, l32, hi);
+                    fv[(ks + PF) % (PF + 1)] = row_frag(vt_, P, kb * 32, ks + PF, l32, hi);
+                }
+                const int c = ks % (PF + 1);
+                st = mma(fk[c], qreg[ks], ks == 0 ? f32x16{} : st);
+                dpt = mma(fv[c], oreg[ks], ks == 0 ? f32x16{} : dpt);
             }
+            // the first half of the product's key fragments, read while the
+            // exponentials run
+            uint4 tf[NDB];
+#pragma unroll
+            for (int nb = 0; nb < NDB; ++nb) tf[nb] = tr_frag(kt_, P, kb * 32, nb * 32, l32, hi);
             // lane: query row; entries: keys kk0 + 8j + 4hi + i
             float dsv[16];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int e = 0; e < 16; ++e) dsv[e] = exp2_fast(st[e] * sl2 - lse2) * (dpt[e] - dlt);
+            // blocks with an invisible (row, key) pair select zero there (the
+            // exponentials may be infinite); the branch is uniform
+            if ((a.causal && kk0 + 31 > r0) || kk0 + 31 >= S || r0 + 31 >= S) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = kk0 + 8 * j + 4 * hi + i;
+                for (int e = 0; e < 16; ++e) {
+                    const int key = kk0 + 8 * (e >> 2) + 4 * hi + (e & 3);
                     const bool vis = row_ok && key < S && (!a.causal || key <= row);
-                    const float p = vis ? exp2_fast(st[4 * j + i] * sl2 - lse2) : 0.0f;
-                    dsv[4 * j + i] = p * (dpt[4 * j + i] - dlt);
+                    dsv[e] = vis ? dsv[e] : 0.0f;
                 }
+            }
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 const uint4 da = make_uint4(pack2_bf16(dsv[8 * c + 0], dsv[8 * c + 1]),
@@ -708,8 +747,11 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(const BwdArgs a)
                                             pack2_bf16(dsv[8 * c + 4], dsv[8 * c + 5]),
                                             pack2_bf16(dsv[8 * c + 6], dsv[8 * c + 7]));
 #pragma unroll
-                for (int nb = 0; nb < NDB; ++nb)
-                    dq[nb] = mma(da, tr_frag(kt_, P, kb * 32 + 16 * c, nb * 32, l32, hi), dq[nb]);
+                for (int nb = 0; nb < NDB; ++nb) {
+                    const uint4 f = tf[nb];
+                    if (c == 0) tf[nb] = tr_frag(kt_, P, kb * 32 + 16, nb * 32, l32, hi);
+                    dq[nb] = mma(da, f, dq[nb]);
+                }
             }
         }
         if (t + 1 < nt) store_tile(buf ^ 1);
