@@ -173,7 +173,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs a)
 // (scores, P, dVf += P^T dO), wave w >= 4 key block w - 4 for the keys
 // (scores, dP, dS, dKf += dS^T Q).  Each wave holds one accumulator and the
 // operands it needs, which fits two waves per SIMD (waves w and w + 4
-// share one); the scores are formed by both waves of a block.
+// share one); the scores are formed by both waves of a block.  The value
+// waves, with two products per tile against the key waves' three, also
+// stage the Q / dO tiles.
 template <int D, bool FUSED, int G>
 __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs a)
 {
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
 
     // ---- this block's 32 fused keys as B operands (lane: key l32); key
     // waves also stage the block's fused values in LDS ----
-    uint4 kreg[KS];
+    uint4 kreg[KS], vreg[KS];  // vreg: key waves' fused values (A operands of dP)
     {
         // This block's 32 keys as B operands (lane: key l32); key waves also
         // stage the block's values in LDS.  Four sources are fused here, one
@@ -254,6 +256,7 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
                 }
             }
             kreg[ks] = k;
+            vreg[ks] = v;
             if (kwave) *reinterpret_cast<uint4*>(vsm + (kb * 32 + l32) * P + ch) = v;
             if constexpr (FUSED) __builtin_amdgcn_sched_barrier(0);
         }
@@ -269,9 +272,13 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
     const int nqb = S > q_begin ? (S - q_begin + kQRows - 1) / kQRows : 0;
     const int nit = nqb * G;
 
-    // tile loader: thread -> (row, 16-byte chunk) items of Q and dO
+    // tile loader: thread -> (row, 16-byte chunk) items of Q and dO.  Only
+    // the value waves stage tiles: they have fewer products per tile than
+    // the key waves and would otherwise wait at the barrier, so the loads
+    // and stores leave the key waves' critical path.
+    constexpr int kStageThreads = kDkvThreads / 2;
     constexpr int NITEM = kQRows * CPR;
-    constexpr int NPASS = (NITEM + kDkvThreads - 1) / kDkvThreads;
+    constexpr int NPASS = (NITEM + kStageThreads - 1) / kStageThreads;
     uint4 xq[NPASS], xo[NPASS];
     float xl = 0.0f, xd = 0.0f;
     // Q and dO rows of one tile through buffer descriptors whose base is the
@@ -289,7 +296,7 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
         const __amdgpu_buffer_rsrc_t ro = slab_rsrc(static_cast<const uint16_t*>(a.dout) + base, bytes);
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
-            const int e = tid + p * kDkvThreads;
+            const int e = tid + p * kStageThreads;
             const int r = e / CPR, c = e - (e / CPR) * CPR;
             const uint32_t off = e < NITEM ? (uint32_t)r * rstride + c * 16 : kOffNone;
             xq[p] = ld16(rq, off);
@@ -307,7 +314,7 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
         uint16_t* os = smem + (buf * 2 + 1) * TILE;
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
-            const int e = tid + p * kDkvThreads;
+            const int e = tid + p * kStageThreads;
             if (e < NITEM) {
                 const int r = e / CPR, c = e - (e / CPR) * CPR;
                 *reinterpret_cast<uint4*>(qs + r * P + c * 8) = xq[p];
@@ -321,7 +328,7 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
     };
 
     const float sl2 = a.scale_log2;
-    if (nit > 0) {
+    if (nit > 0 && !kwave) {
         load_tile(0, tid);
         store_tile(0, tid);
     }
@@ -344,7 +351,7 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
             asm volatile("" : "+v"(tid_o));
             const int l32 = tid_o & 31, hi = (tid_o >> 5) & 1;
             __syncthreads();  // tile `it` stored; tile it-1's readers are done
-            if (it + 1 < nit) load_tile(it + 1, tid_o);
+            if (!KW && it + 1 < nit) load_tile(it + 1, tid_o);
             const int qb = q_begin + (it / G) * kQRows;
             const uint16_t* qs = smem + (buf * 2 + 0) * TILE;
             const uint16_t* os = smem + (buf * 2 + 1) * TILE;
@@ -358,29 +365,23 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
             for (int sb = 0; sb < 2; ++sb) {
                 // scores S^T (and dP^T) of 32 keys x 32 rows
                 f32x16 sacc, pacc;
-                uint4 fq[PF + 1], fo[PF + 1], fv[PF + 1];
+                uint4 fq[PF + 1], fo[PF + 1];
 #pragma unroll
                 for (int ks = 0; ks < PF; ++ks) {
                     fq[ks] = row_frag(qs, P, sb * 32, ks, l32, hi);
-                    if constexpr (KW) {
-                        fo[ks] = row_frag(os, P, sb * 32, ks, l32, hi);
-                        fv[ks] = row_frag(vsm, P, kb * 32, ks, l32, hi);
-                    }
+                    if constexpr (KW) fo[ks] = row_frag(os, P, sb * 32, ks, l32, hi);
                 }
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     if (ks + PF < KS) {
                         const int n = (ks + PF) % (PF + 1);
                         fq[n] = row_frag(qs, P, sb * 32, ks + PF, l32, hi);
-                        if constexpr (KW) {
-                            fo[n] = row_frag(os, P, sb * 32, ks + PF, l32, hi);
-                            fv[n] = row_frag(vsm, P, kb * 32, ks + PF, l32, hi);
-                        }
+                        if constexpr (KW) fo[n] = row_frag(os, P, sb * 32, ks + PF, l32, hi);
                     }
                     // the chains start from a zero operand, not zeroed registers
                     const int c = ks % (PF + 1);
                     sacc = mma(fq[c], kreg[ks], ks == 0 ? f32x16{} : sacc);
-                    if constexpr (KW) pacc = mma(fo[c], fv[c], ks == 0 ? f32x16{} : pacc);
+                    if constexpr (KW) pacc = mma(fo[c], vreg[ks], ks == 0 ? f32x16{} : pacc);
                 }
                 // the product's transposed operand fragments (dK += dS^T Q,
                 // dV += P^T dO), read while the exponentials run
@@ -432,7 +433,7 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
                 // products (hoisted, they run a wave out of registers)
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (it + 1 < nit) store_tile(buf ^ 1, tid_o);
+            if (!KW && it + 1 < nit) store_tile(buf ^ 1, tid_o);
         }
     };
     if (kwave)
