@@ -191,12 +191,13 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
     constexpr int CPR = D / 8;              // 16-byte chunks per row
     constexpr int TILE = kQRows * P;
     constexpr int SP = DP + 4;              // pitch of the float32 transpose buffer
-    static_assert(2 * 2 * TILE * 2 >= kKeysPerWg * SP * 4, "transpose buffer fits in the tile buffers");
+    constexpr int NBUF = 3;                 // Q / dO tile buffers in LDS
+    static_assert(NBUF * 2 * TILE * 2 >= kKeysPerWg * SP * 4, "transpose buffer fits in the tile buffers");
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];  // [buf][Q, dO][row][P]
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NBUF * 2 * TILE];  // [buf][Q, dO][row][P]
     __shared__ __attribute__((aligned(16))) uint16_t vsm[kKeysPerWg * P];   // fused values [key][P]
-    __shared__ __attribute__((aligned(16))) float Ls[2][kQRows];
-    __shared__ __attribute__((aligned(16))) float Dl[2][kQRows];
+    __shared__ __attribute__((aligned(16))) float Ls[NBUF][kQRows];
+    __shared__ __attribute__((aligned(16))) float Dl[NBUF][kQRows];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
 
     // zero the padded channels [D, DP) of every tile row (never loaded)
     if constexpr (DP > D) {
-        for (int i = tid; i < 2 * 2 * kQRows * (DP - D); i += kDkvThreads) {
+        for (int i = tid; i < NBUF * 2 * kQRows * (DP - D); i += kDkvThreads) {
             const int r = i / (DP - D), c = i - r * (DP - D);
             smem[r * P + D + c] = 0;
         }
@@ -312,11 +313,17 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
     auto store_tile = [&](int buf, int tid) {
         uint16_t* qs = smem + (buf * 2 + 0) * TILE;
         uint16_t* os = smem + (buf * 2 + 1) * TILE;
+        // tid < kStageThreads: passes below NITEM / kStageThreads are whole
+        // and are stored without a branch, at fixed offsets from one address
+        // when CPR divides kStageThreads
+        constexpr bool kEven = kStageThreads % CPR == 0;
+        const int r0 = tid / CPR, c0 = tid - (tid / CPR) * CPR;
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
             const int e = tid + p * kStageThreads;
-            if (e < NITEM) {
-                const int r = e / CPR, c = e - (e / CPR) * CPR;
+            const int r = kEven ? r0 + p * (kStageThreads / CPR) : e / CPR;
+            const int c = kEven ? c0 : e - (e / CPR) * CPR;
+            if ((p + 1) * kStageThreads <= NITEM || e < NITEM) {
                 *reinterpret_cast<uint4*>(qs + r * P + c * 8) = xq[p];
                 *reinterpret_cast<uint4*>(os + r * P + c * 8) = xo[p];
             }
@@ -328,9 +335,13 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
     };
 
     const float sl2 = a.scale_log2;
+    // Tiles are loaded two iterations ahead of use and stored to LDS one
+    // iteration ahead, right after the barrier, so a tile's loads have a
+    // whole iteration to arrive before the store waits on them.
     if (nit > 0 && !kwave) {
         load_tile(0, tid);
         store_tile(0, tid);
+        if (nit > 1) load_tile(1, tid);
     }
     // The query-tile loop, instantiated once per wave role (KW: key wave)
     // with one straight-line tile body: the accumulators then stay in one
@@ -341,8 +352,12 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
     auto run = [&](auto role) {
         constexpr bool KW = decltype(role)::value;
         constexpr int PF = 2;  // k-steps of score fragments in flight
-        for (int it = 0; it < nit; ++it) {
-            const int buf = it & 1;
+        if constexpr (KW) __builtin_amdgcn_s_setprio(1);  // the key waves carry more products
+        // one query tile; MASKED: some (row, key) pair of the tile is
+        // invisible (causal diagonal, rows or keys past S)
+        auto tile = [&](int it, auto masked_c) {
+            constexpr bool MASKED = decltype(masked_c)::value;
+            const int buf = it % NBUF;
             // Lane indices re-derived per tile from an opaque copy of the
             // thread index: the loop's address terms are then recomputed (a
             // few VALU instructions) instead of held in registers across the
@@ -351,26 +366,70 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
             asm volatile("" : "+v"(tid_o));
             const int l32 = tid_o & 31, hi = (tid_o >> 5) & 1;
             __syncthreads();  // tile `it` stored; tile it-1's readers are done
-            if (!KW && it + 1 < nit) load_tile(it + 1, tid_o);
+            if (!KW && it + 1 < nit) {
+                store_tile((it + 1) % NBUF, tid_o);  // tile it+1, loaded an iteration ago
+                if (it + 2 < nit) load_tile(it + 2, tid_o);
+            }
             const int qb = q_begin + (it / G) * kQRows;
             const uint16_t* qs = smem + (buf * 2 + 0) * TILE;
             const uint16_t* os = smem + (buf * 2 + 1) * TILE;
-            // Tiles with any invisible (row, key) pair (causal diagonal, rows
-            // or keys past S) select zeros there; everything else is the same
-            // code, so a sub-block with no visible pair is computed and
+            // Masked tiles select zeros at invisible pairs and are otherwise
+            // the same code: a sub-block with no visible pair is computed and
             // contributes zeros.
-            const bool masked = !(qb + 63 < S && kw + 31 < S && (!a.causal || qb >= kw + 31));
             const int key = kw + l32;
+            // Ls / Dl of the rows of entries 4j .. 4j+3 of sub-block sb
+            auto ld_rows = [&](int sb, int j, float4& L4, float4& D4) {
+                L4 = *reinterpret_cast<const float4*>(&Ls[buf][sb * 32 + 8 * j + 4 * hi]);
+                if constexpr (KW) D4 = *reinterpret_cast<const float4*>(&Dl[buf][sb * 32 + 8 * j + 4 * hi]);
+            };
+            // entry e of sub-block sb: P (value waves) or dS (key waves);
+            // lane: key kw + l32, entry e: query row qb + 32 sb + 8(e/4) + 4hi + e%4
+            auto prob = [&](int e, const float4& L4, const float4& D4, const f32x16& sacc, const f32x16& pacc) {
+                const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
+                const float p = exp2_fast(sacc[e] * sl2 - Lv[e & 3]);
+                if constexpr (KW) {
+                    const float Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+                    return p * (pacc[e] - Dv[e & 3]);
+                } else {
+                    return p;
+                }
+            };
+            // invisible pairs select zero (their exponentials may be infinite)
+            auto mask = [&](int sb, float* xv) {
+                if constexpr (MASKED) {
+                    const int qs0 = qb + sb * 32;
+                    const bool key_ok = key < S;
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                // scores S^T (and dP^T) of 32 keys x 32 rows
-                f32x16 sacc, pacc;
+                    for (int e = 0; e < 16; ++e) {
+                        const int q = qs0 + 8 * (e >> 2) + 4 * hi + (e & 3);
+                        const bool vis = key_ok & (q < S) & (!a.causal | (key <= q));
+                        xv[e] = vis ? xv[e] : 0.0f;
+                    }
+                }
+            };
+            auto pack = [&](const float* xv, uint4* xa) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+                    xa[c] = make_uint4(pack2_bf16(xv[8 * c + 0], xv[8 * c + 1]), pack2_bf16(xv[8 * c + 2], xv[8 * c + 3]),
+                                       pack2_bf16(xv[8 * c + 4], xv[8 * c + 5]), pack2_bf16(xv[8 * c + 6], xv[8 * c + 7]));
+            };
+            const uint16_t* other = KW ? qs : os;  // dK += dS^T Q, dV += P^T dO
+            // Scores S^T (and dP^T) of sub-block sb (32 keys x 32 rows), with
+            // the 16 entries of the previous sub-block's P / dS computed a
+            // few at a time between the matrix-core steps (prev_s: its score
+            // accumulators, or null for the first sub-block).  A scheduling
+            // fence after each step keeps the vector work beside the
+            // matrix-core instructions it overlaps.
+            auto scores = [&](int sb, f32x16& sacc, f32x16& pacc, int psb, const f32x16* ps, const f32x16* pp,
+                              float* xv) {
                 uint4 fq[PF + 1], fo[PF + 1];
+                float4 L4[4], D4[4];
 #pragma unroll
                 for (int ks = 0; ks < PF; ++ks) {
                     fq[ks] = row_frag(qs, P, sb * 32, ks, l32, hi);
                     if constexpr (KW) fo[ks] = row_frag(os, P, sb * 32, ks, l32, hi);
                 }
+                if (ps) ld_rows(psb, 0, L4[0], D4[0]);
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     if (ks + PF < KS) {
@@ -378,63 +437,78 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
                         fq[n] = row_frag(qs, P, sb * 32, ks + PF, l32, hi);
                         if constexpr (KW) fo[n] = row_frag(os, P, sb * 32, ks + PF, l32, hi);
                     }
-                    // the chains start from a zero operand, not zeroed registers
                     const int c = ks % (PF + 1);
                     sacc = mma(fq[c], kreg[ks], ks == 0 ? f32x16{} : sacc);
                     if constexpr (KW) pacc = mma(fo[c], vreg[ks], ks == 0 ? f32x16{} : pacc);
-                }
-                // the product's transposed operand fragments (dK += dS^T Q,
-                // dV += P^T dO), read while the exponentials run
-                const uint16_t* other = KW ? qs : os;
-                uint4 tf[2][NDB];
+                    if (ps) {
+                        const int e0 = ks * 16 / KS, e1 = (ks + 1) * 16 / KS;
+                        // the next step's row values, one step ahead
+                        const int j1 = e1 < 16 ? e1 >> 2 : 3;
+                        if (e1 < 16 && (e0 >> 2) != j1) ld_rows(psb, j1, L4[j1], D4[j1]);
 #pragma unroll
-                for (int c = 0; c < 2; ++c)
-#pragma unroll
-                    for (int nb = 0; nb < NDB; ++nb)
-                        tf[c][nb] = tr_frag(other, P, sb * 32 + 16 * c, nb * 32, l32, hi);
-                // P (value waves) or dS (key waves); lane: key kw + l32,
-                // entries: query rows qs0 + 8j + 4hi + i
-                const int qs0 = qb + sb * 32;
-                float xv[16];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float4 L4 = *reinterpret_cast<const float4*>(&Ls[buf][sb * 32 + 8 * j + 4 * hi]);
-                    const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
-                    float Dv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                    if constexpr (KW) {
-                        const float4 D4 = *reinterpret_cast<const float4*>(&Dl[buf][sb * 32 + 8 * j + 4 * hi]);
-                        Dv[0] = D4.x, Dv[1] = D4.y, Dv[2] = D4.z, Dv[3] = D4.w;
+                        for (int e = e0; e < e1; ++e) xv[e] = prob(e, L4[e >> 2], D4[e >> 2], *ps, *pp);
                     }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            // dK / dV += (dS or P)^T (Q or dO) over the 32 rows of sub-block
+            // sb, with the entries of sub-block nsb computed between the
+            // matrix-core steps (ns: its score accumulators, or null)
+            auto product = [&](int sb, const uint4* xa, int nsb, const f32x16* ns, const f32x16* np, float* xv) {
+                constexpr int NM = 2 * NDB;
+                uint4 tf[3];
+                float4 L4[4], D4[4];
+                tf[0] = tr_frag(other, P, sb * 32, 0, l32, hi);
+                if (NM > 1) tf[1] = tr_frag(other, P, sb * 32 + (NDB > 1 ? 0 : 16), (NDB > 1 ? 32 : 0), l32, hi);
+                if (ns) ld_rows(nsb, 0, L4[0], D4[0]);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float p = exp2_fast(sacc[4 * j + i] * sl2 - Lv[i]);
-                        xv[4 * j + i] = KW ? p * (pacc[4 * j + i] - Dv[i]) : p;
+                for (int m = 0; m < NM; ++m) {
+                    if (m + 2 < NM) {
+                        const int m2 = m + 2;
+                        tf[m2 % 3] = tr_frag(other, P, sb * 32 + 16 * (m2 / NDB), (m2 % NDB) * 32, l32, hi);
                     }
-                }
-                // invisible pairs select zero (their exponentials may be
-                // infinite); the branch is uniform and holds no accumulator
-                if (masked) {
-                    const bool key_ok = key < S;
+                    acc[m % NDB] = mma(xa[m / NDB], tf[m % 3], acc[m % NDB]);
+                    if (ns) {
+                        const int e0 = m * 16 / NM, e1 = (m + 1) * 16 / NM;
+                        const int j1 = e1 < 16 ? e1 >> 2 : 3;
+                        if (e1 < 16 && (e0 >> 2) != j1) ld_rows(nsb, j1, L4[j1], D4[j1]);
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int q = qs0 + 8 * (e >> 2) + 4 * hi + (e & 3);
-                        const bool vis = key_ok && q < S && (!a.causal || key <= q);
-                        xv[e] = vis ? xv[e] : 0.0f;
+                        for (int e = e0; e < e1; ++e) xv[e] = prob(e, L4[e >> 2], D4[e >> 2], *ns, *np);
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const uint4 xa = make_uint4(pack2_bf16(xv[8 * c + 0], xv[8 * c + 1]), pack2_bf16(xv[8 * c + 2], xv[8 * c + 3]),
-                                                pack2_bf16(xv[8 * c + 4], xv[8 * c + 5]), pack2_bf16(xv[8 * c + 6], xv[8 * c + 7]));
-#pragma unroll
-                    for (int nb = 0; nb < NDB; ++nb) acc[nb] = mma(xa, tf[c][nb], acc[nb]);
-                }
-                // keeps the next sub-block's fragment reads below this one's
-                // products (hoisted, they run a wave out of registers)
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if (!KW && it + 1 < nit) store_tile(buf ^ 1, tid_o);
+            };
+            // Two sub-blocks in a software pipeline: sub-block 1's score
+            // products run beside sub-block 0's exponentials, and sub-block
+            // 0's product beside sub-block 1's.
+            f32x16 s0, p0, s1, p1;
+            float xv[16];
+            uint4 xa[2];
+            scores(0, s0, p0, 0, nullptr, nullptr, xv);
+            scores(1, s1, p1, 0, &s0, &p0, xv);
+            mask(0, xv);
+            pack(xv, xa);
+            __builtin_amdgcn_sched_barrier(0);
+            product(0, xa, 1, &s1, &p1, xv);
+            mask(1, xv);
+            pack(xv, xa);
+            __builtin_amdgcn_sched_barrier(0);
+            product(1, xa, 0, nullptr, nullptr, xv);
+        };
+        // Iterations [it_lo, it_hi) see every (row, key) pair of this wave's
+        // block: the masked tiles are a causal prefix and a tail (rows past
+        // S, or every tile when the block's keys pass S).
+        int it_lo = 0, it_hi = nit;
+        if (kw + 31 >= S) {
+            it_hi = 0;
+        } else {
+            if (a.causal) it_lo = min(nit, (kw + 31 - q_begin + kQRows - 1) / kQRows * G);
+            it_hi = max(it_lo, (S - q_begin) / kQRows * G);
         }
+        int it = 0;
+        for (; it < it_lo; ++it) tile(it, std::true_type{});
+        for (; it < it_hi; ++it) tile(it, std::false_type{});
+        for (; it < nit; ++it) tile(it, std::true_type{});
     };
     if (kwave)
         run(std::true_type{});
