@@ -157,6 +157,19 @@ def test_lengths_and_full_attention(S):
         compare(c.run(), c.reference(), FUSED_NAMES)
 
 
+@pytest.mark.parametrize("D", [80, 128])
+def test_whole_tiles(D):
+    """S = 256: every 64-row query tile and 128-key block is whole.  Full
+    attention has no masked tile at all (the key-tile kernel's unmasked loop
+    alone); causal has masked diagonal tiles before unmasked ones."""
+    for causal in (False, True):
+        say("backward whole tiles D=%d causal=%s B=1 S=256 Hq=4 Hkv=2" % (D, causal))
+        c = Case(1, 256, 4, 2, D, 2400 + D, causal=causal)
+        compare(c.run(), c.reference(), FUSED_NAMES)
+        c = Case(1, 256, 4, 2, D, 2400 + D, causal=causal, lite=True)
+        compare(c.run(), c.reference(), LITE_NAMES)
+
+
 @pytest.mark.parametrize("layout", ["bhsd", "bshd"])
 def test_layouts(layout):
     say("backward layout=%s B=2 S=256 Hq=8 Hkv=4 D=96" % layout)
