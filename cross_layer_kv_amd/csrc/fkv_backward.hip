@@ -30,7 +30,8 @@
 //      head): four waves accumulate dVf and four dKf of one 32-key block
 //      each, keeping the block's fused keys (and values) as matrix-core
 //      operands in registers, and walk the query rows of all G heads of the
-//      group in 64-row LDS tiles.  It writes the
+//      group in 64-row LDS tiles; the value waves hand P (fp16) to the key
+//      waves through LDS, so the scores are formed once.  It writes the
 //      four source gradients and its partial column sums for the weight
 //      gradients.
 //   3. query tiles: a workgroup of 8 waves owns 256 (query row, head)
@@ -171,11 +172,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs a)
 // ---- 2. key tiles: dKf, dVf, source gradients, weight partials ----
 // Eight waves over 128 keys: wave w < 4 takes key block w for the values
 // (scores, P, dVf += P^T dO), wave w >= 4 key block w - 4 for the keys
-// (scores, dP, dS, dKf += dS^T Q).  Each wave holds one accumulator and the
-// operands it needs, which fits two waves per SIMD (waves w and w + 4
-// share one); the scores are formed by both waves of a block.  The value
-// waves, with two products per tile against the key waves' three, also
-// stage the Q / dO tiles.
+// (dP, dS = P (dP - delta), dKf += dS^T Q) one tile later, with the value
+// wave's P.  Each wave holds one accumulator and the operands it needs,
+// which fits two waves per SIMD (waves w and w + 4 share one); both have
+// two products per tile, and the value waves also stage the Q / dO tiles.
 template <int D, bool FUSED, int G>
 __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs a)
 {
@@ -195,7 +195,12 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
     static_assert(NBUF * 2 * TILE * 2 >= kKeysPerWg * SP * 4, "transpose buffer fits in the tile buffers");
 
     __shared__ __attribute__((aligned(16))) uint16_t smem[NBUF * 2 * TILE];  // [buf][Q, dO][row][P]
-    __shared__ __attribute__((aligned(16))) uint16_t vsm[kKeysPerWg * P];   // fused values [key][P]
+    // the P hand-off in the loop ([tile parity][key block][sub-block][chunk]
+    // [lane], 16 bytes each), then the weight-gradient partials in the
+    // epilogue ([key group][source][channel] floats)
+    constexpr int kXpBytes = 2 * 4 * 2 * 2 * 64 * 16;
+    constexpr int kRedBytes = (kKeysPerWg / 4) * 2 * D * 4;
+    __shared__ __attribute__((aligned(16))) uint4 xsm[(kXpBytes > kRedBytes ? kXpBytes : kRedBytes) / 16];
     __shared__ __attribute__((aligned(16))) float Ls[NBUF][kQRows];
     __shared__ __attribute__((aligned(16))) float Dl[NBUF][kQRows];
 
@@ -258,7 +263,6 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
             }
             kreg[ks] = k;
             vreg[ks] = v;
-            if (kwave) *reinterpret_cast<uint4*>(vsm + (kb * 32 + l32) * P + ch) = v;
             if constexpr (FUSED) __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -343,60 +347,68 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
         store_tile(0, tid);
         if (nit > 1) load_tile(1, tid);
     }
+    // P hand-off from the value waves to the key waves: [tile parity][key
+    // block][sub-block][16-byte chunk][lane], fp16 (P <= 1), in the fused
+    // value tile, which the loop no longer reads (the key waves hold their
+    // fused values in registers).
+    auto xp_chunk = [&](int par, int sb, int c, int lane_) { return xsm + (((par * 4 + kb) * 2 + sb) * 2 + c) * 64 + lane_; };
     // The query-tile loop, instantiated once per wave role (KW: key wave)
     // with one straight-line tile body: the accumulators then stay in one
     // register set across the loop (branches merging inside the body made
     // the compiler keep a second copy and move it every tile), and the
     // registers left over hold LDS fragments read ahead of the matrix-core
-    // instructions that use them.
+    // instructions that use them.  The value waves form the scores and P of
+    // tile it and hand P to the key waves, which take tile it one iteration
+    // later (dP, dS = P (dP - delta), dK): the per-tile barrier orders the
+    // hand-off, and no score product is formed twice.
     auto run = [&](auto role) {
         constexpr bool KW = decltype(role)::value;
-        constexpr int PF = 2;  // k-steps of score fragments in flight
-        if constexpr (KW) __builtin_amdgcn_s_setprio(1);  // the key waves carry more products
-        // one query tile; MASKED: some (row, key) pair of the tile is
-        // invisible (causal diagonal, rows or keys past S)
+        constexpr int PF = 2;  // k-steps of fragments in flight
+        // one query tile (the value waves' tile it, the key waves' tile it-1);
+        // MASKED (value waves): some (row, key) pair of the tile is invisible
+        // (causal diagonal, rows or keys past S)
         auto tile = [&](int it, auto masked_c) {
             constexpr bool MASKED = decltype(masked_c)::value;
-            const int buf = it % NBUF;
             // Lane indices re-derived per tile from an opaque copy of the
             // thread index: the loop's address terms are then recomputed (a
             // few VALU instructions) instead of held in registers across the
             // loop.
             int tid_o = tid;
             asm volatile("" : "+v"(tid_o));
-            const int l32 = tid_o & 31, hi = (tid_o >> 5) & 1;
-            __syncthreads();  // tile `it` stored; tile it-1's readers are done
+            const int l32 = tid_o & 31, hi = (tid_o >> 5) & 1, lane_o = tid_o & 63;
+            __syncthreads();  // tile `it` stored, P of tile it-1 handed over; older readers done
             if (!KW && it + 1 < nit) {
                 store_tile((it + 1) % NBUF, tid_o);  // tile it+1, loaded an iteration ago
                 if (it + 2 < nit) load_tile(it + 2, tid_o);
             }
-            const int qb = q_begin + (it / G) * kQRows;
+            const int t = KW ? it - 1 : it;  // the tile this wave works on
+            const int buf = t % NBUF, par = t & 1;
+            const int qb = q_begin + (t / G) * kQRows;
             const uint16_t* qs = smem + (buf * 2 + 0) * TILE;
             const uint16_t* os = smem + (buf * 2 + 1) * TILE;
-            // Masked tiles select zeros at invisible pairs and are otherwise
-            // the same code: a sub-block with no visible pair is computed and
-            // contributes zeros.
             const int key = kw + l32;
-            // Ls / Dl of the rows of entries 4j .. 4j+3 of sub-block sb
-            auto ld_rows = [&](int sb, int j, float4& L4, float4& D4) {
-                L4 = *reinterpret_cast<const float4*>(&Ls[buf][sb * 32 + 8 * j + 4 * hi]);
-                if constexpr (KW) D4 = *reinterpret_cast<const float4*>(&Dl[buf][sb * 32 + 8 * j + 4 * hi]);
+            // Ls (value waves) or Dl (key waves) of the rows of entries
+            // 4j .. 4j+3 of sub-block sb
+            auto ld_rows = [&](int sb, int j, float4& R4) {
+                R4 = *reinterpret_cast<const float4*>(KW ? &Dl[buf][sb * 32 + 8 * j + 4 * hi]
+                                                         : &Ls[buf][sb * 32 + 8 * j + 4 * hi]);
             };
-            // entry e of sub-block sb: P (value waves) or dS (key waves);
-            // lane: key kw + l32, entry e: query row qb + 32 sb + 8(e/4) + 4hi + e%4
-            auto prob = [&](int e, const float4& L4, const float4& D4, const f32x16& sacc, const f32x16& pacc) {
-                const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
-                const float p = exp2_fast(sacc[e] * sl2 - Lv[e & 3]);
+            // entry e of sub-block sb: P (value waves, from the score) or dS
+            // (key waves, from the handed-over P and dP); lane: key kw + l32,
+            // entry e: query row qb + 32 sb + 8(e/4) + 4hi + e%4
+            auto entry = [&](int e, const float4& R4, const f32x16& acc_s, const uint4* ph) {
+                const float Rv[4] = {R4.x, R4.y, R4.z, R4.w};
                 if constexpr (KW) {
-                    const float Dv[4] = {D4.x, D4.y, D4.z, D4.w};
-                    return p * (pacc[e] - Dv[e & 3]);
+                    const uint32_t w[8] = {ph[0].x, ph[0].y, ph[0].z, ph[0].w, ph[1].x, ph[1].y, ph[1].z, ph[1].w};
+                    const float p = (float)__builtin_bit_cast(f16x2, w[e >> 1])[e & 1];
+                    return p * (acc_s[e] - Rv[e & 3]);
                 } else {
-                    return p;
+                    return exp2_fast(acc_s[e] * sl2 - Rv[e & 3]);
                 }
             };
             // invisible pairs select zero (their exponentials may be infinite)
             auto mask = [&](int sb, float* xv) {
-                if constexpr (MASKED) {
+                if constexpr (!KW && MASKED) {
                     const int qs0 = qb + sb * 32;
                     const bool key_ok = key < S;
 #pragma unroll
@@ -407,60 +419,73 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
                     }
                 }
             };
-            auto pack = [&](const float* xv, uint4* xa) {
+            // bf16 A operands of the product; the value waves also hand P
+            // over as fp16
+            auto pack = [&](int sb, const float* xv, uint4* xa) {
 #pragma unroll
                 for (int c = 0; c < 2; ++c)
                     xa[c] = make_uint4(pack2_bf16(xv[8 * c + 0], xv[8 * c + 1]), pack2_bf16(xv[8 * c + 2], xv[8 * c + 3]),
                                        pack2_bf16(xv[8 * c + 4], xv[8 * c + 5]), pack2_bf16(xv[8 * c + 6], xv[8 * c + 7]));
+                if constexpr (!KW) {
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+                        *xp_chunk(par, sb, c, lane_o) = make_uint4(pack2(xv[8 * c + 0], xv[8 * c + 1]), pack2(xv[8 * c + 2], xv[8 * c + 3]),
+                                                                   pack2(xv[8 * c + 4], xv[8 * c + 5]), pack2(xv[8 * c + 6], xv[8 * c + 7]));
+                }
             };
             const uint16_t* other = KW ? qs : os;  // dK += dS^T Q, dV += P^T dO
-            // Scores S^T (and dP^T) of sub-block sb (32 keys x 32 rows), with
-            // the 16 entries of the previous sub-block's P / dS computed a
-            // few at a time between the matrix-core steps (prev_s: its score
-            // accumulators, or null for the first sub-block).  A scheduling
-            // fence after each step keeps the vector work beside the
-            // matrix-core instructions it overlaps.
-            auto scores = [&](int sb, f32x16& sacc, f32x16& pacc, int psb, const f32x16* ps, const f32x16* pp,
-                              float* xv) {
-                uint4 fq[PF + 1], fo[PF + 1];
-                float4 L4[4], D4[4];
+            // The score chain S^T = Q K~^T (value waves) or dP^T = dO V~^T
+            // (key waves) of sub-block sb (32 keys x 32 rows), with the 16
+            // entries of the previous sub-block psb computed a few at a time
+            // between the matrix-core steps (ps: its chain accumulator, or
+            // null for the first sub-block).  A scheduling fence after each
+            // step keeps the vector work beside the matrix-core instructions
+            // it overlaps.
+            auto chain = [&](int sb, f32x16& cacc, int psb, const f32x16* ps, float* xv) {
+                const uint16_t* src = KW ? os : qs;
+                uint4 fr[PF + 1], ph[2];
+                float4 R4[4];
 #pragma unroll
-                for (int ks = 0; ks < PF; ++ks) {
-                    fq[ks] = row_frag(qs, P, sb * 32, ks, l32, hi);
-                    if constexpr (KW) fo[ks] = row_frag(os, P, sb * 32, ks, l32, hi);
+                for (int ks = 0; ks < PF; ++ks) fr[ks] = row_frag(src, P, sb * 32, ks, l32, hi);
+                if (ps) {
+                    ld_rows(psb, 0, R4[0]);
+                    if constexpr (KW) {
+                        ph[0] = *xp_chunk(par, psb, 0, lane_o);
+                        ph[1] = *xp_chunk(par, psb, 1, lane_o);
+                    }
                 }
-                if (ps) ld_rows(psb, 0, L4[0], D4[0]);
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    if (ks + PF < KS) {
-                        const int n = (ks + PF) % (PF + 1);
-                        fq[n] = row_frag(qs, P, sb * 32, ks + PF, l32, hi);
-                        if constexpr (KW) fo[n] = row_frag(os, P, sb * 32, ks + PF, l32, hi);
-                    }
-                    const int c = ks % (PF + 1);
-                    sacc = mma(fq[c], kreg[ks], ks == 0 ? f32x16{} : sacc);
-                    if constexpr (KW) pacc = mma(fo[c], vreg[ks], ks == 0 ? f32x16{} : pacc);
+                    if (ks + PF < KS) fr[(ks + PF) % (PF + 1)] = row_frag(src, P, sb * 32, ks + PF, l32, hi);
+                    // the chain starts from a zero operand, not zeroed registers
+                    cacc = mma(fr[ks % (PF + 1)], KW ? vreg[ks] : kreg[ks], ks == 0 ? f32x16{} : cacc);
                     if (ps) {
                         const int e0 = ks * 16 / KS, e1 = (ks + 1) * 16 / KS;
                         // the next step's row values, one step ahead
                         const int j1 = e1 < 16 ? e1 >> 2 : 3;
-                        if (e1 < 16 && (e0 >> 2) != j1) ld_rows(psb, j1, L4[j1], D4[j1]);
+                        if (e1 < 16 && (e0 >> 2) != j1) ld_rows(psb, j1, R4[j1]);
 #pragma unroll
-                        for (int e = e0; e < e1; ++e) xv[e] = prob(e, L4[e >> 2], D4[e >> 2], *ps, *pp);
+                        for (int e = e0; e < e1; ++e) xv[e] = entry(e, R4[e >> 2], *ps, ph);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
             };
             // dK / dV += (dS or P)^T (Q or dO) over the 32 rows of sub-block
             // sb, with the entries of sub-block nsb computed between the
-            // matrix-core steps (ns: its score accumulators, or null)
-            auto product = [&](int sb, const uint4* xa, int nsb, const f32x16* ns, const f32x16* np, float* xv) {
+            // matrix-core steps (ns: its chain accumulator, or null)
+            auto product = [&](int sb, const uint4* xa, int nsb, const f32x16* ns, float* xv) {
                 constexpr int NM = 2 * NDB;
-                uint4 tf[3];
-                float4 L4[4], D4[4];
+                uint4 tf[3], ph[2];
+                float4 R4[4];
                 tf[0] = tr_frag(other, P, sb * 32, 0, l32, hi);
                 if (NM > 1) tf[1] = tr_frag(other, P, sb * 32 + (NDB > 1 ? 0 : 16), (NDB > 1 ? 32 : 0), l32, hi);
-                if (ns) ld_rows(nsb, 0, L4[0], D4[0]);
+                if (ns) {
+                    ld_rows(nsb, 0, R4[0]);
+                    if constexpr (KW) {
+                        ph[0] = *xp_chunk(par, nsb, 0, lane_o);
+                        ph[1] = *xp_chunk(par, nsb, 1, lane_o);
+                    }
+                }
 #pragma unroll
                 for (int m = 0; m < NM; ++m) {
                     if (m + 2 < NM) {
@@ -471,44 +496,54 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
                     if (ns) {
                         const int e0 = m * 16 / NM, e1 = (m + 1) * 16 / NM;
                         const int j1 = e1 < 16 ? e1 >> 2 : 3;
-                        if (e1 < 16 && (e0 >> 2) != j1) ld_rows(nsb, j1, L4[j1], D4[j1]);
+                        if (e1 < 16 && (e0 >> 2) != j1) ld_rows(nsb, j1, R4[j1]);
 #pragma unroll
-                        for (int e = e0; e < e1; ++e) xv[e] = prob(e, L4[e >> 2], D4[e >> 2], *ns, *np);
+                        for (int e = e0; e < e1; ++e) xv[e] = entry(e, R4[e >> 2], *ns, ph);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
             };
-            // Two sub-blocks in a software pipeline: sub-block 1's score
-            // products run beside sub-block 0's exponentials, and sub-block
-            // 0's product beside sub-block 1's.
-            f32x16 s0, p0, s1, p1;
+            if (KW && it == 0) return;  // the key waves' tile -1: the barrier only
+            // Two sub-blocks in a software pipeline: sub-block 1's chain runs
+            // beside sub-block 0's entries, and sub-block 0's product beside
+            // sub-block 1's.
+            f32x16 c0, c1;
             float xv[16];
             uint4 xa[2];
-            scores(0, s0, p0, 0, nullptr, nullptr, xv);
-            scores(1, s1, p1, 0, &s0, &p0, xv);
+            chain(0, c0, 0, nullptr, xv);
+            chain(1, c1, 0, &c0, xv);
             mask(0, xv);
-            pack(xv, xa);
+            pack(0, xv, xa);
             __builtin_amdgcn_sched_barrier(0);
-            product(0, xa, 1, &s1, &p1, xv);
+            product(0, xa, 1, &c1, xv);
             mask(1, xv);
-            pack(xv, xa);
+            pack(1, xv, xa);
             __builtin_amdgcn_sched_barrier(0);
-            product(1, xa, 0, nullptr, nullptr, xv);
+            product(1, xa, 0, nullptr, xv);
         };
-        // Iterations [it_lo, it_hi) see every (row, key) pair of this wave's
-        // block: the masked tiles are a causal prefix and a tail (rows past
-        // S, or every tile when the block's keys pass S).
-        int it_lo = 0, it_hi = nit;
-        if (kw + 31 >= S) {
-            it_hi = 0;
+        if constexpr (KW) {
+            // key waves: the barrier of iteration 0, then tiles 0 .. nit-1 in
+            // iterations 1 .. nit
+            // (nit + 1 barriers, as the value waves)
+            if (nit > 0)
+                for (int it = 0; it <= nit; ++it) tile(it, std::false_type{});
         } else {
-            if (a.causal) it_lo = min(nit, (kw + 31 - q_begin + kQRows - 1) / kQRows * G);
-            it_hi = max(it_lo, (S - q_begin) / kQRows * G);
+            // Iterations [it_lo, it_hi) see every (row, key) pair of this
+            // wave's block: the masked tiles are a causal prefix and a tail
+            // (rows past S, or every tile when the block's keys pass S).
+            int it_lo = 0, it_hi = nit;
+            if (kw + 31 >= S) {
+                it_hi = 0;
+            } else {
+                if (a.causal) it_lo = min(nit, (kw + 31 - q_begin + kQRows - 1) / kQRows * G);
+                it_hi = max(it_lo, (S - q_begin) / kQRows * G);
+            }
+            int it = 0;
+            for (; it < it_lo; ++it) tile(it, std::true_type{});
+            for (; it < it_hi; ++it) tile(it, std::false_type{});
+            for (; it < nit; ++it) tile(it, std::true_type{});
+            if (nit > 0) __syncthreads();  // the key waves' last iteration
         }
-        int it = 0;
-        for (; it < it_lo; ++it) tile(it, std::true_type{});
-        for (; it < it_hi; ++it) tile(it, std::false_type{});
-        for (; it < nit; ++it) tile(it, std::true_type{});
     };
     if (kwave)
         run(std::true_type{});
@@ -565,13 +600,13 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
             // column sums over this tile's keys of dKf * K1 and dKf * Kn
             // (values: dVf * V1, dVf * Vn): a thread takes 8 channels of 4
             // keys (its 8 source loads in flight together), the 32 key
-            // groups' partials meet in the idle value tile, and one thread
+            // groups' partials meet in the hand-off array, and one thread
             // per (source, channel) adds them in a fixed order
             constexpr int NCH = D / 8;
             constexpr int KPT = 4, NKG = kKeysPerWg / KPT;
             static_assert(NKG * NCH <= kDkvThreads, "one (key group, chunk) item per thread");
-            static_assert(NKG * 2 * D * 4 <= kKeysPerWg * P * 2, "partials fit in the value tile");
-            float* red = reinterpret_cast<float*>(vsm);  // [NKG][2][D]
+            static_assert(NKG * 2 * D * 4 <= (int)sizeof(xsm), "partials fit in the shared array");
+            float* red = reinterpret_cast<float*>(xsm);  // [NKG][2][D]
             const View& s1 = which == 0 ? a.k1 : a.v1;
             const View& sn = which == 0 ? a.kn : a.vn;
             if (tid < NKG * NCH) {
