@@ -347,10 +347,8 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
         store_tile(0, tid);
         if (nit > 1) load_tile(1, tid);
     }
-    // P hand-off from the value waves to the key waves: [tile parity][key
-    // block][sub-block][16-byte chunk][lane], fp16 (P <= 1), in the fused
-    // value tile, which the loop no longer reads (the key waves hold their
-    // fused values in registers).
+    // P hand-off from the value waves to the key waves in the shared array:
+    // [tile parity][key block][sub-block][16-byte chunk][lane], fp16 (P <= 1)
     auto xp_chunk = [&](int par, int sb, int c, int lane_) { return xsm + (((par * 4 + kb) * 2 + sb) * 2 + c) * 64 + lane_; };
     // The query-tile loop, instantiated once per wave role (KW: key wave)
     // with one straight-line tile body: the accumulators then stay in one
