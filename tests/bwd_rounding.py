@@ -4,7 +4,9 @@ module, and not an implementation the kernels are compared with).
 The fp64 backward oracle (oracle/backward.py) is evaluated a second time
 with bfloat16 rounding applied at the points where the kernels round:
   * the fused key and value tiles (matrix-core operands),
-  * the probabilities P and dS = P (dP - Delta) (matrix-core operands),
+  * the probabilities P and dS = P (dP - Delta) (matrix-core operands;
+    the key-tile kernel forms its dS from P rounded once to binary16,
+    2^-11, which is left out here as an eighth of a bfloat16 rounding),
   * Delta = rowsum(dO * O) taken from the bfloat16 forward output O,
   * the bfloat16 gradient outputs.
 Its error against the exact oracle is the error this arithmetic has by
