@@ -230,16 +230,14 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
         }
     }
 
-    // ---- this block's 32 fused keys as B operands (lane: key l32); key
-    // waves also stage the block's fused values in LDS ----
-    uint4 kreg[KS], vreg[KS];  // vreg: key waves' fused values (A operands of dP)
+    // ---- this block's 32 fused keys (and, key waves, values) as MFMA
+    // operands in registers (lane: key l32) ----
+    uint4 kreg[KS], vreg[KS];  // vreg: key waves' fused values (B operands of dP)
     {
-        // This block's 32 keys as B operands (lane: key l32); key waves also
-        // stage the block's values in LDS.  Four sources are fused here, one
-        // 8-channel chunk at a time, in float32 and rounded to bf16: the
-        // fused rows exist only in registers and LDS.  The scheduling fence
-        // after each chunk keeps the compiler from hoisting every chunk's
-        // loads and weights at once.
+        // Four sources are fused here, one 8-channel chunk at a time, in
+        // float32 and rounded to bf16: the fused rows exist only in
+        // registers.  The scheduling fence after each chunk keeps the
+        // compiler from hoisting every chunk's loads and weights at once.
         const int key = kw + l32;
         const bool ok = key < S;
 #pragma unroll
@@ -277,10 +275,9 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
     const int nqb = S > q_begin ? (S - q_begin + kQRows - 1) / kQRows : 0;
     const int nit = nqb * G;
 
-    // tile loader: thread -> (row, 16-byte chunk) items of Q and dO.  Only
-    // the value waves stage tiles: they have fewer products per tile than
-    // the key waves and would otherwise wait at the barrier, so the loads
-    // and stores leave the key waves' critical path.
+    // tile loader: thread -> (row, 16-byte chunk) items of Q and dO, staged
+    // by the value waves (the key waves, a tile behind, measured slower with
+    // a share of the staging).
     constexpr int kStageThreads = kDkvThreads / 2;
     constexpr int NITEM = kQRows * CPR;
     constexpr int NPASS = (NITEM + kStageThreads - 1) / kStageThreads;
@@ -379,6 +376,7 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
                 store_tile((it + 1) % NBUF, tid_o);  // tile it+1, loaded an iteration ago
                 if (it + 2 < nit) load_tile(it + 2, tid_o);
             }
+            if (KW && it == 0) return;  // the key waves' tile -1: the barrier only
             const int t = KW ? it - 1 : it;  // the tile this wave works on
             const int buf = t % NBUF, par = t & 1;
             const int qb = q_begin + (t / G) * kQRows;
@@ -501,7 +499,6 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
                     __builtin_amdgcn_sched_barrier(0);
                 }
             };
-            if (KW && it == 0) return;  // the key waves' tile -1: the barrier only
             // Two sub-blocks in a software pipeline: sub-block 1's chain runs
             // beside sub-block 0's entries, and sub-block 0's product beside
             // sub-block 1's.
