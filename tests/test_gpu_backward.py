@@ -170,6 +170,15 @@ def test_whole_tiles(D):
         compare(c.run(), c.reference(), LITE_NAMES)
 
 
+def test_long_ragged_full_attention():
+    """S = 1000 without a mask and G = 4: many query tiles through the
+    key-tile kernel's P hand-off and its three tile buffers, every key block
+    live, a ragged 40-row tail."""
+    say("backward long ragged full B=1 S=1000 Hq=8 Hkv=2 D=96")
+    c = Case(1, 1000, 8, 2, 96, 2501, causal=False)
+    compare(c.run(), c.reference(), FUSED_NAMES)
+
+
 @pytest.mark.parametrize("layout", ["bhsd", "bshd"])
 def test_layouts(layout):
     say("backward layout=%s B=2 S=256 Hq=8 Hkv=4 D=96" % layout)
