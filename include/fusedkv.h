@@ -372,8 +372,11 @@ size_t fkv_backward_workspace_size(const fkv_params* params);
  * seqlen_k, bfloat16 data, G in {1, 2, 4, 8}, causal 0 or 1.  Recomputes the
  * probabilities from the forward LSE; matrix-core operands are bfloat16
  * (fused tiles, probabilities and dS rounded once from float32), all
- * accumulation float32.  Outputs are overwritten, not accumulated.  Every
- * result is run-to-run deterministic (no float atomics).
+ * accumulation float32; the key-gradient pass forms dS from the
+ * probabilities rounded to binary16, which holds them because P <= 1 when
+ * lse is the forward's row log-sum-exp (another lse voids the results).
+ * Outputs are overwritten, not accumulated.  Every result is run-to-run
+ * deterministic (no float atomics).
  *
  *   q, out, dout  device [B, S, H_q, D] bfloat16 (out: the forward output)
  *   lse           device float32 [B, H_q, S] (the forward LSE, natural log)
