@@ -31,9 +31,11 @@
 //      each, keeping the block's fused keys (and values) as matrix-core
 //      operands in registers, and walk the query rows of all G heads of the
 //      group in 64-row LDS tiles; the value waves hand P (fp16) to the key
-//      waves through LDS, so the scores are formed once.  It writes the
-//      four source gradients and its partial column sums for the weight
-//      gradients.
+//      waves through LDS, so the scores are formed once.  At 128 channels
+//      the Q / dO tiles are copied from memory straight into LDS (buffer
+//      loads with an LDS destination), elsewhere through registers.  It
+//      writes the four source gradients and its partial column sums for
+//      the weight gradients.
 //   3. query tiles: a workgroup of 8 waves owns 256 (query row, head)
 //      columns and walks 64-key tiles staged in LDS, accumulating dQ; four
 //      sources are fused as each tile is staged.  dQ is thus written once,
@@ -101,6 +103,35 @@ __device__ __forceinline__ uint4 tr_frag(const uint16_t* tile, int pitch, int kr
     const uint16_t* p = tile + (krow0 + hi * 4 + ((l32 & 15) >> 2)) * pitch + col0 + (l32 >> 4) * 16 + (l32 & 3) * 4;
     const v4s x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
     const v4s x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p + 8 * pitch));
+    return __builtin_bit_cast(uint4, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// s_waitcnt operand: vector memory count 0, the other counters at their
+// maximum (no wait).
+constexpr int kWaitLoads = 0x0F70;
+
+// Unpadded 128-channel tiles (256-byte rows), filled by direct-to-LDS loads
+// that write 1 KB contiguous per instruction: logical 16-byte chunk c of row
+// r sits at chunk c ^ swz(r).  swz permutes the low four row bits, so 16
+// consecutive rows put one chunk in 16 different chunk slots (row reads),
+// and rows 4k .. 4k+3 put a chunk pair in 8 different slots (transposing
+// reads).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
+
+__device__ __forceinline__ uint4 row_frag_sw(const uint16_t* tile, int r0, int ks, int l32, int hi)
+{
+    const int r = r0 + l32;
+    return *reinterpret_cast<const uint4*>(tile + r * 128 + (((2 * ks + hi) ^ swz(r)) << 3));
+}
+
+__device__ __forceinline__ uint4 tr_frag_sw(const uint16_t* tile, int krow0, int col0, int l32, int hi)
+{
+    const int r = krow0 + hi * 4 + ((l32 & 15) >> 2);
+    const int e = col0 + (l32 >> 4) * 16 + (l32 & 3) * 4;
+    const uint16_t* p0 = tile + r * 128 + (((e >> 3) ^ swz(r)) << 3) + (e & 7);
+    const uint16_t* p1 = tile + (r + 8) * 128 + (((e >> 3) ^ swz(r + 8)) << 3) + (e & 7);
+    const v4s x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p0);
+    const v4s x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p1);
     return __builtin_bit_cast(uint4, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -187,7 +218,10 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
     // rows per 16-lane group); at 128 channels a 152-element pitch keeps the
     // row reads conflict-free and halves the transposing reads' bank
     // conflicts against DP + 8 (17% faster in an in-bounds probe).
-    constexpr int P = DP == 128 ? DP + 24 : DP + 8;
+    // At 128 channels the Q / dO tiles arrive by direct-to-LDS loads into
+    // unpadded, swizzled 256-byte rows.
+    constexpr bool kDma = D == 128;
+    constexpr int P = kDma ? 128 : (DP == 128 ? DP + 24 : DP + 8);
     constexpr int CPR = D / 8;              // 16-byte chunks per row
     constexpr int TILE = kQRows * P;
     constexpr int SP = DP + 4;              // pitch of the float32 transpose buffer
@@ -275,9 +309,9 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
     const int nqb = S > q_begin ? (S - q_begin + kQRows - 1) / kQRows : 0;
     const int nit = nqb * G;
 
-    // tile loader: thread -> (row, 16-byte chunk) items of Q and dO, staged
-    // by the value waves (the key waves, a tile behind, measured slower with
-    // a share of the staging).
+    // register staging (below 128 channels): thread -> (row, 16-byte chunk)
+    // items of Q and dO, staged by the value waves (the key waves, a tile
+    // behind, measured slower with a share of the staging).
     constexpr int kStageThreads = kDkvThreads / 2;
     constexpr int NITEM = kQRows * CPR;
     constexpr int NPASS = (NITEM + kStageThreads - 1) / kStageThreads;
@@ -335,14 +369,57 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
         }
     };
 
+    // 128 channels: each value wave copies 16 of the tile's rows of Q and dO
+    // straight from memory into LDS, four 1 KB load instructions per tensor
+    // (lane l: 16 bytes of row 4j + l/16, placed as the swizzle puts them),
+    // and value waves 0 and 1 copy the rows' LSE and delta (4 bytes a lane).
+    // Rows past S read as zero.  A wave waits for its copies before the next
+    // barrier.
+    auto dma_tile = [&](int t, int bufi, int tid_) {
+        typedef __attribute__((address_space(3))) void lds_void;
+        const int qb = q_begin + (t / G) * kQRows;
+        const int h = g * G + t % G;
+        const int64_t base = (((int64_t)b * S + qb) * a.Hq + h) * D;
+        const int rows = min(S - qb, kQRows);
+        const uint32_t rstride = (uint32_t)a.Hq * D * 2;
+        const uint32_t bytes = (uint32_t)(rows - 1) * rstride + D * 2;
+        const __amdgpu_buffer_rsrc_t rq = slab_rsrc(static_cast<const uint16_t*>(a.q) + base, bytes);
+        const __amdgpu_buffer_rsrc_t ro = slab_rsrc(static_cast<const uint16_t*>(a.dout) + base, bytes);
+        // vw (LDS addresses) keeps the thread index's known range, so the
+        // copies' LDS ranges stay visible to the alias analysis; vwu (the
+        // same value) drives the branches and descriptors
+        const int vw = tid_ >> 6, lane_ = tid_ & 63;
+        const int vwu = __builtin_amdgcn_readfirstlane(tid_ >> 6);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = vw * 4 + i;
+            const int r = 4 * j + (lane_ >> 4);
+            const uint32_t off = (uint32_t)r * rstride + (uint32_t)(((lane_ & 15) ^ swz(r)) << 4);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(smem + (bufi * 2 + 0) * TILE + j * 512), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (lds_void*)(smem + (bufi * 2 + 1) * TILE + j * 512), 16, off, 0, 0, 0);
+        }
+        const int64_t rb = ((int64_t)b * a.Hq + h) * S + qb;
+        if (vwu == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(slab_rsrc(a.lse2 + rb, (uint32_t)rows * 4), (lds_void*)&Ls[bufi][0],
+                                                     4, (uint32_t)lane_ * 4, 0, 0, 0);
+        else if (vwu == 1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(slab_rsrc(a.delta + rb, (uint32_t)rows * 4), (lds_void*)&Dl[bufi][0],
+                                                     4, (uint32_t)lane_ * 4, 0, 0, 0);
+    };
+
     const float sl2 = a.scale_log2;
-    // Tiles are loaded two iterations ahead of use and stored to LDS one
-    // iteration ahead, right after the barrier, so a tile's loads have a
-    // whole iteration to arrive before the store waits on them.
+    // Register staging: tiles are loaded two iterations ahead of use and
+    // stored to LDS one iteration ahead, right after the barrier, so a
+    // tile's loads have a whole iteration to arrive before the store waits
+    // on them.  Direct copies: tile it+1 is copied during iteration it.
     if (nit > 0 && !kwave) {
-        load_tile(0, tid);
-        store_tile(0, tid);
-        if (nit > 1) load_tile(1, tid);
+        if constexpr (kDma) {
+            dma_tile(0, 0, tid);
+        } else {
+            load_tile(0, tid);
+            store_tile(0, tid);
+            if (nit > 1) load_tile(1, tid);
+        }
     }
     // P hand-off from the value waves to the key waves in the shared array:
     // [tile parity][key block][sub-block][16-byte chunk][lane], fp16 (P <= 1)
@@ -362,8 +439,11 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
         // one query tile (the value waves' tile it, the key waves' tile it-1);
         // MASKED (value waves): some (row, key) pair of the tile is invisible
         // (causal diagonal, rows or keys past S)
-        auto tile = [&](int it, auto masked_c) {
+        auto tile = [&](int it, auto masked_c, auto buf_c) {
             constexpr bool MASKED = decltype(masked_c)::value;
+            // BC: the tile's LDS buffer when known at compile time (value
+            // waves at 128 channels), else -1
+            constexpr int BC = decltype(buf_c)::value;
             // Lane indices re-derived per tile from an opaque copy of the
             // thread index: the loop's address terms are then recomputed (a
             // few VALU instructions) instead of held in registers across the
@@ -371,14 +451,24 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
             int tid_o = tid;
             asm volatile("" : "+v"(tid_o));
             const int l32 = tid_o & 31, hi = (tid_o >> 5) & 1, lane_o = tid_o & 63;
+            // the direct-to-LDS copies of this wave complete before the
+            // barrier (the barrier alone does not wait for them)
+            if constexpr (!KW && kDma) __builtin_amdgcn_s_waitcnt(kWaitLoads);
             __syncthreads();  // tile `it` stored, P of tile it-1 handed over; older readers done
-            if (!KW && it + 1 < nit) {
+            if (!KW && !kDma && it + 1 < nit) {
                 store_tile((it + 1) % NBUF, tid_o);  // tile it+1, loaded an iteration ago
                 if (it + 2 < nit) load_tile(it + 2, tid_o);
             }
             if (KW && it == 0) return;  // the key waves' tile -1: the barrier only
             const int t = KW ? it - 1 : it;  // the tile this wave works on
-            const int buf = t % NBUF, par = t & 1;
+            const int buf = BC >= 0 ? BC : t % NBUF, par = t & 1;
+            // With the buffer known, the copies of tile it+1 go out first:
+            // the compiler sees this tile's row reads and the P stores as
+            // disjoint from them and issues them without waiting; the
+            // transposing reads (intrinsics with no alias information) wait
+            // for the copies, after both score chains.
+            if constexpr (!KW && kDma && BC >= 0)
+                if (it + 1 < nit) dma_tile(it + 1, (BC + 1) % NBUF, tid);
             const int qb = q_begin + (t / G) * kQRows;
             const uint16_t* qs = smem + (buf * 2 + 0) * TILE;
             const uint16_t* os = smem + (buf * 2 + 1) * TILE;
@@ -424,12 +514,26 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
                                        pack2_bf16(xv[8 * c + 4], xv[8 * c + 5]), pack2_bf16(xv[8 * c + 6], xv[8 * c + 7]));
                 if constexpr (!KW) {
 #pragma unroll
-                    for (int c = 0; c < 2; ++c)
-                        *xp_chunk(par, sb, c, lane_o) = make_uint4(pack2(xv[8 * c + 0], xv[8 * c + 1]), pack2(xv[8 * c + 2], xv[8 * c + 3]),
-                                                                   pack2(xv[8 * c + 4], xv[8 * c + 5]), pack2(xv[8 * c + 6], xv[8 * c + 7]));
+                    for (int c = 0; c < 2; ++c) {
+                        uint32_t w0 = pack2(xv[8 * c + 0], xv[8 * c + 1]), w1 = pack2(xv[8 * c + 2], xv[8 * c + 3]);
+                        uint32_t w2 = pack2(xv[8 * c + 4], xv[8 * c + 5]), w3 = pack2(xv[8 * c + 6], xv[8 * c + 7]);
+                        // one vector store: split stores lose the array's
+                        // alias information, and each then waits for the
+                        // direct-to-LDS copies in flight
+                        typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+                        *reinterpret_cast<u32x4v*>(xp_chunk(par, sb, c, lane_o)) = u32x4v{w0, w1, w2, w3};
+                    }
                 }
             };
             const uint16_t* other = KW ? qs : os;  // dK += dS^T Q, dV += P^T dO
+            auto rfrag = [&](const uint16_t* t_, int r0, int ks) {
+                if constexpr (kDma) return row_frag_sw(t_, r0, ks, l32, hi);
+                else return row_frag(t_, P, r0, ks, l32, hi);
+            };
+            auto tfrag = [&](const uint16_t* t_, int krow0, int col0) {
+                if constexpr (kDma) return tr_frag_sw(t_, krow0, col0, l32, hi);
+                else return tr_frag(t_, P, krow0, col0, l32, hi);
+            };
             // The score chain S^T = Q K~^T (value waves) or dP^T = dO V~^T
             // (key waves) of sub-block sb (32 keys x 32 rows), with the 16
             // entries of the previous sub-block psb computed a few at a time
@@ -442,7 +546,7 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
                 uint4 fr[PF + 1], ph[2];
                 float4 R4[4];
 #pragma unroll
-                for (int ks = 0; ks < PF; ++ks) fr[ks] = row_frag(src, P, sb * 32, ks, l32, hi);
+                for (int ks = 0; ks < PF; ++ks) fr[ks] = rfrag(src, sb * 32, ks);
                 if (ps) {
                     ld_rows(psb, 0, R4[0]);
                     if constexpr (KW) {
@@ -452,7 +556,7 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
                 }
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    if (ks + PF < KS) fr[(ks + PF) % (PF + 1)] = row_frag(src, P, sb * 32, ks + PF, l32, hi);
+                    if (ks + PF < KS) fr[(ks + PF) % (PF + 1)] = rfrag(src, sb * 32, ks + PF);
                     // the chain starts from a zero operand, not zeroed registers
                     cacc = mma(fr[ks % (PF + 1)], KW ? vreg[ks] : kreg[ks], ks == 0 ? f32x16{} : cacc);
                     if (ps) {
@@ -473,8 +577,8 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
                 constexpr int NM = 2 * NDB;
                 uint4 tf[3], ph[2];
                 float4 R4[4];
-                tf[0] = tr_frag(other, P, sb * 32, 0, l32, hi);
-                if (NM > 1) tf[1] = tr_frag(other, P, sb * 32 + (NDB > 1 ? 0 : 16), (NDB > 1 ? 32 : 0), l32, hi);
+                tf[0] = tfrag(other, sb * 32, 0);
+                if (NM > 1) tf[1] = tfrag(other, sb * 32 + (NDB > 1 ? 0 : 16), (NDB > 1 ? 32 : 0));
                 if (ns) {
                     ld_rows(nsb, 0, R4[0]);
                     if constexpr (KW) {
@@ -486,7 +590,7 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
                 for (int m = 0; m < NM; ++m) {
                     if (m + 2 < NM) {
                         const int m2 = m + 2;
-                        tf[m2 % 3] = tr_frag(other, P, sb * 32 + 16 * (m2 / NDB), (m2 % NDB) * 32, l32, hi);
+                        tf[m2 % 3] = tfrag(other, sb * 32 + 16 * (m2 / NDB), (m2 % NDB) * 32);
                     }
                     acc[m % NDB] = mma(xa[m / NDB], tf[m % 3], acc[m % NDB]);
                     if (ns) {
@@ -514,14 +618,30 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
             mask(1, xv);
             pack(1, xv, xa);
             __builtin_amdgcn_sched_barrier(0);
-            product(1, xa, 0, nullptr, xv);
+            if constexpr (!KW && kDma && BC < 0) {
+                // The last product's operands are read first, then the copies
+                // of tile it+1 are issued: no LDS access of this iteration
+                // follows them (each would wait for the copies), and they
+                // arrive while the products and the key waves finish.
+                constexpr int NM = 2 * NDB;
+                uint4 tf[NM];
+#pragma unroll
+                for (int m = 0; m < NM; ++m) tf[m] = tfrag(other, 32 + 16 * (m / NDB), (m % NDB) * 32);
+                __builtin_amdgcn_sched_barrier(0);
+                if (it + 1 < nit) dma_tile(it + 1, (it + 1) % NBUF, tid_o);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int m = 0; m < NM; ++m) acc[m % NDB] = mma(xa[m / NDB], tf[m], acc[m % NDB]);
+            } else {
+                product(1, xa, 0, nullptr, xv);
+            }
         };
         if constexpr (KW) {
             // key waves: the barrier of iteration 0, then tiles 0 .. nit-1 in
             // iterations 1 .. nit
             // (nit + 1 barriers, as the value waves)
             if (nit > 0)
-                for (int it = 0; it <= nit; ++it) tile(it, std::false_type{});
+                for (int it = 0; it <= nit; ++it) tile(it, std::false_type{}, std::integral_constant<int, -1>{});
         } else {
             // Iterations [it_lo, it_hi) see every (row, key) pair of this
             // wave's block: the masked tiles are a causal prefix and a tail
@@ -534,9 +654,28 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
                 it_hi = max(it_lo, (S - q_begin) / kQRows * G);
             }
             int it = 0;
-            for (; it < it_lo; ++it) tile(it, std::true_type{});
-            for (; it < it_hi; ++it) tile(it, std::false_type{});
-            for (; it < nit; ++it) tile(it, std::true_type{});
+            using BR = std::integral_constant<int, -1>;
+            for (; it < it_lo; ++it) tile(it, std::true_type{}, BR{});
+            if constexpr (kDma) {
+                // whole tiles with their buffer index (it % 3) as a constant
+                using B0 = std::integral_constant<int, 0>;
+                using B1 = std::integral_constant<int, 1>;
+                using B2 = std::integral_constant<int, 2>;
+                static_assert(NBUF == 3, "three tile buffers");
+                if (it < it_hi && it % 3 == 1) tile(it++, std::false_type{}, B1{});
+                if (it < it_hi && it % 3 == 2) tile(it++, std::false_type{}, B2{});
+                while (it < it_hi) {
+                    tile(it, std::false_type{}, B0{});
+                    if (++it == it_hi) break;
+                    tile(it, std::false_type{}, B1{});
+                    if (++it == it_hi) break;
+                    tile(it, std::false_type{}, B2{});
+                    ++it;
+                }
+            } else {
+                for (; it < it_hi; ++it) tile(it, std::false_type{}, BR{});
+            }
+            for (; it < nit; ++it) tile(it, std::true_type{}, BR{});
             if (nit > 0) __syncthreads();  // the key waves' last iteration
         }
     };

@@ -170,13 +170,18 @@ def test_whole_tiles(D):
         compare(c.run(), c.reference(), LITE_NAMES)
 
 
-def test_long_ragged_full_attention():
+@pytest.mark.parametrize("D", [96, 128])
+def test_long_ragged_full_attention(D):
     """S = 1000 without a mask and G = 4: many query tiles through the
-    key-tile kernel's P hand-off and its three tile buffers, every key block
-    live, a ragged 40-row tail."""
-    say("backward long ragged full B=1 S=1000 Hq=8 Hkv=2 D=96")
-    c = Case(1, 1000, 8, 2, 96, 2501, causal=False)
+    key-tile kernel's P hand-off and its three tile buffers (at 128
+    channels the copy-ahead loop with its buffer index unrolled), every key
+    block live, a ragged 40-row tail."""
+    say("backward long ragged full B=1 S=1000 Hq=8 Hkv=2 D=%d" % D)
+    c = Case(1, 1000, 8, 2, D, 2501, causal=False)
     compare(c.run(), c.reference(), FUSED_NAMES)
+    if D == 128:
+        c = Case(1, 1000, 8, 2, D, 2502, causal=True, lite=True)
+        compare(c.run(), c.reference(), LITE_NAMES)
 
 
 @pytest.mark.parametrize("layout", ["bhsd", "bshd"])
