@@ -75,6 +75,7 @@ constexpr int kKTile = 64;        // query-tile kernel: keys per LDS tile
 constexpr int kDqWaves = 8;       // query-tile kernel: 8 x 32 (query row, head) columns
 constexpr int kDkvThreads = 512;  // key-tile kernel: 4 value waves + 4 key waves
 constexpr int kDqThreads = 64 * kDqWaves;
+constexpr int kPrepRows = 4;      // prep kernel: rows per lane group
 
 // Slot of the (batch, KV head, key tile) weight-gradient partial.
 __device__ __forceinline__ int64_t item_index(int b, int g, int kt, int Hkv, int nkt)
@@ -177,26 +178,36 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdArgs a)
 {
     constexpr int LPR = D / 8 <= 8 ? 8 : 16;  // lanes per row
     const int64_t n = (int64_t)a.B * a.S * a.Hq;
-    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;
+    // a lane group takes kPrepRows consecutive rows, all loads issued first
+    const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR * kPrepRows;
     const int pc = threadIdx.x % LPR;
-    const bool on = i < n && pc < D / 8;
-    float s = 0.0f;
-    if (on) {
-        const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.out) + i * D + pc * 8);
-        const uint4 y = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.dout) + i * D + pc * 8);
-        const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+    uint4 x[kPrepRows], y[kPrepRows];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) s += bf16_lo(xs[k]) * bf16_lo(ys[k]) + bf16_hi(xs[k]) * bf16_hi(ys[k]);
+    for (int k = 0; k < kPrepRows; ++k) {
+        const int64_t i = i0 + k;
+        x[k] = y[k] = make_uint4(0u, 0u, 0u, 0u);
+        if (i < n && pc < D / 8) {
+            x[k] = stream16(static_cast<const uint16_t*>(a.out) + i * D + pc * 8);
+            y[k] = stream16(static_cast<const uint16_t*>(a.dout) + i * D + pc * 8);
+        }
     }
 #pragma unroll
-    for (int o = 1; o < LPR; o <<= 1) s += __shfl_xor(s, o);
-    if (i < n && pc == 0) {
-        const int h = (int)(i % a.Hq);
-        const int64_t bs = i / a.Hq;
-        const int t = (int)(bs % a.S), b = (int)(bs / a.S);
-        const int64_t r = ((int64_t)b * a.Hq + h) * a.S + t;
-        a.delta[r] = s;
-        a.lse2[r] = a.lse[r] * kLog2e;
+    for (int k = 0; k < kPrepRows; ++k) {
+        const int64_t i = i0 + k;
+        const uint32_t xs[4] = {x[k].x, x[k].y, x[k].z, x[k].w}, ys[4] = {y[k].x, y[k].y, y[k].z, y[k].w};
+        float s = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s += bf16_lo(xs[e]) * bf16_lo(ys[e]) + bf16_hi(xs[e]) * bf16_hi(ys[e]);
+#pragma unroll
+        for (int o = 1; o < LPR; o <<= 1) s += __shfl_xor(s, o);
+        if (i < n && pc == 0) {
+            const int h = (int)(i % a.Hq);
+            const int64_t bs = i / a.Hq;
+            const int t = (int)(bs % a.S), b = (int)(bs / a.S);
+            const int64_t r = ((int64_t)b * a.Hq + h) * a.S + t;
+            a.delta[r] = s;
+            a.lse2[r] = a.lse[r] * kLog2e;
+        }
     }
 }
 
@@ -1055,7 +1066,7 @@ int launch_bwd3(const BwdArgs& a, hipStream_t st)
 {
     const int64_t rows = (int64_t)a.B * a.S * a.Hq;
     {
-        const int64_t lanes = rows * (D / 8 <= 8 ? 8 : 16);
+        const int64_t lanes = (rows + kPrepRows - 1) / kPrepRows * (D / 8 <= 8 ? 8 : 16);
         if ((lanes + 255) / 256 > 0x7fffffff) return (int)hipErrorInvalidValue;
         hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, st, a);
     }
