@@ -666,13 +666,20 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
             }
             int it = 0;
             using BR = std::integral_constant<int, -1>;
-            for (; it < it_lo; ++it) tile(it, std::true_type{}, BR{});
             if constexpr (kDma) {
-                // whole tiles with their buffer index (it % 3) as a constant
+                // tiles with their buffer index (it % 3) as a constant
                 using B0 = std::integral_constant<int, 0>;
                 using B1 = std::integral_constant<int, 1>;
                 using B2 = std::integral_constant<int, 2>;
                 static_assert(NBUF == 3, "three tile buffers");
+                while (it < it_lo) {  // the masked prefix starts at tile 0
+                    tile(it, std::true_type{}, B0{});
+                    if (++it == it_lo) break;
+                    tile(it, std::true_type{}, B1{});
+                    if (++it == it_lo) break;
+                    tile(it, std::true_type{}, B2{});
+                    ++it;
+                }
                 if (it < it_hi && it % 3 == 1) tile(it++, std::false_type{}, B1{});
                 if (it < it_hi && it % 3 == 2) tile(it++, std::false_type{}, B2{});
                 while (it < it_hi) {
@@ -684,6 +691,7 @@ __global__ __launch_bounds__(kDkvThreads, 2) void bwd_dkdv_kernel(const BwdArgs 
                     ++it;
                 }
             } else {
+                for (; it < it_lo; ++it) tile(it, std::true_type{}, BR{});
                 for (; it < it_hi; ++it) tile(it, std::false_type{}, BR{});
             }
             for (; it < nit; ++it) tile(it, std::true_type{}, BR{});
